@@ -1,0 +1,229 @@
+"""CPU oracle for paged KV-cache attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package.  The GPU library never links or calls it,
+and this package imports nothing from the GPU library.
+
+The arithmetic lives in ``oracle.c`` (fp64, plain definition; see its header
+for the passages of the source pages it follows).  This module only marshals
+numpy arrays into it.
+
+Array conventions
+-----------------
+* bf16 data is passed as ``numpy.uint16`` arrays holding the raw bf16 bit
+  patterns; fp32 data as ``numpy.float32``.  q, K and V share one dtype.
+* Caches are ``[num_blocks, Hkv, block_size, D]``; q for decode is
+  ``[B, Hq, D]``; q for prefill is ``[Tq, Hq, D]``.
+* Attention outputs come back as ``numpy.float64``.
+
+Parity status of each function (what pins it) is listed in the design notes
+and checked by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dbl_p = ctypes.POINTER(ctypes.c_double)
+_i32_p = ctypes.POINTER(ctypes.c_int32)
+_i64_p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc -O2 (no fast-math) into liboracle.so."""
+    global _lib
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def use_library(path):
+    """Swap in another build of oracle.c (the mutation tests use this); returns the previous one."""
+    global _lib
+    prev = _lib
+    _lib = None if path is None else _bind(ctypes.CDLL(path))
+    return prev
+
+
+def restore_library(prev):
+    global _lib
+    _lib = prev
+
+
+def _bind(lib):
+    lib.oracle_kv_cache_write.argtypes = [_vp, _vp, _vp, _vp, _i64_p] + [ctypes.c_int] * 6
+    lib.oracle_block_copy.argtypes = [_vp, _vp, _i64_p] + [ctypes.c_int] * 6
+    lib.oracle_paged_decode.argtypes = ([_dbl_p, _vp, _vp, _vp, ctypes.c_int, _i32_p, ctypes.c_int,
+                                         _i32_p] + [ctypes.c_int] * 6 + [ctypes.c_double])
+    lib.oracle_paged_prefill.argtypes = ([_dbl_p, _vp, _vp, _vp, ctypes.c_int, _i32_p, ctypes.c_int,
+                                          _i32_p, _i32_p] + [ctypes.c_int] * 6 + [ctypes.c_double])
+    lib.oracle_contiguous_attention.argtypes = ([_dbl_p, _dbl_p, _dbl_p, _dbl_p, _i32_p]
+                                                + [ctypes.c_int] * 5 + [ctypes.c_double])
+    lib.oracle_blockwise_decode_row.argtypes = ([_dbl_p, _vp, ctypes.c_int64, _vp, _vp, ctypes.c_int,
+                                                 _i32_p] + [ctypes.c_int] * 6
+                                                + [ctypes.c_double, ctypes.c_int, _i32_p])
+    for name in ("oracle_kv_cache_write", "oracle_block_copy", "oracle_paged_decode",
+                 "oracle_paged_prefill", "oracle_contiguous_attention",
+                 "oracle_blockwise_decode_row"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError("oracle takes float32 or uint16 (bf16 bit patterns), got %s" % a.dtype)
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError("%s failed with code %d" % (what, rc))
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of float32 or bf16-bit arrays to float64."""
+    return bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def kv_cache_write(key, value, k_cache, v_cache, slot_mapping):
+    """In-place scatter of key/value [T, Hkv, D] rows into the caches."""
+    lib = _load()
+    NB, Hkv, bs, D = k_cache.shape
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    key, value = _c(key), _c(value)
+    dt = _dtype_code(k_cache)
+    assert key.dtype == k_cache.dtype == value.dtype == v_cache.dtype
+    T = key.shape[0]
+    slots = _c(slot_mapping, np.int64)
+    rc = lib.oracle_kv_cache_write(key.ctypes.data, value.ctypes.data, k_cache.ctypes.data,
+                                   v_cache.ctypes.data, slots.ctypes.data_as(_i64_p), T, NB, Hkv,
+                                   bs, D, dt)
+    _check(rc, "oracle_kv_cache_write")
+
+
+def block_copy(k_cache, v_cache, pairs):
+    """In-place copy of whole blocks (all KV heads) for each (src, dst) pair."""
+    lib = _load()
+    NB, Hkv, bs, D = k_cache.shape
+    pairs = _c(np.asarray(pairs).reshape(-1, 2), np.int64)
+    rc = lib.oracle_block_copy(k_cache.ctypes.data, v_cache.ctypes.data,
+                               pairs.ctypes.data_as(_i64_p), pairs.shape[0], NB, Hkv, bs, D,
+                               _dtype_code(k_cache))
+    _check(rc, "oracle_block_copy")
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale):
+    """fp64 [B, Hq, D] decode attention through the block tables."""
+    lib = _load()
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    assert Dq == D and q.dtype == k_cache.dtype == v_cache.dtype
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.zeros((B, Hq, D), np.float64)
+    rc = lib.oracle_paged_decode(out.ctypes.data_as(_dbl_p), q.ctypes.data, k_cache.ctypes.data,
+                                 v_cache.ctypes.data, _dtype_code(q), bt.ctypes.data_as(_i32_p),
+                                 bt.shape[1], sl.ctypes.data_as(_i32_p), B, Hq, Hkv, D, bs, NB,
+                                 float(scale))
+    _check(rc, "oracle_paged_decode")
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, scale):
+    """fp64 [Tq, Hq, D] causal chunk attention over the paged cache."""
+    lib = _load()
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    NB, Hkv, bs, D = k_cache.shape
+    Tq, Hq, Dq = q.shape
+    assert Dq == D and q.dtype == k_cache.dtype == v_cache.dtype
+    bt = _c(block_tables, np.int32)
+    qsl = _c(query_start_loc, np.int32)
+    sl = _c(seq_lens, np.int32)
+    B = sl.shape[0]
+    assert qsl.shape[0] == B + 1 and qsl[-1] <= Tq
+    out = np.zeros((Tq, Hq, D), np.float64)
+    rc = lib.oracle_paged_prefill(out.ctypes.data_as(_dbl_p), q.ctypes.data, k_cache.ctypes.data,
+                                  v_cache.ctypes.data, _dtype_code(q), bt.ctypes.data_as(_i32_p),
+                                  bt.shape[1], qsl.ctypes.data_as(_i32_p), sl.ctypes.data_as(_i32_p),
+                                  B, Hq, Hkv, D, bs, NB, float(scale))
+    _check(rc, "oracle_paged_prefill")
+    return out
+
+
+def contiguous_attention(q, K, V, n_keys, scale):
+    """fp64 attention over contiguous K,V [Lk, Hkv, D]; q [Tq, Hq, D]; row i sees n_keys[i] keys."""
+    lib = _load()
+    q, K, V = _c(q, np.float64), _c(K, np.float64), _c(V, np.float64)
+    Tq, Hq, D = q.shape
+    Lk, Hkv, _ = K.shape
+    nk = _c(n_keys, np.int32)
+    assert nk.shape[0] == Tq
+    out = np.zeros((Tq, Hq, D), np.float64)
+    rc = lib.oracle_contiguous_attention(out.ctypes.data_as(_dbl_p), q.ctypes.data_as(_dbl_p),
+                                         K.ctypes.data_as(_dbl_p), V.ctypes.data_as(_dbl_p),
+                                         nk.ctypes.data_as(_i32_p), Tq, Lk, Hq, Hkv, D, float(scale))
+    _check(rc, "oracle_contiguous_attention")
+    return out
+
+
+def blockwise_decode_row(q_row, k_cache, v_cache, table, n_keys, kh, scale,
+                         partition_blocks=1 << 30, visit_order=None):
+    """The pages' block loop with online softmax for one query row (fp64 [D])."""
+    lib = _load()
+    q_row = _c(q_row)
+    k_cache, v_cache = _c(k_cache), _c(v_cache)
+    NB, Hkv, bs, D = k_cache.shape
+    table = _c(table, np.int32)
+    order = None if visit_order is None else _c(visit_order, np.int32)
+    out = np.zeros(D, np.float64)
+    rc = lib.oracle_blockwise_decode_row(out.ctypes.data_as(_dbl_p), q_row.ctypes.data, 0,
+                                         k_cache.ctypes.data, v_cache.ctypes.data,
+                                         _dtype_code(q_row), table.ctypes.data_as(_i32_p),
+                                         int(n_keys), int(kh), Hkv, D, bs, NB, float(scale),
+                                         int(min(partition_blocks, 1 << 30)),
+                                         None if order is None else order.ctypes.data_as(_i32_p))
+    _check(rc, "oracle_blockwise_decode_row")
+    return out

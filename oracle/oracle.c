@@ -1,0 +1,363 @@
+/*
+ * oracle.c -- plain CPU reference for paged KV-cache attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header or table with the GPU
+ * library and includes nothing from it.
+ *
+ * Every floating-point result is computed in fp64 from the exactly decoded
+ * input values (a bf16 value widens to double without rounding).  Nothing is
+ * blocked, fused or reordered beyond the plain definition.
+ *
+ * Sources (web pages on KV-cache management):
+ *  - Month 2 "PagedAttention" (infra learning path, memory chapter):
+ *      §2.1  attention with a KV cache, softmax(Q_i K_{:i}^T / sqrt(d)) V_{:i};
+ *      §5.2  one physical KV pool per layer, separate K and V tensors;
+ *      §5.4  the kernel visits logical blocks through the block table.
+ *  - Lecture 7 "KV Cache Management: PagedAttention and Mooncake" (CS349E):
+ *      §4.1  fixed-size blocks, block table, only the last block is partial;
+ *      §4.2  blockwise attention equals attention over the contiguous KV;
+ *      §4.3  the fused kernels: KV write, attention through the table,
+ *            batched copy of the blocks copy-on-write needs.
+ *  - Lecture 16 "LLM Serving (1): Batching, PagedAttention, RadixAttention"
+ *    (CMU 15-779): §3.3 block table and blockwise attention with the
+ *    online-softmax merge rule.
+ *  - Lecture 27 "Better KV Caches: CacheGen, CacheBlend and LMCache"
+ *    (CMU 11-868): §1.1 new tokens' queries attend to cached K,V directly
+ *    (the chunked-prefill case).
+ *
+ * Readings taken where the pages are silent or garbled (each is listed in the
+ * design notes with its reason):
+ *  - a sequence of length L uses ceil(L/bs) blocks; offsets >= L in the last
+ *    block are never read (the pages' loop bound floors the division, which
+ *    would drop the partial last block that §4.1 says exists);
+ *  - query head h reads KV head h / (Hq/Hkv) (contiguous GQA groups);
+ *  - the kernel attends to exactly seq_lens[b] tokens, the current one
+ *    included (its K,V are written before attention);
+ *  - L == 0 gives an all-zero output row;
+ *  - cache layout [num_blocks][Hkv][block_size][D], K and V separate;
+ *  - slot = block * block_size + offset, slot < 0 means "skip this row".
+ *
+ * dtype codes: 0 = fp32, 1 = bf16 (stored as raw 16-bit patterns).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_RANGE (-2)
+#define ORC_ERR_NOMEM (-3)
+
+static double elem(const void *base, int64_t i, int dtype) {
+  if (dtype == 0) return (double)((const float *)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
+
+/* Index of element (blk, h, off, d) in a [NB][Hkv][bs][D] cache. */
+static int64_t cache_index(int64_t blk, int h, int off, int d, int Hkv, int bs,
+                           int D) {
+  return (((blk * Hkv + h) * (int64_t)bs + off) * D) + d;
+}
+
+/*
+ * KV write (Lecture 7 §4.3, first fused kernel; Lecture 16 §3.3 fill rule):
+ * for every token t with slot s = slot_mapping[t] >= 0, copy key[t][h][:] to
+ * K[s / bs][h][s % bs][:] and value[t][h][:] likewise, for every KV head h.
+ * A pure byte copy.  Returns ORC_ERR_RANGE (after writing nothing for that
+ * row) if a slot points past the pool.
+ */
+int oracle_kv_cache_write(const void *key, const void *value, void *k_cache,
+                          void *v_cache, const int64_t *slot_mapping, int T,
+                          int num_blocks, int Hkv, int bs, int D, int dtype) {
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return ORC_ERR_ARG;
+  int eb = elem_bytes(dtype);
+  int rc = ORC_OK;
+  for (int t = 0; t < T; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t blk = s / bs;
+    int off = (int)(s % bs);
+    if (blk >= num_blocks) {
+      rc = ORC_ERR_RANGE;
+      continue;
+    }
+    for (int h = 0; h < Hkv; ++h) {
+      int64_t src = ((int64_t)t * Hkv + h) * D;
+      int64_t dst = cache_index(blk, h, off, 0, Hkv, bs, D);
+      memcpy((char *)k_cache + dst * eb, (const char *)key + src * eb, (size_t)D * eb);
+      memcpy((char *)v_cache + dst * eb, (const char *)value + src * eb, (size_t)D * eb);
+    }
+  }
+  return rc;
+}
+
+/*
+ * Block copy for copy-on-write (Lecture 7 §4.3 third fused kernel and §5.1;
+ * Lecture 16 §3.5): for each pair (src, dst), K[dst] = K[src] and
+ * V[dst] = V[src] over all KV heads of one layer.  Pairs are applied in
+ * order; src == dst is a no-op.
+ */
+int oracle_block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int N,
+                      int num_blocks, int Hkv, int bs, int D, int dtype) {
+  if (!k_cache || !v_cache || (!pairs && N > 0)) return ORC_ERR_ARG;
+  size_t blk_bytes = (size_t)Hkv * bs * D * elem_bytes(dtype);
+  for (int i = 0; i < N; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return ORC_ERR_RANGE;
+    if (src == dst) continue;
+    memmove((char *)k_cache + dst * blk_bytes, (const char *)k_cache + src * blk_bytes, blk_bytes);
+    memmove((char *)v_cache + dst * blk_bytes, (const char *)v_cache + src * blk_bytes, blk_bytes);
+  }
+  return ORC_OK;
+}
+
+/*
+ * One attention row by the definition (Month 2 §2.1): the query q (length D)
+ * against the first n_keys tokens of sequence b, reached through the block
+ * table (Month 2 §5.4: logical block j lives in physical block
+ * block_table[j]; token t sits at offset t % bs of logical block t / bs).
+ *   s_t = scale * sum_d q[d] K_t[d]
+ *   out = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
+ * Two passes over the scores, fp64 throughout.  n_keys == 0 gives zeros.
+ */
+static int attend_row(double *out, const void *q, int64_t q_off, const void *k_cache,
+                      const void *v_cache, int dtype, const int32_t *table,
+                      int max_blocks, int n_keys, int kh, int Hkv, int D, int bs,
+                      int num_blocks, double scale, double *scores) {
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (n_keys <= 0) return ORC_OK;
+  if ((n_keys + bs - 1) / bs > max_blocks) return ORC_ERR_RANGE;
+  double m = -INFINITY;
+  for (int t = 0; t < n_keys; ++t) {
+    int32_t phys = table[t / bs];
+    if (phys < 0 || phys >= num_blocks) return ORC_ERR_RANGE;
+    int64_t base = cache_index(phys, kh, t % bs, 0, Hkv, bs, D);
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, dtype) * elem(k_cache, base + d, dtype);
+    scores[t] = scale * dot;
+    if (scores[t] > m) m = scores[t];
+  }
+  double l = 0.0;
+  for (int t = 0; t < n_keys; ++t) {
+    double e = exp(scores[t] - m);
+    l += e;
+    int64_t base = cache_index(table[t / bs], kh, t % bs, 0, Hkv, bs, D);
+    for (int d = 0; d < D; ++d) out[d] += e * elem(v_cache, base + d, dtype);
+  }
+  for (int d = 0; d < D; ++d) out[d] /= l;
+  return ORC_OK;
+}
+
+/*
+ * Paged decode (Month 2 §5.4; Lecture 7 §4.2): for every sequence b and query
+ * head h, one query row q[b][h][:] attends to all seq_lens[b] cached tokens
+ * of KV head h / (Hq / Hkv).  out is fp64 [B][Hq][D]; q has the KV dtype and
+ * layout [B][Hq][D]; block_tables is [B][max_blocks].
+ */
+int oracle_paged_decode(double *out, const void *q, const void *k_cache,
+                        const void *v_cache, int dtype, const int32_t *block_tables,
+                        int max_blocks, const int32_t *seq_lens, int B, int Hq,
+                        int Hkv, int D, int bs, int num_blocks, double scale) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return ORC_ERR_ARG;
+  if (Hkv <= 0 || Hq % Hkv != 0 || bs <= 0 || D <= 0) return ORC_ERR_ARG;
+  int g = Hq / Hkv;
+  int max_len = 0;
+  for (int b = 0; b < B; ++b)
+    if (seq_lens[b] > max_len) max_len = seq_lens[b];
+  double *scores = (double *)malloc(sizeof(double) * (max_len > 0 ? max_len : 1));
+  if (!scores) return ORC_ERR_NOMEM;
+  int rc = ORC_OK;
+  for (int b = 0; b < B && rc == ORC_OK; ++b) {
+    for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
+      int64_t row = (int64_t)b * Hq + h;
+      rc = attend_row(out + row * D, q, row * D, k_cache, v_cache, dtype,
+                      block_tables + (int64_t)b * max_blocks, max_blocks, seq_lens[b],
+                      h / g, Hkv, D, bs, num_blocks, scale, scores);
+    }
+  }
+  free(scores);
+  return rc;
+}
+
+/*
+ * Chunked prefill over cached blocks (Lecture 27 §1.1; Lecture 7 §8.3: only
+ * the uncached suffix is computed, its queries attend to the cached prefix
+ * and to themselves).  Sequence b owns query rows query_start_loc[b] ..
+ * query_start_loc[b+1]-1 (n_b rows) and has seq_lens[b] tokens in the cache
+ * after the chunk was written.  Row i of the chunk sits at position
+ * pos = seq_lens[b] - n_b + i and attends to tokens 0..pos (causal).
+ * q and out are [Tq][Hq][D].
+ */
+int oracle_paged_prefill(double *out, const void *q, const void *k_cache,
+                         const void *v_cache, int dtype, const int32_t *block_tables,
+                         int max_blocks, const int32_t *query_start_loc,
+                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                         int bs, int num_blocks, double scale) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens)
+    return ORC_ERR_ARG;
+  if (Hkv <= 0 || Hq % Hkv != 0 || bs <= 0 || D <= 0) return ORC_ERR_ARG;
+  int g = Hq / Hkv;
+  int max_len = 0;
+  for (int b = 0; b < B; ++b)
+    if (seq_lens[b] > max_len) max_len = seq_lens[b];
+  double *scores = (double *)malloc(sizeof(double) * (max_len > 0 ? max_len : 1));
+  if (!scores) return ORC_ERR_NOMEM;
+  int rc = ORC_OK;
+  for (int b = 0; b < B && rc == ORC_OK; ++b) {
+    int q0 = query_start_loc[b], n_b = query_start_loc[b + 1] - q0;
+    if (n_b < 0 || n_b > seq_lens[b]) {
+      rc = ORC_ERR_ARG;
+      break;
+    }
+    for (int i = 0; i < n_b && rc == ORC_OK; ++i) {
+      int pos = seq_lens[b] - n_b + i;
+      for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
+        int64_t row = (int64_t)(q0 + i) * Hq + h;
+        rc = attend_row(out + row * D, q, row * D, k_cache, v_cache, dtype,
+                        block_tables + (int64_t)b * max_blocks, max_blocks, pos + 1,
+                        h / g, Hkv, D, bs, num_blocks, scale, scores);
+      }
+    }
+  }
+  free(scores);
+  return rc;
+}
+
+/*
+ * Contiguous attention, no block table: the layout earlier systems used
+ * (Lecture 7 §3.1) and the right-hand side of the equivalence in Lecture 7
+ * §4.2 / Lecture 16 §3.3.  q is fp64 [Tq][Hq][D]; K and V are fp64
+ * [Lk][Hkv][D] for one sequence.  Query row i attends to keys
+ * 0..n_keys[i]-1.  out is fp64 [Tq][Hq][D].
+ */
+int oracle_contiguous_attention(double *out, const double *q, const double *K,
+                                const double *V, const int32_t *n_keys, int Tq,
+                                int Lk, int Hq, int Hkv, int D, double scale) {
+  if (!out || !q || !K || !V || !n_keys) return ORC_ERR_ARG;
+  if (Hkv <= 0 || Hq % Hkv != 0) return ORC_ERR_ARG;
+  int g = Hq / Hkv;
+  double *s = (double *)malloc(sizeof(double) * (Lk > 0 ? Lk : 1));
+  if (!s) return ORC_ERR_NOMEM;
+  for (int i = 0; i < Tq; ++i) {
+    int n = n_keys[i];
+    if (n > Lk) {
+      free(s);
+      return ORC_ERR_RANGE;
+    }
+    for (int h = 0; h < Hq; ++h) {
+      int kh = h / g;
+      const double *qr = q + ((int64_t)i * Hq + h) * D;
+      double *o = out + ((int64_t)i * Hq + h) * D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (n <= 0) continue;
+      double m = -INFINITY;
+      for (int t = 0; t < n; ++t) {
+        const double *k = K + ((int64_t)t * Hkv + kh) * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qr[d] * k[d];
+        s[t] = scale * dot;
+        if (s[t] > m) m = s[t];
+      }
+      double l = 0.0;
+      for (int t = 0; t < n; ++t) {
+        double e = exp(s[t] - m);
+        l += e;
+        const double *v = V + ((int64_t)t * Hkv + kh) * D;
+        for (int d = 0; d < D; ++d) o[d] += e * v[d];
+      }
+      for (int d = 0; d < D; ++d) o[d] /= l;
+    }
+  }
+  free(s);
+  return ORC_OK;
+}
+
+/*
+ * The pages' own algorithm for one decode row, kept to pin the definition
+ * above against it: the kernel loop of Month 2 §5.4 (visit logical blocks,
+ * look up the physical block, score the block, update a running max, a
+ * running sum and a running output with the rescale factor
+ * exp(old_max - new_max)), run independently over partitions of
+ * `partition_blocks` logical blocks, then the partitions' (max, sum, output)
+ * triples merged by the same rule (Lecture 16 §3.3: attention is associative
+ * and commutative under the online-softmax merge).  `visit_order` lists the
+ * logical blocks of each partition in the order to visit them (any order
+ * gives the same real number); NULL means ascending.  Only valid offsets of
+ * the last block are scored (the ceil reading of the loop bound).
+ */
+int oracle_blockwise_decode_row(double *out, const void *q, int64_t q_off,
+                                const void *k_cache, const void *v_cache, int dtype,
+                                const int32_t *table, int n_keys, int kh, int Hkv,
+                                int D, int bs, int num_blocks, double scale,
+                                int partition_blocks, const int32_t *visit_order) {
+  if (!out || !q || !k_cache || !v_cache || !table || partition_blocks <= 0) return ORC_ERR_ARG;
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (n_keys <= 0) return ORC_OK;
+  int n_blocks = (n_keys + bs - 1) / bs;
+  int n_parts = (n_blocks + partition_blocks - 1) / partition_blocks;
+  double *pm = (double *)malloc(sizeof(double) * n_parts);
+  double *pl = (double *)malloc(sizeof(double) * n_parts);
+  double *po = (double *)calloc((size_t)n_parts * D, sizeof(double));
+  double sc[1024];
+  if (!pm || !pl || !po || bs > 1024) {
+    free(pm); free(pl); free(po);
+    return bs > 1024 ? ORC_ERR_ARG : ORC_ERR_NOMEM;
+  }
+  int rc = ORC_OK;
+  for (int p = 0; p < n_parts && rc == ORC_OK; ++p) {
+    double run_max = -INFINITY, run_sum = 0.0;
+    double *acc = po + (int64_t)p * D;
+    int first = p * partition_blocks;
+    int count = n_blocks - first < partition_blocks ? n_blocks - first : partition_blocks;
+    for (int k = 0; k < count; ++k) {
+      int j = visit_order ? visit_order[first + k] : first + k;
+      if (j < first || j >= first + count) { rc = ORC_ERR_ARG; break; }
+      int32_t phys = table[j];
+      if (phys < 0 || phys >= num_blocks) { rc = ORC_ERR_RANGE; break; }
+      int valid = n_keys - j * bs < bs ? n_keys - j * bs : bs;
+      double block_max = -INFINITY;
+      for (int o = 0; o < valid; ++o) {
+        int64_t base = cache_index(phys, kh, o, 0, Hkv, bs, D);
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, dtype) * elem(k_cache, base + d, dtype);
+        sc[o] = scale * dot;
+        if (sc[o] > block_max) block_max = sc[o];
+      }
+      double new_max = run_max > block_max ? run_max : block_max;
+      double correction = exp(run_max - new_max); /* exp(-inf) = 0 on the first block */
+      double block_sum = 0.0;
+      for (int d = 0; d < D; ++d) acc[d] *= correction;
+      for (int o = 0; o < valid; ++o) {
+        double e = exp(sc[o] - new_max);
+        block_sum += e;
+        int64_t base = cache_index(phys, kh, o, 0, Hkv, bs, D);
+        for (int d = 0; d < D; ++d) acc[d] += e * elem(v_cache, base + d, dtype);
+      }
+      run_sum = run_sum * correction + block_sum;
+      run_max = new_max;
+    }
+    pm[p] = run_max;
+    pl[p] = run_sum;
+  }
+  if (rc == ORC_OK) {
+    double m = -INFINITY, l = 0.0;
+    for (int p = 0; p < n_parts; ++p)
+      if (pm[p] > m) m = pm[p];
+    for (int p = 0; p < n_parts; ++p) {
+      double w = exp(pm[p] - m);
+      l += pl[p] * w;
+      for (int d = 0; d < D; ++d) out[d] += po[(int64_t)p * D + d] * w;
+    }
+    for (int d = 0; d < D; ++d) out[d] /= l;
+  }
+  free(pm); free(pl); free(po);
+  return rc;
+}
