@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode on a Llama-3.1-8B-shaped attention layer, one MI355X.
+
+One step = one decode iteration of all 32 layers of the batch: for each layer
+(its own K/V block pool, all layers sharing one block table) the new token's
+K/V rows are scattered into their slots (kv_cache_write) and the batch's
+decode queries attend to every cached token (paged_attn_decode).  32 pools of
+~160 MB rotate through HBM, so no layer's KV is still in the 256 MB
+Infinity Cache when it is read again.
+
+Printed (one JSON line): effective KV GB/s of the whole step (algorithmic bytes
+/ time, inputs resident in HBM), query tokens/s per layer, the live roofline of
+the decode call measured with HIP events on the launch stream, and the CPU
+oracle timed on a bounded sample on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode effective KV GB/s (% of HBM peak) and query tokens/s per layer"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_decode",
+                    choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
+                             "chunked_prefill"])
+    ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
+    ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class EventPairs:
+    """Start/stop HIP events recorded on the launch stream around one call."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ev = EventPairs(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, ev.mean_ms(), wall
+
+
+def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s):
+    """Time the oracle over whole passes of the batch (all sequences, one layer) on all host cores."""
+    import oracle
+    oracle.build(force=False)
+    cores = min(16, os.cpu_count() or 1)
+    B = q.shape[0]
+
+    def one(b):
+        return oracle.paged_decode(q[b:b + 1], k, v, tables[b:b + 1], lens[b:b + 1], scale)
+
+    outs = None
+    passes = 0
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as ex:
+        # order longest first so the pool stays busy
+        order = list(np.argsort(-lens))
+        while True:
+            res = dict(zip(order, ex.map(one, order)))
+            passes += 1
+            if outs is None:
+                outs = np.concatenate([res[b] for b in range(B)])
+            if time.perf_counter() - t0 >= budget_s * 0.5:
+                break
+    return outs, passes, time.perf_counter() - t0, cores
+
+
+def bench_decode(args, torch, pa, W, w, layers, partition):
+    dev = "cuda"
+    B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    lens = w.layout.seq_lens
+    max_len = int(lens.max())
+    shape = w.cache_shape()
+    # per-layer pools, drawn on the device
+    K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+    V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+    q = W.device_values((B, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
+    newk = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
+    newv = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
+    slots = torch.from_numpy(np.array([w.layout.block_tables[b, (lens[b] - 1) // w.block_size] * w.block_size
+                                       + (lens[b] - 1) % w.block_size for b in range(B)], np.int64)).to(dev)
+    bt = torch.from_numpy(w.layout.block_tables).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty(B, Hq, D, device=dev, dtype=torch.float32)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, D, max_len, partition)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    scale = w.scale
+
+    def step(ev):
+        for l in range(layers):
+            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+            s = ev.start() if ev else None
+            pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws)
+            if ev:
+                ev.stop(s)
+
+    ms_step, ms_decode, wall = time_steps(torch, step, args.steps, args.warmup)
+    dec_bytes = w.algorithmic_bytes(out_bytes=4)
+    write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
+    step_bytes = layers * (dec_bytes + write_bytes)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (ms_decode * 1e-3) / 1e9
+
+    # sampled parity + CPU baseline on layer 0 (the oracle on the host copies)
+    torch.cuda.synchronize()
+    pa.paged_attn_decode(out, q, K[0], V[0], bt, sl, scale, max_len, partition, ws)
+    torch.cuda.synchronize()
+    gpu_out = out.double().cpu().numpy()
+
+    def host(t):
+        t = t.contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        ref, passes, secs, cores = cpu_oracle_decode(host(q), host(K[0]), host(V[0]), w.layout.block_tables,
+                                                     lens, scale, args.cpu_seconds)
+        parity = float(np.max(np.abs(gpu_out - ref)))
+        cpu = {"value": round(passes * dec_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": "%d full pass(es) of layer 0 (%d sequences, %d tokens) through the fp64 C oracle, "
+                         "%.1f s, sequences spread over %d threads" % (passes, B, int(lens.sum()), secs, cores)}
+    res = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": w.block_size, "layers": layers, "total_tokens": int(lens.sum()),
+                   "max_seq_len": max_len, "partition_size": partition or 256,
+                   "num_blocks_per_layer": w.layout.num_blocks},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode call", "bytes_per_launch": dec_bytes,
+                     "avg_launch_ms": round(ms_decode, 5)},
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_layer0": parity,
+        "wall_s": round(wall, 3),
+    }
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no collectives or sharding are part of it); "
+              "got --gpus %d, WORLD_SIZE %d" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_attn_amd as pa
+    from synth import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.workload == "llama8b_decode":
+        w = W.llama8b_decode()
+        layers = args.layers or 32
+        part = 0 if args.partition < 0 else args.partition
+        res = bench_decode(args, torch, pa, W, w, layers, part)
+    elif args.workload == "llama70b_long":
+        w = W.llama70b_long()
+        layers = args.layers or 4
+        part = 512 if args.partition < 0 else args.partition
+        res = bench_decode(args, torch, pa, W, w, layers, part)
+    else:
+        raise SystemExit("workload %s: not wired into the bench yet" % args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

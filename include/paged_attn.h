@@ -1,0 +1,207 @@
+/*
+ * paged_attn.h -- C ABI of libpagedattn.so, PagedAttention for AMD MI355X (gfx950).
+ *
+ * Attention for decode and chunked-prefill queries over a KV cache kept in
+ * fixed-size physical blocks that each sequence reaches through its own
+ * block table, plus the two fused memory kernels that go with it: writing
+ * new K/V rows into their slots and copying whole blocks for copy-on-write.
+ *
+ * Sources (web pages on KV-cache management; sections named as on the page):
+ *   [L7]  Lecture 7 "KV Cache Management: PagedAttention and Mooncake"
+ *         (Stanford CS349E notes): §4.1 blocks and block table, §4.2
+ *         blockwise attention, §4.3 the three fused kernels, §5.1 fork and
+ *         copy-on-write.
+ *   [M2]  Month 2 "PagedAttention" (infra learning path, memory chapter):
+ *         §2.1 attention with a KV cache, §5.2 the per-layer block pool,
+ *         §5.4 the kernel loop over logical blocks with online softmax.
+ *   [L16] Lecture 16 "LLM Serving (1): Batching, PagedAttention,
+ *         RadixAttention" (CMU 15-779 notes): §3.3 block table and
+ *         blockwise attention merged by the online-softmax rule, §3.5
+ *         sharing and copy-on-write.
+ *   [L27] Lecture 27 "Better KV Caches: CacheGen, CacheBlend and LMCache"
+ *         (CMU 11-868 notes): §1.1 new tokens' queries attend directly to
+ *         cached K/V.
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers unless stated otherwise; the
+ *     caller owns every buffer (the library never allocates, frees or
+ *     synchronises).  Arrays are dense, row-major, in the layouts given,
+ *     16-byte aligned, and do not alias one another.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; results are ready when the stream
+ *     reaches that point.
+ *   - dtype codes: PA_F32 (IEEE fp32) or PA_BF16 (bfloat16).  q, K and V
+ *     share one dtype; accumulation is always fp32.
+ *   - KV cache layout, one layer: [num_blocks][num_kv_heads][block_size][head_dim],
+ *     K and V in separate arrays ([M2] §5.2; head-major inside a block so one
+ *     (block, head) tile is contiguous).
+ *   - Query head h reads KV head h / (num_heads / num_kv_heads) (contiguous
+ *     GQA groups).
+ *   - Return value: PA_OK, or a negative PA_ERR_* code.  Argument checks run
+ *     on the host before anything is enqueued; a failed check enqueues
+ *     nothing.  PA_ERR_LAUNCH reports a HIP launch error.  No exception
+ *     crosses the ABI.  Calls are stateless and thread-safe.
+ *   - Device-side contents (slots, block ids) are bounds-checked by the
+ *     kernels: an out-of-range slot or pair is skipped and an out-of-range
+ *     block-table entry is not dereferenced (its tokens contribute nothing),
+ *     so bad ids never fault the GPU, but the result for that sequence is then
+ *     unspecified.
+ *   - Supported shapes.  Attention calls: head_dim in {64, 128}, any
+ *     block_size >= 1, num_heads % num_kv_heads == 0 (the MFMA kernels serve
+ *     bf16 KV with head_dim 128, block_size 16 and a GQA group of at most 16;
+ *     other supported shapes run on plain vector kernels).  kv_cache_write
+ *     and block_copy: any block_size >= 1 and any head_dim whose row is a
+ *     multiple of 16 bytes.  Anything else returns PA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PA_EXPORT __attribute__((visibility("default")))
+#else
+#define PA_EXPORT
+#endif
+
+enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 };
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  PA_ERR_SHAPE = -2,       /* negative or inconsistent sizes                    */
+  PA_ERR_UNSUPPORTED = -3, /* valid but not implemented (head_dim, block size)  */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
+  PA_ERR_LAUNCH = -5       /* HIP reported an error when launching              */
+};
+
+/* Static, NUL-terminated description of a status code (host). */
+PA_EXPORT const char *pa_status_string(int status);
+
+/* PA_ABI_VERSION of the built library (host). */
+PA_EXPORT int pa_abi_version(void);
+
+/*
+ * kv_cache_write -- scatter new K/V rows into their cache slots
+ * ([L7] §4.3 first fused kernel; [L7] §4.1 and [L16] §3.3: a token lands in
+ * the next free slot of its sequence's last block).
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim], dtype
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim], dtype (written)
+ *   slot_mapping  [num_tokens] int64: slot = block * block_size + offset;
+ *                 slot < 0 skips the token (padding); slot >= num_blocks*block_size
+ *                 is out of range and skipped.
+ * For every token t with a valid slot s and every KV head h:
+ *   K[s / bs][h][s % bs][:] = key[t][h][:];  V likewise.
+ * A bit-exact copy.  Two tokens with the same slot in one call: which one
+ * wins is unspecified.  num_tokens == 0 is a no-op.
+ */
+PA_EXPORT int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
+                   const int64_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,
+                   void *stream);
+
+/*
+ * paged_attn_decode_workspace_size -- bytes of device workspace that
+ * paged_attn_decode needs for these sizes (host, pure function).
+ * partition_size 0 means the library's choice (the same choice
+ * paged_attn_decode makes).  Returns 0 when every sequence fits one
+ * partition (no workspace needed).
+ */
+PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * paged_attn_decode -- one query token per sequence attends to all of its
+ * cached tokens through the block table ([M2] §2.1 and §5.4; [L7] §4.2).
+ *
+ *   out           [num_seqs][num_heads][head_dim], out_dtype (PA_F32 or PA_BF16,
+ *                 rounded to nearest even once at the end)
+ *   q             [num_seqs][num_heads][head_dim], kv_dtype
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32: logical block j of
+ *                 sequence b lives in physical block block_tables[b][j]; only
+ *                 the first ceil(seq_lens[b] / block_size) entries are read.
+ *   seq_lens      [num_seqs] int32: tokens in the cache for each sequence,
+ *                 the current token included (its K/V are written first).
+ *                 Must be <= max_seq_len and <= max_blocks_per_seq*block_size;
+ *                 larger values are clamped to those bounds.  0 gives a zero row.
+ *   max_seq_len   host-side upper bound of seq_lens (sizes the launch grid).
+ *   scale         multiplies q.k (normally 1/sqrt(head_dim)).
+ *   partition_size  tokens per split-K partition, a multiple of block_size,
+ *                 or 0 for the library's choice.  Each partition is reduced to
+ *                 (max, sum of exponentials, unnormalised output) and the
+ *                 partitions are merged by the online-softmax rule ([L16]
+ *                 §3.3), in a fixed order, so results are bit-identical for
+ *                 any physical block permutation.
+ *   workspace     device scratch of at least
+ *                 paged_attn_decode_workspace_size(...) bytes (may be NULL when
+ *                 that size is 0).  Contents on entry are ignored.
+ * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t over the
+ * seq_lens[b] tokens of KV head h / (num_heads / num_kv_heads).
+ */
+PA_EXPORT int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                      const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * paged_attn_prefill_chunk -- causal attention of a chunk of new query
+ * tokens per sequence over the cached prefix plus the chunk itself
+ * ([L27] §1.1: the new tokens' queries attend to the cached K/V directly;
+ * the chunk's own K/V must already be in the cache, e.g. via kv_cache_write).
+ *
+ *   out           [num_query_tokens][num_heads][head_dim], out_dtype
+ *   q             [num_query_tokens][num_heads][head_dim], kv_dtype
+ *   query_start_loc [num_seqs + 1] int32, non-decreasing, query_start_loc[0] == 0:
+ *                 sequence b owns query rows query_start_loc[b] ..
+ *                 query_start_loc[b+1]-1 (n_b rows, n_b <= seq_lens[b]).
+ *   num_query_tokens  rows of q and out; rows at or beyond it are never read
+ *                 or written, whatever query_start_loc says.
+ *   seq_lens      [num_seqs] int32: tokens in the cache after the chunk.
+ *   max_query_len host-side upper bound of n_b (rows beyond it are not
+ *                 computed); max_seq_len bounds seq_lens.
+ * Row i of sequence b sits at position seq_lens[b] - n_b + i and attends to
+ * tokens 0 .. that position (inclusive).  The prefix need not end on a block
+ * boundary.
+ */
+PA_EXPORT int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                             const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *query_start_loc,
+                             const int32_t *seq_lens, int32_t num_seqs, int32_t num_query_tokens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_query_len,
+                             int32_t max_seq_len, float scale, void *stream);
+
+/*
+ * block_copy -- batched copy of whole physical blocks for copy-on-write
+ * ([L7] §4.3 third fused kernel: the copies copy-on-write needs are gathered
+ * and done in one launch; [L7] §5.1 and [L16] §3.5: a shared block is copied
+ * before a sequence writes into it).
+ *
+ *   pairs  [num_pairs][2] int64 (src, dst): K[dst] = K[src] and V[dst] = V[src]
+ *          over all num_kv_heads heads of the block.  Pairs with an id outside
+ *          [0, num_blocks) are skipped; src == dst is a no-op.  A dst may not
+ *          appear twice and no dst may be another pair's src in the same call
+ *          (the copies run concurrently).
+ * Bit-exact.  num_pairs == 0 is a no-op.
+ */
+PA_EXPORT int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_pairs,
+               int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+               int32_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,214 @@
+"""PagedAttention for AMD MI355X: Python binding of libpagedattn.so.
+
+Thin argument marshalling over the C ABI in ``include/paged_attn.h``: every
+step of the computation runs in the library's HIP kernels.  PyTorch supplies
+device memory and the stream (``torch.cuda.current_stream()``).  The functions
+have the C ABI's names; sizes are read from the tensors' shapes.
+
+There is no fallback: if the library is missing, the first call (or the
+first access to ``lib``) raises ImportError, and every call checks that its
+tensors live on a GPU.  Importing the package itself never loads the library,
+so ``python -m paged_kv_cache_attn_amd.build`` works on a fresh tree.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PA_F32", "PA_BF16", "PagedAttnError", "lib", "library_path", "pa_status_string",
+    "pa_abi_version", "kv_cache_write", "paged_attn_decode_workspace_size", "paged_attn_decode",
+    "paged_attn_prefill_chunk", "block_copy", "EXPORTED_SYMBOLS",
+]
+
+PA_F32 = 0
+PA_BF16 = 1
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
+                    "paged_attn_decode_workspace_size", "paged_attn_decode",
+                    "paged_attn_prefill_chunk", "block_copy")
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, pa_status_string(status), status))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError("libpagedattn.so is not built (run `python -m paged_kv_cache_attn_amd.build`); "
+                          "there is no fallback path")
+    L = ctypes.CDLL(library_path)
+    vp, i32, i64p, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_abi_version.argtypes = []
+    L.pa_abi_version.restype = ctypes.c_int
+    L.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [vp]
+    L.kv_cache_write.restype = ctypes.c_int
+    L.paged_attn_decode_workspace_size.argtypes = [i32] * 5
+    L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
+    L.paged_attn_decode.argtypes = ([vp, i32, vp, vp, vp, i32, vp, i32, vp] + [i32] * 7
+                                    + [ctypes.c_float, i32, vp, ctypes.c_size_t, vp])
+    L.paged_attn_decode.restype = ctypes.c_int
+    L.paged_attn_prefill_chunk.argtypes = ([vp, i32, vp, vp, vp, i32, vp, i32, vp, vp] + [i32] * 9
+                                           + [ctypes.c_float, vp])
+    L.paged_attn_prefill_chunk.restype = ctypes.c_int
+    L.block_copy.argtypes = [vp, vp, vp] + [i32] * 6 + [vp]
+    L.block_copy.restype = ctypes.c_int
+    return L
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _L()
+    raise AttributeError(name)
+
+
+def pa_status_string(status: int) -> str:
+    return _L().pa_status_string(int(status)).decode()
+
+
+def pa_abi_version() -> int:
+    return int(_L().pa_abi_version())
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev(t, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (no CPU path exists)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PagedAttnError(fn, status)
+
+
+# ----------------------------------------------------------------------------- the calls
+def kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Scatter key/value [T, Hkv, D] into the [NB, Hkv, bs, D] caches at slot_mapping (int64)."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or key.shape != value.shape or k_cache.shape != v_cache.shape:
+        raise ValueError("shape mismatch: key %s value %s cache %s" % (tuple(key.shape), tuple(value.shape),
+                                                                      tuple(k_cache.shape)))
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    dt = _dtype_code(k_cache)
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("key, value and caches must share one dtype")
+    st = _L().kv_cache_write(_dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+                            _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+                            T, NB, Hkv, bs, D, dt, _stream(stream))
+    _check("kv_cache_write", st)
+
+
+def paged_attn_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_seq_len: int,
+                                     partition_size: int = 0) -> int:
+    return int(_L().paged_attn_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len,
+                                                    partition_size))
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                      partition_size: int = 0, workspace=None, stream=None):
+    """out[B, Hq, D] (fp32 or bf16) = decode attention of q[B, Hq, D] over the paged caches.
+
+    ``workspace`` is a uint8 GPU tensor of at least
+    ``paged_attn_decode_workspace_size(B, Hq, D, max_seq_len, partition_size)`` bytes
+    (may be None when that is 0).
+    """
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, max_blocks], seq_lens [B]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and caches must share one dtype")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _L().paged_attn_decode(_dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                               _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                               _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                               _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D, bs, NB,
+                               int(max_seq_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                               _stream(stream))
+    _check("paged_attn_decode", st)
+
+
+def paged_attn_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, seq_lens,
+                             scale: float, max_query_len: int, max_seq_len: int, stream=None):
+    """out[Tq, Hq, D] = causal chunk attention of q[Tq, Hq, D] over cached prefix + chunk."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    Tq, Hq, Dq = q.shape
+    B = seq_lens.shape[0]
+    if Dq != D or tuple(out.shape) != (Tq, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(query_start_loc.shape) != (B + 1,):
+        raise ValueError("block_tables must be [B, max_blocks], query_start_loc [B+1]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and caches must share one dtype")
+    st = _L().paged_attn_prefill_chunk(_dev(out, "out"), _dtype_code(out), _dev(q, "q"),
+                                      _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                      _dtype_code(k_cache), _dev(block_tables, "block_tables", torch.int32),
+                                      block_tables.shape[1],
+                                      _dev(query_start_loc, "query_start_loc", torch.int32),
+                                      _dev(seq_lens, "seq_lens", torch.int32), B, Tq, Hq, Hkv, D, bs, NB,
+                                      int(max_query_len), int(max_seq_len), float(scale), _stream(stream))
+    _check("paged_attn_prefill_chunk", st)
+
+
+def block_copy(k_cache, v_cache, pairs, stream=None):
+    """Copy whole blocks K[dst] = K[src], V[dst] = V[src] for pairs [N, 2] (int64)."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [N, 2]")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("caches must match")
+    st = _L().block_copy(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs", torch.int64),
+                        pairs.shape[0], NB, Hkv, bs, D, _dtype_code(k_cache), _stream(stream))
+    _check("block_copy", st)

@@ -1,0 +1,193 @@
+// api.hip -- the C ABI of libpagedattn (declared in include/paged_attn.h):
+// host-side argument checks, kernel selection and launch.  Every check runs
+// before anything is enqueued; a failed check returns its code and launches
+// nothing.  No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "paged_attn.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 256;
+constexpr int kMaxGridYZ = 65535;
+
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+// Partition size (tokens) the decode call uses; 0 selects the default,
+// rounded up to a whole number of blocks.
+int64_t effective_partition(int32_t partition_size, int32_t block_size) {
+  if (partition_size > 0) return partition_size;
+  return ceil_div(kDefaultPartitionTokens, block_size) * block_size;
+}
+
+// Shape checks shared by both attention calls.
+int check_attention_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t kv_dtype,
+                           int32_t out_dtype) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(kv_dtype) || !dtype_ok(out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "negative or inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block size or grid size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
+                   const int64_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,
+                   void *stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  return launch_status(pa::launch_kv_cache_write(key, value, k_cache, v_cache, slot_mapping,
+                                                 num_tokens, num_blocks, num_kv_heads, block_size,
+                                                 head_dim, elem_bytes(dtype),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition_size < 0)
+    return 0;
+  const int64_t P = partition_size > 0 ? partition_size : kDefaultPartitionTokens;
+  const int64_t nparts = ceil_div(max_seq_len, P);
+  return pa::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)nparts);
+}
+
+int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                      const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                  num_blocks, max_blocks_per_seq, max_seq_len, kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+
+  const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
+  const int64_t P = effective_partition(partition_size, block_size);
+  const int64_t nparts = cap > 0 ? ceil_div(cap, P) : 1;
+  if (nparts > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)nparts);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_len_cap = (int)cap;
+  p.scale = scale;
+  p.part_blocks = (int)(P / block_size);
+  p.nparts_max = (int)nparts;
+  p.ws_o = need > 0 ? static_cast<float *>(workspace) : nullptr;
+  p.ws_ml = need > 0 ? static_cast<float *>(workspace) +
+                           (size_t)num_seqs * num_heads * nparts * head_dim
+                     : nullptr;
+  return launch_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                             const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *query_start_loc,
+                             const int32_t *seq_lens, int32_t num_seqs, int32_t num_query_tokens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_query_len,
+                             int32_t max_seq_len, float scale, void *stream) {
+  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                  num_blocks, max_blocks_per_seq, max_seq_len, kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  if (max_query_len < 0 || num_query_tokens < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens)
+    return PA_ERR_NULL;
+  const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
+  pa::PrefillParams p;
+  p.out = out;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.query_start_loc = query_start_loc;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_query_len = max_query_len;
+  p.num_query_tokens = num_query_tokens;
+  p.max_len_cap = (int)cap;
+  p.scale = scale;
+  return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_pairs,
+               int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+               int32_t dtype, void *stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
+  if ((int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype) / 16 > 0x7fffffff)
+    return PA_ERR_UNSUPPORTED;
+  return launch_status(pa::launch_block_copy(k_cache, v_cache, pairs, num_pairs, num_blocks,
+                                             num_kv_heads, block_size, head_dim, elem_bytes(dtype),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

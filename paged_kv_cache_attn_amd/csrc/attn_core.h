@@ -1,0 +1,101 @@
+// attn_core.h -- one wave's attention over 16-token KV blocks on MFMA (gfx950).
+//
+// A wave serves 16 query "columns" at once (the GQA group of one decode
+// token, or several chunk tokens x the group in prefill).  Per 16-token
+// block of one KV head (bf16, head_dim 128, 4 KB of K and 4 KB of V):
+//   S^T[token][col] = K_blk . Q^T      4 x v_mfma_f32_16x16x32_bf16
+//   online softmax per column (the pages' rescale rule, Month 2
+//   "PagedAttention" §5.4), in the exp2 domain
+//   O^T[dim][col] += V_blk^T . P^T     8 x v_mfma_f32_16x16x16_bf16
+// Operand placement (lane = 16r + c):
+//   K: lane loads token c, dims 32i + 8r .. +7 (i = 0..3): A of the QK MFMA;
+//   Q: lane holds column c, the same dims: B of the QK MFMA;
+//   S: lane receives tokens 4r .. 4r+3 of column c, which is exactly the
+//      P^T (B) operand layout of the 16x16x16 PV MFMA;
+//   V: lane loads tokens 4r + v (v = 0..3), dims 8c .. 8c+7, i.e. whole
+//      256-byte rows per instruction; v_perm regroups them into the V^T (A)
+//      operand {V[4r+v][8c + jj]}_v for jj = 0..7;
+//   O: acc[jj][i] = O[column c][dim 32r + 8i + jj].
+// Every quantity a column needs (its max, its sum, its correction factor)
+// lives in the lanes of that column, so only the block max crosses rows.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+struct KVTile {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+// kt, vt: start of one (block, head) tile, [16][128] bf16 each.
+__device__ __forceinline__ void load_kv_tile_d128(KVTile &t, const uint16_t *kt, const uint16_t *vt,
+                                                  int r, int c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.k[i] = ld16(kt + c * 128 + 32 * i + 8 * r);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) t.v[v] = ld16(vt + (4 * r + v) * 128 + 8 * c);
+}
+
+// Q^T operand for column c from a query row of 128 bf16 (nullptr -> zeros).
+__device__ __forceinline__ void load_q_operand_d128(bf16x8 qb[4], const uint16_t *qrow, int r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 v = qrow ? ld16(qrow + 32 * i + 8 * r) : u32x4{0u, 0u, 0u, 0u};
+    qb[i] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+struct MfmaAttnState {
+  float m;          // running max of the column, log2 domain
+  float l;          // running sum of this lane's share of the weights
+  floatx4 acc[8];   // unnormalised output, see the header comment
+
+  __device__ __forceinline__ void init() {
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One 16-token block whose first token has logical index tok0; keys with
+  // logical index >= lim are masked for this lane's column.  sl2 =
+  // scale * log2(e).
+  __device__ __forceinline__ void step(const bf16x8 qb[4], const KVTile &t, int tok0, int lim,
+                                       float sl2, int r) {
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]), qb[i], s);
+    const int tok = tok0 + 4 * r;
+    float x[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[v] = (tok + v < lim) ? s[v] * sl2 : kNegInf;
+    const float mx = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float corr = fast_exp2(m - m_use);
+    float e[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) e[v] = fast_exp2(x[v] - m_use);
+    const uint32_t pk0 = pack_bf16x2(e[0], e[1]);
+    const uint32_t pk1 = pack_bf16x2(e[2], e[3]);
+    // the sum uses the same bf16-rounded weights as the PV product
+    const float esum = (bf16_bits_to_float(pk0 & 0xffffu) + bf16_bits_to_float(pk0 >> 16)) +
+                       (bf16_bits_to_float(pk1 & 0xffffu) + bf16_bits_to_float(pk1 >> 16));
+    l = l * corr + esum;
+    m = m_new;
+    const u32x2 pb = {pk0, pk1};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const u32x2 a_lo = {pack_lo_halves(t.v[0][w2], t.v[1][w2]), pack_lo_halves(t.v[2][w2], t.v[3][w2])};
+      const u32x2 a_hi = {pack_hi_halves(t.v[0][w2], t.v[1][w2]), pack_hi_halves(t.v[2][w2], t.v[3][w2])};
+      acc[2 * w2] = mfma_16x16x16_bf16(a_lo, pb, acc[2 * w2]);
+      acc[2 * w2 + 1] = mfma_16x16x16_bf16(a_hi, pb, acc[2 * w2 + 1]);
+    }
+  }
+};
+
+}  // namespace pa

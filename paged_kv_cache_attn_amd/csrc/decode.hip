@@ -1,0 +1,325 @@
+// decode.hip -- paged attention for decode queries on gfx950.
+//
+// What is computed (Month 2 "PagedAttention" §2.1 and §5.4; Lecture 7 "KV
+// Cache Management" §4.2): for sequence b and query head h,
+//   out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t
+// over the seq_lens[b] cached tokens of KV head h / g, where token t lives at
+// offset t % bs of physical block block_tables[b][t / bs].
+//
+// How (MI355X design, not the pages' CUDA kernel):
+//   * one workgroup per (split-K partition, KV head, sequence); the whole GQA
+//     group of g query heads is served by the same workgroup, so each K/V
+//     tile is read from HBM once per group, not once per query head;
+//   * inside a wave, the g query heads are the 16 "columns" of 16x16 MFMA
+//     tiles: S^T = K_blk * Q^T (v_mfma_f32_16x16x32_bf16, K straight from
+//     global memory, 16 tokens x 128 dims per block), then
+//     O^T += V_blk^T * P^T (v_mfma_f32_16x16x16_bf16); the V^T operand is
+//     formed in registers with v_perm from 16-byte row loads, no LDS;
+//   * online softmax per column in the exp2 domain (scale*log2e folded in),
+//     the running max/sum kept per lane, so the rescale of the output tile
+//     needs no lane exchange;
+//   * the waves of a workgroup take the partition's blocks round-robin and
+//     are merged through LDS; partitions are merged by a second kernel in a
+//     fixed order (Lecture 16 "LLM Serving (1)" §3.3: the merge rule of the
+//     online softmax), so the result depends only on logical positions and
+//     is bit-identical under any physical block permutation.
+#include "attn_core.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+__device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, float v) {
+  if (out_bf16) {
+    reinterpret_cast<__bf16 *>(out)[idx] = (__bf16)v;
+  } else {
+    reinterpret_cast<float *>(out)[idx] = v;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// MFMA kernel: bf16 KV, head_dim 128, block_size 16, g <= 16.
+// Lane (r, c) = (lane >> 4, lane & 15); column c is query head kh*g + c.
+// ----------------------------------------------------------------------------
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int BS = 16;
+  const int part = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int g = p.num_heads / p.num_kv_heads;
+  const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
+  const int nblk = (L + BS - 1) / BS;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.part_blocks - 1) / p.part_blocks;
+  if (part >= nparts) return;
+  const int j0 = part * p.part_blocks;
+  const int j1 = min(j0 + p.part_blocks, nblk);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4, c = lane & 15;
+  const bool col_ok = c < g;
+
+  bf16x8 qb[4];
+  load_q_operand_d128(qb,
+                      col_ok ? reinterpret_cast<const uint16_t *>(p.q) +
+                                   ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * D
+                             : nullptr,
+                      r);
+
+  const float sl2 = p.scale * kLog2e;
+  const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(p.k_cache) + (int64_t)kh * BS * D;
+  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(p.v_cache) + (int64_t)kh * BS * D;
+  const int64_t blk_stride = (int64_t)p.num_kv_heads * BS * D;
+
+  MfmaAttnState st;
+  st.init();
+
+  // An out-of-range table entry is never dereferenced: the tile is read from
+  // block 0 and fully masked.
+  auto load = [&](int j, KVTile &t, int &lim) {
+    int phys = table[j];
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    lim = ok ? L : 0;
+    phys = ok ? phys : 0;
+    load_kv_tile_d128(t, kbase + phys * blk_stride, vbase + phys * blk_stride, r, c);
+  };
+
+  // Two-deep software pipeline: the next tile's loads are in flight while
+  // the current one is multiplied.
+  int j = j0 + w;
+  if (j < j1) {
+    KVTile cur;
+    int lim;
+    load(j, cur, lim);
+    while (true) {
+      const int jn = j + NW;
+      if (jn < j1) {
+        KVTile nxt;
+        int limn;
+        load(jn, nxt, limn);
+        st.step(qb, cur, j * BS, lim, sl2, r);
+        cur = nxt;
+        lim = limn;
+        j = jn;
+      } else {
+        st.step(qb, cur, j * BS, lim, sl2, r);
+        break;
+      }
+    }
+  }
+  float m = st.m, l = st.l;
+  floatx4 *acc = st.acc;
+
+  // Per-lane l covers this lane's tokens; sum the four rows.
+  l = row_sum4(l);
+  // acc[jj][i] = O[column c][dim 32r + 8i + jj], relative to max m.
+
+  const int64_t row = (int64_t)b * p.num_heads + (int64_t)kh * g + c;  // valid when col_ok
+  if (NW == 1) {
+    if (!col_ok) return;
+    if (nparts == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          store_out(p.out, p.out_bf16, row * D + 32 * r + 8 * i + jj, acc[jj][i] * inv);
+    } else {
+      float *wo = p.ws_o + (row * p.nparts_max + part) * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) wo[32 * r + 8 * i + jj] = acc[jj][i];
+      if (r == 0) {
+        p.ws_ml[(row * p.nparts_max + part) * 2 + 0] = m;
+        p.ws_ml[(row * p.nparts_max + part) * 2 + 1] = l;
+      }
+    }
+    return;
+  }
+
+  // Merge the NW wave states of this workgroup through LDS.
+  __shared__ float sm_o[NW][16][D];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  if (col_ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sm_o[w][c][32 * r + 8 * i + jj] = acc[jj][i];
+    if (r == 0) {
+      sm_m[w][c] = m;
+      sm_l[w][c] = l;
+    }
+  }
+  __syncthreads();
+  const int total = g * D;
+  for (int idx = threadIdx.x; idx < total; idx += 64 * NW) {
+    const int cc = idx / D, d = idx - cc * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][cc]);
+    const float M_use = M == kNegInf ? 0.f : M;
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float wgt = fast_exp2(sm_m[ww][cc] - M_use);
+      lsum += sm_l[ww][cc] * wgt;
+      o += sm_o[ww][cc][d] * wgt;
+    }
+    const int64_t rr = (int64_t)b * p.num_heads + (int64_t)kh * g + cc;
+    if (nparts == 1) {
+      store_out(p.out, p.out_bf16, rr * D + d, lsum > 0.f ? o / lsum : 0.f);
+    } else {
+      p.ws_o[(rr * p.nparts_max + part) * D + d] = o;
+      if (d == 0) {
+        p.ws_ml[(rr * p.nparts_max + part) * 2 + 0] = M;
+        p.ws_ml[(rr * p.nparts_max + part) * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Generic VALU kernel: fp32 or bf16 KV, head_dim 64 or 128, any group size.
+// One wave per (partition, query head, sequence); lane owns D/64 dims; one
+// token per step with a wave-wide dot-product reduction.
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
+  constexpr int DPL = D / 64;
+  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = p.num_heads / p.num_kv_heads;
+  const int kh = h / g;
+  const int bs = p.block_size;
+  const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
+  const int nblk = (L + bs - 1) / bs;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.part_blocks - 1) / p.part_blocks;
+  if (part >= nparts) return;
+  const int j0 = part * p.part_blocks;
+  const int j1 = min(j0 + p.part_blocks, nblk);
+  const int lane = threadIdx.x;
+
+  auto ld = [&](const void *base, int64_t idx) -> float {
+    if (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[idx]);
+    return reinterpret_cast<const float *>(base)[idx];
+  };
+
+  const int64_t row = (int64_t)b * p.num_heads + h;
+  float qv[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) qv[i] = ld(p.q, row * D + lane * DPL + i);
+  const float sl2 = p.scale * kLog2e;
+  const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+  float m = kNegInf, l = 0.f, acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+
+  for (int j = j0; j < j1; ++j) {
+    const int phys = table[j];
+    if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
+    const int valid = min(bs, L - j * bs);
+    for (int o = 0; o < valid; ++o) {
+      const int64_t base = (((int64_t)phys * p.num_kv_heads + kh) * bs + o) * D + lane * DPL;
+      float part_dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) part_dot += qv[i] * ld(p.k_cache, base + i);
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) part_dot += shfl_xor_f(part_dot, s);
+      const float t = part_dot * sl2;
+      const float m_new = fmaxf(m, t);
+      const float corr = fast_exp2(m - m_new);
+      const float e = fast_exp2(t - m_new);
+      l = l * corr + e;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * corr + e * ld(p.v_cache, base + i);
+      m = m_new;
+    }
+  }
+  if (nparts == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) store_out(p.out, p.out_bf16, row * D + lane * DPL + i, acc[i] * inv);
+  } else {
+    float *wo = p.ws_o + (row * p.nparts_max + part) * D;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) wo[lane * DPL + i] = acc[i];
+    if (lane == 0) {
+      p.ws_ml[(row * p.nparts_max + part) * 2 + 0] = m;
+      p.ws_ml[(row * p.nparts_max + part) * 2 + 1] = l;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Partition merge: one workgroup per (query head, sequence), one thread per
+// output dim; partitions combined in ascending order.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
+  const int nblk = (L + p.block_size - 1) / p.block_size;
+  const int nparts = nblk == 0 ? 1 : (nblk + p.part_blocks - 1) / p.part_blocks;
+  if (nparts <= 1) return;
+  const int64_t row = (int64_t)b * p.num_heads + h;
+  const float *ml = p.ws_ml + row * p.nparts_max * 2;
+  float M = kNegInf;
+  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+  const float M_use = M == kNegInf ? 0.f : M;
+  for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
+    float lsum = 0.f, o = 0.f;
+    for (int q = 0; q < nparts; ++q) {
+      const float wgt = fast_exp2(ml[2 * q] - M_use);
+      lsum += ml[2 * q + 1] * wgt;
+      o += p.ws_o[(row * p.nparts_max + q) * p.head_dim + d] * wgt;
+    }
+    store_out(p.out, p.out_bf16, row * p.head_dim + d, lsum > 0.f ? o / lsum : 0.f);
+  }
+}
+
+}  // namespace
+
+int decode_default_partition(int num_seqs, int num_kv_heads, int max_seq_len, int block_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_seq_len;
+  return 16 * block_size;  // 256 tokens at block size 16
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int nparts_max) {
+  if (nparts_max <= 1) return 0;
+  return (size_t)num_seqs * num_heads * nparts_max * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
+  const int g = p.num_heads / p.num_kv_heads;
+  const bool mfma = p.kv_bf16 && p.head_dim == 128 && p.block_size == 16 && g <= 16;
+  if (p.num_seqs == 0) return hipSuccess;
+  if (mfma) {
+    dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL(decode_mfma_d128_kernel<4>, grid, dim3(256), 0, stream, p);
+  } else {
+    dim3 grid(p.nparts_max, p.num_heads, p.num_seqs);
+    if (p.head_dim == 64) {
+      if (p.kv_bf16)
+        hipLaunchKernelGGL((decode_valu_kernel<64, true>), grid, dim3(64), 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_valu_kernel<64, false>), grid, dim3(64), 0, stream, p);
+    } else {
+      if (p.kv_bf16)
+        hipLaunchKernelGGL((decode_valu_kernel<128, true>), grid, dim3(64), 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_valu_kernel<128, false>), grid, dim3(64), 0, stream, p);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nparts_max <= 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_heads, p.num_seqs), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

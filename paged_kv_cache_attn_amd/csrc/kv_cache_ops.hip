@@ -1,0 +1,94 @@
+// kv_cache_ops.hip -- the two memory kernels around paged attention:
+//   kv_cache_write: scatter new K/V rows into their slots (Lecture 7 "KV Cache
+//     Management" §4.3, first fused kernel; slots follow the fill rule of
+//     §4.1 and of Lecture 16 "LLM Serving (1)" §3.3);
+//   block_copy: batched whole-block copies for copy-on-write (Lecture 7 §4.3,
+//     third fused kernel, and §5.1).
+// Both are pure HBM streams: each thread moves 16-byte chunks with
+// global_load_dwordx4 / global_store_dwordx4, consecutive threads take
+// consecutive chunks of a row so every wave touches whole 256-byte rows.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// One thread per 16-byte chunk of one (token, head) row; K and V handled by
+// the same thread.  row_chunks = head_dim * elem_bytes / 16.
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+    const uint8_t *__restrict__ key, const uint8_t *__restrict__ value,
+    uint8_t *__restrict__ k_cache, uint8_t *__restrict__ v_cache,
+    const int64_t *__restrict__ slot_mapping, int64_t total_chunks, int num_kv_heads,
+    int block_size, int row_chunks, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const int chunk = (int)(gid % row_chunks);
+  const int64_t row = gid / row_chunks;  // t * num_kv_heads + h
+  const int h = (int)(row % num_kv_heads);
+  const int64_t t = row / num_kv_heads;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot - blk * block_size);
+  const int64_t dst_row = (blk * num_kv_heads + h) * block_size + off;
+  const int64_t row_bytes = (int64_t)row_chunks * 16;
+  const int64_t src = row * row_bytes + chunk * 16;
+  const int64_t dst = dst_row * row_bytes + chunk * 16;
+  const u32x4 kv = ld16(key + src);
+  const u32x4 vv = ld16(value + src);
+  st16(k_cache + dst, kv);
+  st16(v_cache + dst, vv);
+}
+
+// grid.x = pair, grid.y = 0 (K) / 1 (V); each workgroup copies one block of
+// one cache: block_chunks 16-byte chunks, strided over 256 threads.
+__global__ __launch_bounds__(256) void block_copy_kernel(uint8_t *__restrict__ k_cache,
+                                                         uint8_t *__restrict__ v_cache,
+                                                         const int64_t *__restrict__ pairs,
+                                                         int64_t num_blocks, int block_chunks) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
+  uint8_t *cache = blockIdx.y == 0 ? k_cache : v_cache;
+  const int64_t bytes = (int64_t)block_chunks * 16;
+  const uint8_t *s = cache + src * bytes;
+  uint8_t *d = cache + dst * bytes;
+  // 4 chunks in flight per thread before the stores
+  int i = threadIdx.x;
+  for (; i + 3 * 256 < block_chunks; i += 4 * 256) {
+    u32x4 a = ld16(s + (int64_t)i * 16), b = ld16(s + (int64_t)(i + 256) * 16);
+    u32x4 c = ld16(s + (int64_t)(i + 512) * 16), e = ld16(s + (int64_t)(i + 768) * 16);
+    st16(d + (int64_t)i * 16, a);
+    st16(d + (int64_t)(i + 256) * 16, b);
+    st16(d + (int64_t)(i + 512) * 16, c);
+    st16(d + (int64_t)(i + 768) * 16, e);
+  }
+  for (; i < block_chunks; i += 256) st16(d + (int64_t)i * 16, ld16(s + (int64_t)i * 16));
+}
+
+hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
+                                 const int64_t *slot_mapping, int num_tokens, int num_blocks,
+                                 int num_kv_heads, int block_size, int head_dim, int elem_bytes,
+                                 hipStream_t stream) {
+  const int row_chunks = head_dim * elem_bytes / 16;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * row_chunks;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(kv_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint8_t *)key, (const uint8_t *)value, (uint8_t *)k_cache,
+                     (uint8_t *)v_cache, slot_mapping, total, num_kv_heads, block_size, row_chunks,
+                     (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int num_pairs,
+                             int num_blocks, int num_kv_heads, int block_size, int head_dim,
+                             int elem_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int block_chunks = num_kv_heads * block_size * head_dim * elem_bytes / 16;
+  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)num_pairs, 2), dim3(256), 0, stream,
+                     (uint8_t *)k_cache, (uint8_t *)v_cache, pairs, (int64_t)num_blocks,
+                     block_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,82 @@
+// pa_device.h -- device helpers shared by the gfx950 kernels of libpagedattn.
+//
+// Wave64 conventions used throughout: lane = threadIdx.x & 63, and the 64
+// lanes are viewed as 4 rows of 16 (r = lane >> 4, c = lane & 15), which is
+// how the 16x16 MFMA instructions distribute their operands:
+//   v_mfma_f32_16x16x32_bf16  A: lane holds A[m = c][k = 8r .. 8r+7]
+//                             B: lane holds B[k = 8r .. 8r+7][n = c]
+//   v_mfma_f32_16x16x16_bf16  A: lane holds A[m = c][k = 4r .. 4r+3]
+//                             B: lane holds B[k = 4r .. 4r+3][n = c]
+//   both                      C: lane holds C[m = 4r + i][n = c], i = 0..3
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed lo | hi << 16
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
+                                                      const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_16x16x16_bf16(const u32x2 &a, const u32x2 &b,
+                                                      const floatx4 &c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Lane-crossing helpers (wave64).  xor 16 / xor 32 exchange between rows.
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ float row_max4(float v) {
+  // max over the four rows (lanes c, c+16, c+32, c+48)
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float row_sum4(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+
+// 16-byte global load/store through a plain vector type (global_load_dwordx4).
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// Select halves of two packed-bf16 dwords: lo16(a) | lo16(b) << 16 and
+// hi16(a) | hi16(b) << 16 (v_perm_b32).
+__device__ __forceinline__ uint32_t pack_lo_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+}  // namespace pa

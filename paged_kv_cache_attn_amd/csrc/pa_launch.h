@@ -1,0 +1,68 @@
+// pa_launch.h -- host-side launchers of the gfx950 kernels (internal to
+// libpagedattn; the public C ABI is include/paged_attn.h).  Arguments are
+// assumed validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
+                                 const int64_t *slot_mapping, int num_tokens, int num_blocks,
+                                 int num_kv_heads, int block_size, int head_dim, int elem_bytes,
+                                 hipStream_t stream);
+
+hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int num_pairs,
+                             int num_blocks, int num_kv_heads, int block_size, int head_dim,
+                             int elem_bytes, hipStream_t stream);
+
+// Everything one decode launch needs.  Sizes are validated; pointers are device.
+struct DecodeParams {
+  void *out;
+  int out_bf16;            // 0: fp32 output, 1: bf16 output
+  const void *q;           // [B][Hq][D]
+  const void *k_cache;     // [NB][Hkv][bs][D]
+  const void *v_cache;
+  int kv_bf16;             // 0: fp32 KV, 1: bf16 KV
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *seq_lens;
+  int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  int max_len_cap;         // min(max_seq_len, max_blocks_per_seq * block_size)
+  float scale;
+  int part_blocks;         // blocks per split-K partition
+  int nparts_max;          // ceil(ceil(max_len_cap / bs) / part_blocks), >= 1
+  float *ws_o;             // [B][Hq][nparts_max][D]   (unused when nparts_max == 1)
+  float *ws_ml;            // [B][Hq][nparts_max][2]   (max in log2 units, sum)
+};
+
+// Library choice of split-K partition size (tokens) for these sizes.
+int decode_default_partition(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
+
+size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int nparts_max);
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
+struct PrefillParams {
+  void *out;
+  int out_bf16;
+  const void *q;           // [Tq][Hq][D]
+  const void *k_cache;
+  const void *v_cache;
+  int kv_bf16;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *query_start_loc;  // [B+1]
+  const int32_t *seq_lens;         // [B]
+  int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  int max_query_len;
+  int num_query_tokens;    // rows of q / out; rows at or beyond are never touched
+  int max_len_cap;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP kernels against the fp64 CPU oracle on identical seeded
+inputs, called through the C ABI (via the thin binding).
+
+Tolerances (max abs error): 1e-5 for fp32 KV, 2e-3 for bf16 KV (fp32 output;
+a bf16 output is compared against the oracle rounded to bf16).  Slot writes
+and block copies are compared bit for bit over the whole caches.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as W
+from gpu_helpers import TOL, bf16_round_f64, max_err, out_to_f64, require_gpu, to_gpu, to_host, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    mod = require_gpu()
+    oracle.build(force=False)
+    return mod
+
+
+def rand_problem(lens, Hq, Hkv, D, bs, dtype, seed, std=1.0, pool_factor=1.3):
+    lay = synth.build_paged_layout(lens, bs, seed=seed, pool_factor=pool_factor)
+    shape = (lay.num_blocks, Hkv, bs, D)
+    k = W.host_values(shape, std, seed * 11 + 1, dtype)
+    v = W.host_values(shape, std, seed * 11 + 2, dtype)
+    q = W.host_values((len(lens), Hq, D), std, seed * 11 + 3, dtype)
+    return lay, q, k, v
+
+
+def gpu_decode(pa, lay, q, k, v, scale, out_dtype="f32", partition_size=0):
+    torch = torch_mod()
+    B, Hq, D = q.shape
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+    bt = to_gpu(lay.block_tables.astype(np.int32))
+    sl = to_gpu(lay.seq_lens.astype(np.int32))
+    out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device="cuda")
+    max_len = max(int(lay.seq_lens.max()), 1)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, D, max_len, partition_size)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    pa.paged_attn_decode(out, qg, kg, vg, bt, sl, scale, max_len, partition_size, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+# ----------------------------------------------------------------------------- kv_cache_write / block_copy
+@pytest.mark.parametrize("dtype,D,bs", [("bf16", 128, 16), ("f32", 64, 16), ("bf16", 64, 8), ("f32", 128, 1)])
+def test_kv_cache_write_bit_exact(pa, dtype, D, bs):
+    NB, Hkv, T = 37, 4, 50
+    rng = np.random.default_rng(7)
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[[3, 17]] = -1                 # padding rows are skipped
+    slots[25] = NB * bs + 5             # out of range: skipped
+    kc = W.host_values((NB, Hkv, bs, D), 1.0, 1, dtype)
+    vc = W.host_values((NB, Hkv, bs, D), 1.0, 2, dtype)
+    key = W.host_values((T, Hkv, D), 1.0, 3, dtype)
+    val = W.host_values((T, Hkv, D), 1.0, 4, dtype)
+    kg, vg = to_gpu(kc), to_gpu(vc)
+    pa.kv_cache_write(to_gpu(key), to_gpu(val), kg, vg, to_gpu(slots))
+    torch_mod().cuda.synchronize()
+    ok_slots = slots.copy()
+    ok_slots[25] = -1
+    oracle.kv_cache_write(key, val, kc, vc, ok_slots)
+    assert np.array_equal(to_host(kg), kc)
+    assert np.array_equal(to_host(vg), vc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_copy_bit_exact(pa, dtype):
+    NB, Hkv, bs, D = 40, 8, 16, 128
+    kc = W.host_values((NB, Hkv, bs, D), 1.0, 5, dtype)
+    vc = W.host_values((NB, Hkv, bs, D), 1.0, 6, dtype)
+    pairs = np.array([[1, 30], [2, 31], [7, 7], [9, 33], [0, 39], [12, NB + 3]], np.int64)
+    kg, vg = to_gpu(kc), to_gpu(vc)
+    pa.block_copy(kg, vg, to_gpu(pairs))
+    torch_mod().cuda.synchronize()
+    oracle.block_copy(kc, vc, pairs[:-1])
+    assert np.array_equal(to_host(kg), kc)
+    assert np.array_equal(to_host(vg), vc)
+
+
+def test_empty_calls_are_noops(pa):
+    torch = torch_mod()
+    kc = torch.zeros(4, 2, 16, 64, device="cuda")
+    pa.kv_cache_write(torch.zeros(0, 2, 64, device="cuda"), torch.zeros(0, 2, 64, device="cuda"), kc,
+                      kc.clone(), torch.zeros(0, dtype=torch.int64, device="cuda"))
+    pa.block_copy(kc, kc.clone(), torch.zeros(0, 2, dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert float(kc.abs().sum()) == 0.0
+
+
+# ----------------------------------------------------------------------------- decode
+def test_decode_tiny_fp32(pa):
+    """The tiny fp32 configuration, also checked against contiguous attention."""
+    w = W.tiny_decode()
+    q = W.host_values(w.q_shape(), w.std, 101, w.dtype)
+    k = W.host_values(w.cache_shape(), w.std, 102, w.dtype)
+    v = W.host_values(w.cache_shape(), w.std, 103, w.dtype)
+    ref = oracle.paged_decode(q, k, v, w.layout.block_tables, w.layout.seq_lens, w.scale)
+    out = out_to_f64(gpu_decode(pa, w.layout, q, k, v, w.scale))
+    assert max_err(out, ref) <= TOL["f32"], max_err(out, ref)
+    for b, L in enumerate(w.layout.seq_lens):
+        rows = [(w.layout.block_tables[b, t // 16], t % 16) for t in range(L)]
+        Kc = np.stack([k[blk, :, off] for blk, off in rows]).astype(np.float64)
+        Vc = np.stack([v[blk, :, off] for blk, off in rows]).astype(np.float64)
+        cont = oracle.contiguous_attention(q[b:b + 1].astype(np.float64), Kc, Vc, [L], w.scale)[0]
+        assert max_err(out[b], cont) <= TOL["f32"]
+
+
+DECODE_CASES = [
+    # dtype, D, Hq, Hkv, out, partition
+    ("bf16", 128, 32, 8, "f32", 0),      # the 8B shape, MFMA path
+    ("bf16", 128, 64, 8, "f32", 512),    # the 70B shape (group 8), MFMA path
+    ("bf16", 128, 16, 16, "f32", 64),    # MHA (group 1), MFMA path
+    ("bf16", 128, 32, 2, "f32", 128),    # group 16, MFMA path
+    ("bf16", 128, 32, 8, "bf16", 256),   # bf16 output
+    ("bf16", 64, 8, 2, "f32", 32),       # head_dim 64 bf16 (vector path)
+    ("f32", 64, 8, 2, "f32", 48),        # fp32, vector path
+    ("f32", 128, 12, 4, "f32", 0),       # fp32, head_dim 128
+    ("bf16", 128, 24, 8, "f32", 16),     # group 3, one block per partition
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,out_dtype,part", DECODE_CASES)
+def test_decode_parity(pa, dtype, D, Hq, Hkv, out_dtype, part):
+    P = part or 256
+    lens = [1, 2, 15, 16, 17, P - 1, P, P + 1, 2 * P + 1, 3 * P + 7, 40, 5]
+    lay, q, k, v = rand_problem(lens, Hq, Hkv, D, 16, dtype, seed=D + Hq + Hkv + part)
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, scale)
+    out = out_to_f64(gpu_decode(pa, lay, q, k, v, scale, out_dtype, part))
+    if out_dtype == "bf16":
+        ref = bf16_round_f64(ref)
+    err = max_err(out, ref)
+    assert err <= TOL[dtype], "max abs err %.3e" % err
+    assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("dtype,bs", [("f32", 1), ("bf16", 8), ("bf16", 32), ("f32", 64)])
+def test_decode_other_block_sizes(pa, dtype, bs):
+    lens = [1, 7, 64, 65, 300]
+    lay, q, k, v = rand_problem(lens, 8, 2, 64, bs, dtype, seed=bs + 50)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.125)
+    out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.125, "f32", 0))
+    assert max_err(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_permutation_bit_exact(pa, dtype):
+    """Same logical K/V under another physical permutation: identical bits."""
+    D, Hq, Hkv = (128, 32, 8) if dtype == "bf16" else (64, 8, 2)
+    lens = [33, 700, 5, 1029]
+    lay, q, k, v = rand_problem(lens, Hq, Hkv, D, 16, dtype, seed=77)
+    lay2 = synth.build_paged_layout(lens, 16, seed=12345, pool_factor=1.7)
+    k2 = np.zeros((lay2.num_blocks,) + k.shape[1:], k.dtype)
+    v2 = np.zeros_like(k2)
+    for b, L in enumerate(lens):
+        for j in range((L + 15) // 16):
+            k2[lay2.block_tables[b, j]] = k[lay.block_tables[b, j]]
+            v2[lay2.block_tables[b, j]] = v[lay.block_tables[b, j]]
+    o1 = gpu_decode(pa, lay, q, k, v, 0.1, "f32", 128).cpu().numpy()
+    o2 = gpu_decode(pa, lay2, q, k2, v2, 0.1, "f32", 128).cpu().numpy()
+    assert np.array_equal(o1, o2)
+
+
+def test_decode_partition_size_independence(pa):
+    lens = [2000, 513, 1, 4096]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=91)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.09)
+    for part in (16, 64, 256, 512, 1024, 4096):
+        out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.09, "f32", part))
+        assert max_err(out, ref) <= TOL["bf16"], part
+
+
+def test_decode_zero_length_gives_zeros(pa):
+    lens = [0, 20, 0]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=5)
+    out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.1))
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.1)
+    assert max_err(out[1], ref[1]) <= TOL["bf16"]
+
+
+def test_decode_deterministic(pa):
+    lens = [100, 3000, 257]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=6)
+    o1 = gpu_decode(pa, lay, q, k, v, 0.1).cpu().numpy()
+    o2 = gpu_decode(pa, lay, q, k, v, 0.1).cpu().numpy()
+    assert np.array_equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------- prefill
+def gpu_prefill(pa, lay, chunk_lens, q, k, v, scale, out_dtype="f32"):
+    torch = torch_mod()
+    qsl = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    Tq, Hq, D = q.shape
+    out = torch.empty((Tq, Hq, D), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device="cuda")
+    pa.paged_attn_prefill_chunk(out, to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(lay.block_tables.astype(np.int32)),
+                                to_gpu(qsl), to_gpu(lay.seq_lens.astype(np.int32)), scale,
+                                int(max(chunk_lens)), int(lay.seq_lens.max()))
+    torch.cuda.synchronize()
+    return out, qsl
+
+
+PREFILL_CASES = [
+    ("bf16", 128, 32, 8),     # 8B shape: MFMA path, 4 tokens x 4 heads per wave
+    ("bf16", 128, 64, 8),     # group 8
+    ("bf16", 128, 8, 8),      # group 1
+    ("f32", 64, 8, 2),        # vector path
+    ("bf16", 128, 24, 8),     # group 3: vector path
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", PREFILL_CASES)
+def test_prefill_parity(pa, dtype, D, Hq, Hkv):
+    total = [40, 64, 17, 5, 300, 1, 129]
+    chunk = [13, 64, 1, 5, 37, 1, 128]     # chunks starting mid-block, at 0, and of one row
+    lay, _, k, v = rand_problem(total, Hq, Hkv, D, 16, dtype, seed=D + Hq)
+    q = W.host_values((sum(chunk), Hq, D), 1.0, 4242, dtype)
+    qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle.paged_prefill(q, k, v, lay.block_tables, qsl, lay.seq_lens, scale)
+    out, _ = gpu_prefill(pa, lay, chunk, q, k, v, scale)
+    err = max_err(out_to_f64(out), ref)
+    assert err <= TOL[dtype], err
+
+
+def test_prefill_one_row_equals_decode(pa):
+    lens = [77, 300, 16]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=8)
+    out_p, _ = gpu_prefill(pa, lay, [1, 1, 1], q, k, v, 0.1)
+    out_d = gpu_decode(pa, lay, q, k, v, 0.1, "f32", 16 * 1024)
+    # different wave splits round the weights differently: compare at the bf16 bar
+    assert max_err(out_to_f64(out_p), out_to_f64(out_d)) <= TOL["bf16"]
