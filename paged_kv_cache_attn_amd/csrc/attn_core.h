@@ -6,7 +6,8 @@
 //   S^T[token][col] = K_blk . Q^T      4 x v_mfma_f32_16x16x32_bf16
 //   online softmax per column (the pages' rescale rule, Month 2
 //   "PagedAttention" §5.4), in the exp2 domain
-//   O^T[dim][col] += V_blk^T . P^T     8 x v_mfma_f32_16x16x16_bf16
+//   O^T[dim][col] += V_blk^T . P^T     16 x v_mfma_f32_16x16x16_bf16 (P as
+//                                      bf16 hi + lo parts)
 // Operand placement (lane = 16r + c):
 //   K: lane loads token c, dims 32i + 8r .. +7 (i = 0..3): A of the QK MFMA;
 //   Q: lane holds column c, the same dims: B of the QK MFMA;
@@ -78,22 +79,27 @@ struct MfmaAttnState {
     float e[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) e[v] = fast_exp2(x[v] - m_use);
-    const uint32_t pk0 = pack_bf16x2(e[0], e[1]);
-    const uint32_t pk1 = pack_bf16x2(e[2], e[3]);
-    // the sum uses the same bf16-rounded weights as the PV product
-    const float esum = (bf16_bits_to_float(pk0 & 0xffffu) + bf16_bits_to_float(pk0 >> 16)) +
-                       (bf16_bits_to_float(pk1 & 0xffffu) + bf16_bits_to_float(pk1 >> 16));
-    l = l * corr + esum;
+    // The weights enter the bf16 PV product as hi + lo bf16 parts: hi is e
+    // rounded to bf16, lo is the (exactly representable) remainder rounded to
+    // bf16, so hi + lo carries e to about 2^-17 relative.
+    const uint32_t hi0 = pack_bf16x2(e[0], e[1]);
+    const uint32_t hi1 = pack_bf16x2(e[2], e[3]);
+    const uint32_t lo0 = pack_bf16x2(e[0] - bf16_bits_to_float(hi0 & 0xffffu), e[1] - bf16_bits_to_float(hi0 >> 16));
+    const uint32_t lo1 = pack_bf16x2(e[2] - bf16_bits_to_float(hi1 & 0xffffu), e[3] - bf16_bits_to_float(hi1 >> 16));
+    l = l * corr + ((e[0] + e[1]) + (e[2] + e[3]));
     m = m_new;
-    const u32x2 pb = {pk0, pk1};
+    const u32x2 pb_hi = {hi0, hi1};
+    const u32x2 pb_lo = {lo0, lo1};
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       const u32x2 a_lo = {pack_lo_halves(t.v[0][w2], t.v[1][w2]), pack_lo_halves(t.v[2][w2], t.v[3][w2])};
       const u32x2 a_hi = {pack_hi_halves(t.v[0][w2], t.v[1][w2]), pack_hi_halves(t.v[2][w2], t.v[3][w2])};
-      acc[2 * w2] = mfma_16x16x16_bf16(a_lo, pb, acc[2 * w2]);
-      acc[2 * w2 + 1] = mfma_16x16x16_bf16(a_hi, pb, acc[2 * w2 + 1]);
+      acc[2 * w2] = mfma_16x16x16_bf16(a_lo, pb_hi, acc[2 * w2]);
+      acc[2 * w2] = mfma_16x16x16_bf16(a_lo, pb_lo, acc[2 * w2]);
+      acc[2 * w2 + 1] = mfma_16x16x16_bf16(a_hi, pb_hi, acc[2 * w2 + 1]);
+      acc[2 * w2 + 1] = mfma_16x16x16_bf16(a_hi, pb_lo, acc[2 * w2 + 1]);
     }
   }
 };
