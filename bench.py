@@ -132,7 +132,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     bt = torch.from_numpy(w.layout.block_tables).to(dev)
     sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
     out = torch.empty(B, Hq, D, device=dev, dtype=torch.float32)
-    wsb = pa.paged_attn_decode_workspace_size(B, Hq, D, max_len, partition)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, w.block_size, max_len, partition)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     scale = w.scale
 

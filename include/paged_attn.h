@@ -110,13 +110,15 @@ PA_EXPORT int kv_cache_write(const void *key, const void *value, void *k_cache, 
 
 /*
  * paged_attn_decode_workspace_size -- bytes of device workspace that
- * paged_attn_decode needs for these sizes (host, pure function).
- * partition_size 0 means the library's choice (the same choice
- * paged_attn_decode makes).  Returns 0 when every sequence fits one
- * partition (no workspace needed).
+ * paged_attn_decode needs for these sizes (host, pure function; an upper
+ * bound over the kernels the call may pick).  partition_size as in
+ * paged_attn_decode.  0 means no workspace is needed.  Returns 0 for invalid
+ * sizes as well.
  */
-PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                        int32_t max_seq_len, int32_t partition_size);
+PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                                  int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t block_size, int32_t max_seq_len,
+                                                  int32_t partition_size);
 
 /*
  * paged_attn_decode -- one query token per sequence attends to all of its
@@ -135,15 +137,19 @@ PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_
  *                 larger values are clamped to those bounds.  0 gives a zero row.
  *   max_seq_len   host-side upper bound of seq_lens (sizes the launch grid).
  *   scale         multiplies q.k (normally 1/sqrt(head_dim)).
- *   partition_size  tokens per split-K partition, a multiple of block_size,
- *                 or 0 for the library's choice.  Each partition is reduced to
- *                 (max, sum of exponentials, unnormalised output) and the
- *                 partitions are merged by the online-softmax rule ([L16]
- *                 §3.3), in a fixed order, so results are bit-identical for
- *                 any physical block permutation.
+ *   partition_size  split-K granularity in tokens, a multiple of block_size,
+ *                 or 0 for the library's choice.  The KV blocks of all
+ *                 (sequence, KV head) rows are split into contiguous pieces of
+ *                 this many tokens (0: as many equal pieces as keep the GPU
+ *                 busy); each piece of a row is reduced to (max, sum of
+ *                 exponentials, unnormalised output) and the pieces are merged
+ *                 by the online-softmax rule ([L16] §3.3) in a fixed order, so
+ *                 results are bit-identical for any physical block permutation
+ *                 and agree to rounding for any partition_size.
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL when
- *                 that size is 0).  Contents on entry are ignored.
+ *                 that size is 0).  Contents on entry are ignored.  Two calls
+ *                 that may run at the same time need separate workspaces.
  * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t over the
  * seq_lens[b] tokens of KV head h / (num_heads / num_kv_heads).
  */

@@ -49,7 +49,7 @@ def _load():
     L.pa_abi_version.restype = ctypes.c_int
     L.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [vp]
     L.kv_cache_write.restype = ctypes.c_int
-    L.paged_attn_decode_workspace_size.argtypes = [i32] * 5
+    L.paged_attn_decode_workspace_size.argtypes = [i32] * 7
     L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
     L.paged_attn_decode.argtypes = ([vp, i32, vp, vp, vp, i32, vp, i32, vp] + [i32] * 7
                                     + [ctypes.c_float, i32, vp, ctypes.c_size_t, vp])
@@ -142,10 +142,10 @@ def kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check("kv_cache_write", st)
 
 
-def paged_attn_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_seq_len: int,
-                                     partition_size: int = 0) -> int:
-    return int(_L().paged_attn_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len,
-                                                    partition_size))
+def paged_attn_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                     block_size: int, max_seq_len: int, partition_size: int = 0) -> int:
+    return int(_L().paged_attn_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                    max_seq_len, partition_size))
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
@@ -153,8 +153,8 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: f
     """out[B, Hq, D] (fp32 or bf16) = decode attention of q[B, Hq, D] over the paged caches.
 
     ``workspace`` is a uint8 GPU tensor of at least
-    ``paged_attn_decode_workspace_size(B, Hq, D, max_seq_len, partition_size)`` bytes
-    (may be None when that is 0).
+    ``paged_attn_decode_workspace_size(B, Hq, Hkv, D, block_size, max_seq_len, partition_size)``
+    bytes (may be None when that is 0).
     """
     torch = _torch()
     NB, Hkv, bs, D = k_cache.shape

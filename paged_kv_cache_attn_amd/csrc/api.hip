@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "paged_attn.h"
 #include "pa_launch.h"
@@ -12,6 +13,7 @@
 namespace {
 
 constexpr int kDefaultPartitionTokens = 256;
+constexpr int64_t kStreamKMaxPiecesPerRow = 16;
 constexpr int kMaxGridYZ = 65535;
 
 int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
@@ -41,6 +43,77 @@ int check_attention_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   return PA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// How a decode call splits its work, and where its workspace pieces live.
+struct DecodePlan {
+  bool streamk = false;
+  bool too_large = false;
+  int ranges = 0, range_blocks = 0;      // balanced path
+  int part_blocks = 0, nparts = 1;       // partition-grid path
+  size_t off_part = 0, off_ml = 0, off_tickets = 0, workspace_bytes = 0;
+};
+
+DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       int max_seq_len, int64_t cap, int partition_size, bool mfma_shape) {
+  DecodePlan pl;
+  const int g = num_heads / num_kv_heads;
+  const int64_t rows = (int64_t)num_seqs * num_kv_heads;
+  const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, block_size) : 0;
+  const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
+  (void)max_seq_len;
+  // The balanced split merges a row's pieces in the workgroup that finishes
+  // last, one coherent load at a time; that is cheap for a handful of pieces
+  // per row and slow for dozens.  Estimate the pieces per row and keep the
+  // balanced split only when it is small; otherwise the partition grid with a
+  // separate merge kernel (plain loads after the kernel boundary) is faster.
+  const int64_t sk_ranges_default = std::max<int64_t>(1, std::min<int64_t>(pa::kStreamKRanges, t_upper));
+  const int64_t pieces_per_row =
+      partition_size > 0 ? ceil_div(std::max<int64_t>(blocks_per_row, 1), partition_size / block_size)
+                         : ceil_div(sk_ranges_default, std::max<int64_t>(rows, 1)) + 1;
+  if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff &&
+      pieces_per_row <= kStreamKMaxPiecesPerRow) {
+    pl.streamk = true;
+    if (partition_size > 0) {
+      pl.range_blocks = partition_size / block_size;
+      pl.ranges = (int)std::max<int64_t>(1, ceil_div(t_upper, pl.range_blocks));
+    } else {
+      pl.range_blocks = 0;
+      pl.ranges = (int)sk_ranges_default;
+    }
+    const size_t part = (size_t)pl.ranges * 2 * g * head_dim * sizeof(float);
+    const size_t ml = (size_t)pl.ranges * 2 * g * 2 * sizeof(float);
+    pl.off_part = 0;
+    pl.off_ml = align256(part);
+    pl.off_tickets = pl.off_ml + align256(ml);
+    pl.workspace_bytes = pl.off_tickets + align256((size_t)rows * sizeof(unsigned long long));
+    return pl;
+  }
+  const int64_t P = effective_partition(partition_size, block_size);
+  const int64_t nparts = cap > 0 ? ceil_div(cap, P) : 1;
+  if (nparts > 0x7fffffff) {
+    pl.too_large = true;
+    return pl;
+  }
+  pl.part_blocks = (int)(P / block_size);
+  pl.nparts = (int)nparts;
+  if (nparts > 1) {
+    const size_t o = (size_t)num_seqs * num_heads * nparts * head_dim * sizeof(float);
+    pl.off_part = 0;
+    pl.off_ml = align256(o);
+    pl.workspace_bytes = pl.off_ml + align256((size_t)num_seqs * num_heads * nparts * 2 * sizeof(float));
+  }
+  return pl;
+}
+
+// Process-wide call generation for the balanced decode's tickets (never 0).
+uint32_t next_generation() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t g = ++counter;
+  if (g == 0) g = ++counter;
+  return g;
 }
 
 }  // namespace
@@ -77,13 +150,19 @@ int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_ca
                                                  static_cast<hipStream_t>(stream)));
 }
 
-size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                        int32_t max_seq_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition_size < 0)
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                        int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_seq_len < 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
     return 0;
-  const int64_t P = partition_size > 0 ? partition_size : kDefaultPartitionTokens;
-  const int64_t nparts = ceil_div(max_seq_len, P);
-  return pa::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)nparts);
+  if (partition_size > 0 && partition_size % block_size != 0) return 0;
+  // the larger of the two kernels' needs: the dtype is not an argument here
+  DecodePlan a = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                             max_seq_len, partition_size, true);
+  DecodePlan b = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                             max_seq_len, partition_size, false);
+  return std::max(a.workspace_bytes, b.workspace_bytes);
 }
 
 int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k_cache,
@@ -102,13 +181,15 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
 
   const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
-  const int64_t P = effective_partition(partition_size, block_size);
-  const int64_t nparts = cap > 0 ? ceil_div(cap, P) : 1;
-  if (nparts > 0x7fffffff) return PA_ERR_UNSUPPORTED;
-  const size_t need = pa::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)nparts);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const bool mfma_shape = kv_dtype == PA_BF16 && head_dim == 128 && block_size == 16 &&
+                          num_heads / num_kv_heads <= 16;
+  DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                                cap, partition_size, mfma_shape);
+  if (plan.too_large) return PA_ERR_UNSUPPORTED;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return PA_ERR_WORKSPACE;
 
-  pa::DecodeParams p;
+  pa::DecodeParams p = {};
   p.out = out;
   p.out_bf16 = out_dtype == PA_BF16;
   p.q = q;
@@ -126,13 +207,22 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   p.num_blocks = num_blocks;
   p.max_len_cap = (int)cap;
   p.scale = scale;
-  p.part_blocks = (int)(P / block_size);
-  p.nparts_max = (int)nparts;
-  p.ws_o = need > 0 ? static_cast<float *>(workspace) : nullptr;
-  p.ws_ml = need > 0 ? static_cast<float *>(workspace) +
-                           (size_t)num_seqs * num_heads * nparts * head_dim
-                     : nullptr;
-  return launch_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.streamk) {
+    p.sk_ranges = plan.ranges;
+    p.sk_range_blocks = plan.range_blocks;
+    p.sk_gen = next_generation();
+    p.sk_part = reinterpret_cast<float *>(ws + plan.off_part);
+    p.sk_ml = reinterpret_cast<float *>(ws + plan.off_ml);
+    p.sk_tickets = reinterpret_cast<unsigned long long *>(ws + plan.off_tickets);
+    return launch_status(pa::launch_decode_streamk(p, s));
+  }
+  p.part_blocks = plan.part_blocks;
+  p.nparts_max = plan.nparts;
+  p.ws_o = plan.workspace_bytes > 0 ? reinterpret_cast<float *>(ws + plan.off_part) : nullptr;
+  p.ws_ml = plan.workspace_bytes > 0 ? reinterpret_cast<float *>(ws + plan.off_ml) : nullptr;
+  return launch_status(pa::launch_decode(p, s));
 }
 
 int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,

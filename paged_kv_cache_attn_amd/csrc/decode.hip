@@ -301,7 +301,8 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
   if (mfma) {
     dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL(decode_mfma_d128_kernel<4>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_mfma_d128_kernel<PA_DECODE_WAVES>, grid, dim3(64 * PA_DECODE_WAVES), 0,
+                       stream, p);
   } else {
     dim3 grid(p.nparts_max, p.num_heads, p.num_seqs);
     if (p.head_dim == 64) {

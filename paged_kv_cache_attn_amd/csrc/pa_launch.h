@@ -7,7 +7,20 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Waves per decode workgroup (they split each segment's blocks round-robin).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+
 namespace pa {
+
+// Balanced (stream-K) decode: largest batch whose per-sequence prefix fits the
+// workgroup's LDS, and the number of ranges the library picks by default.
+constexpr int kStreamKMaxSeqs = 2048;
+#ifndef PA_STREAMK_RANGES
+#define PA_STREAMK_RANGES 512
+#endif
+constexpr int kStreamKRanges = PA_STREAMK_RANGES;
 
 hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
                                  const int64_t *slot_mapping, int num_tokens, int num_blocks,
@@ -36,6 +49,13 @@ struct DecodeParams {
   int nparts_max;          // ceil(ceil(max_len_cap / bs) / part_blocks), >= 1
   float *ws_o;             // [B][Hq][nparts_max][D]   (unused when nparts_max == 1)
   float *ws_ml;            // [B][Hq][nparts_max][2]   (max in log2 units, sum)
+  // balanced (stream-K) path
+  int sk_ranges;           // workgroups = ranges of the flat block space
+  int sk_range_blocks;     // 0: T / sk_ranges blocks each (balanced); > 0: fixed
+  uint32_t sk_gen;         // call generation tagged into the tickets (never 0)
+  float *sk_part;          // [ranges][2][g][D] partial outputs
+  float *sk_ml;            // [ranges][2][g][2] partial (max, sum)
+  unsigned long long *sk_tickets;  // [B * Hkv]
 };
 
 // Library choice of split-K partition size (tokens) for these sizes.
@@ -44,6 +64,7 @@ int decode_default_partition(int num_seqs, int num_kv_heads, int max_seq_len, in
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int nparts_max);
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream);
 
 struct PrefillParams {
   void *out;

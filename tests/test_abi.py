@@ -92,17 +92,42 @@ def test_decode_validation(pa):
     assert _dec(pa, bt=N) == PA_ERR_NULL
     # 4096 tokens in 256-token partitions need a workspace
     assert _dec(pa, max_len=4096, maxblk=256) == PA_ERR_WORKSPACE
-    need = pa.paged_attn_decode_workspace_size(2, 8, 128, 4096, 0)
+    need = pa.paged_attn_decode_workspace_size(2, 8, 2, 128, 16, 4096, 0)
     assert _dec(pa, max_len=4096, maxblk=256, ws=P, ws_bytes=need - 1) == PA_ERR_WORKSPACE
     assert _dec(pa, B=0) == PA_OK
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_decode_workspace_size(pa):
     f = pa.paged_attn_decode_workspace_size
-    assert f(4, 8, 64, 203, 0) == 0                        # one partition
-    assert f(64, 32, 128, 4096, 0) == 64 * 32 * 16 * (128 + 2) * 4
-    assert f(8, 64, 128, 32768, 512) == 8 * 64 * 64 * 130 * 4
-    assert f(0, 8, 64, 100, 0) == 0
+    # 8B shape, library choice: 512 balanced ranges, 2 partial slots each, plus one ticket per row
+    B, Hq, Hkv, D, bs = 64, 32, 8, 128, 16
+    g = Hq // Hkv
+    ranges = 512
+    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256(B * Hkv * 8)
+    grid = _a256(B * Hq * 16 * D * 4) + _a256(B * Hq * 16 * 2 * 4)       # 4096 / 256 partitions
+    assert f(B, Hq, Hkv, D, bs, 4096, 0) == max(streamk, grid)
+    # fixed 512-token pieces on 32K-token rows: 64 pieces per row, so the partition grid
+    B, Hq, Hkv = 8, 64, 8
+    grid = _a256(B * Hq * 64 * D * 4) + _a256(B * Hq * 64 * 2 * 4)
+    assert f(B, Hq, Hkv, D, bs, 32768, 512) == grid
+    # fixed 4096-token pieces on the same rows: 8 pieces per row, the balanced split
+    g = Hq // Hkv
+    ranges = B * Hkv * (32768 // 16) // 256
+    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256(B * Hkv * 8)
+    grid = _a256(B * Hq * 8 * D * 4) + _a256(B * Hq * 8 * 2 * 4)
+    assert f(B, Hq, Hkv, D, bs, 32768, 4096) == max(streamk, grid)
+    # tiny problem, explicit 64-token pieces: fewer ranges than the default
+    t_up = 4 * 2 * 13
+    ranges = (t_up + 3) // 4
+    assert f(4, 8, 2, 64, 16, 203, 64) == (_a256(ranges * 2 * 4 * 64 * 4) + _a256(ranges * 2 * 4 * 2 * 4)
+                                           + _a256(4 * 2 * 8))
+    assert f(0, 8, 2, 64, 16, 100, 0) == 0
+    assert f(4, 8, 3, 64, 16, 100, 0) == 0          # invalid group
+    assert f(4, 8, 2, 64, 16, 100, 24) == 0         # partition not a block multiple
 
 
 def test_prefill_validation(pa):

@@ -42,7 +42,7 @@ def gpu_decode(pa, lay, q, k, v, scale, out_dtype="f32", partition_size=0):
     sl = to_gpu(lay.seq_lens.astype(np.int32))
     out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device="cuda")
     max_len = max(int(lay.seq_lens.max()), 1)
-    wsb = pa.paged_attn_decode_workspace_size(B, Hq, D, max_len, partition_size)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, k.shape[1], D, k.shape[2], max_len, partition_size)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
     pa.paged_attn_decode(out, qg, kg, vg, bt, sl, scale, max_len, partition_size, ws)
     torch.cuda.synchronize()
@@ -244,3 +244,61 @@ def test_prefill_one_row_equals_decode(pa):
     out_d = gpu_decode(pa, lay, q, k, v, 0.1, "f32", 16 * 1024)
     # different wave splits round the weights differently: compare at the bf16 bar
     assert max_err(out_to_f64(out_p), out_to_f64(out_d)) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- balanced decode specifics
+def test_decode_one_row_split_over_many_ranges(pa):
+    """One KV head, one long row: every 16-token block its own range, merged by the last arrival."""
+    lens = [5000]
+    lay, q, k, v = rand_problem(lens, 16, 1, 128, 16, "bf16", seed=13)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.088)
+    for part in (16, 48, 0):
+        out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.088, "f32", part))
+        assert max_err(out, ref) <= TOL["bf16"], part
+
+
+def test_decode_workspace_reuse_and_garbage(pa):
+    """Tickets are tagged with the call generation: stale or garbage workspace contents are ignored."""
+    torch = torch_mod()
+    lens = [300, 1, 0, 2048, 77, 0, 513]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=17)
+    B, Hq, D = q.shape
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+    bt, sl = to_gpu(lay.block_tables), to_gpu(lay.seq_lens)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.1)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, 8, D, 16, 2048, 32)
+    ws = torch.full((wsb,), 0xAB, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, D, device="cuda")
+    for rep in range(3):
+        out.fill_(float("nan"))
+        pa.paged_attn_decode(out, qg, kg, vg, bt, sl, 0.1, 2048, 32, ws)
+        torch.cuda.synchronize()
+        o = out_to_f64(out)
+        assert np.isfinite(o).all(), rep
+        assert max_err(o, ref) <= TOL["bf16"], rep
+        assert np.all(o[2] == 0) and np.all(o[5] == 0)
+
+
+def test_decode_partial_handoff_stress(pa):
+    """Thousands of partial rows handed between workgroups on all XCDs, repeated: every repeat
+    matches the oracle and is bit-identical to the first."""
+    torch = torch_mod()
+    lens = [4096, 3001, 4096, 17, 2500, 4096, 1, 3333]
+    lay, q, k, v = rand_problem(lens, 64, 8, 128, 16, "bf16", seed=23)
+    B, Hq, D = q.shape
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+    bt, sl = to_gpu(lay.block_tables), to_gpu(lay.seq_lens)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.09)
+    for part in (16, 32, 0):
+        wsb = pa.paged_attn_decode_workspace_size(B, Hq, 8, D, 16, 4096, part)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        out = torch.empty(B, Hq, D, device="cuda")
+        first = None
+        for rep in range(20):
+            pa.paged_attn_decode(out, qg, kg, vg, bt, sl, 0.09, 4096, part, ws)
+            o = out.cpu().numpy()
+            if first is None:
+                first = o.copy()
+                assert max_err(o.astype(np.float64), ref) <= TOL["bf16"], part
+            else:
+                assert np.array_equal(o, first), (part, rep)
