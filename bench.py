@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
                     choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
-                             "chunked_prefill"])
+                             "chunked_prefill", "copy_calibration"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
@@ -192,6 +192,27 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     return res
 
 
+def bench_copy(args, torch):
+    """A plain device copy of known size: the reference for scaling the HBM byte counters."""
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        y.copy_(x)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    return {"workload": "copy_calibration", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+            "ms_per_copy": round(ms, 4), "copy_GBs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,6 +237,8 @@ def main():
         layers = args.layers or 4
         part = 512 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part)
+    elif args.workload == "copy_calibration":
+        res = bench_copy(args, torch)
     else:
         raise SystemExit("workload %s: not wired into the bench yet" % args.workload)
     print(json.dumps(res), flush=True)

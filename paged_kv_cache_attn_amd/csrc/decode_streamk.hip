@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kBS = 16;
+constexpr int kStreamKTabCache = 1024;  // block-table entries staged per range
 
 struct SegInfo {
   int b, kh;
@@ -65,11 +66,15 @@ __device__ __forceinline__ int range_of(int x, int T, int G, int R) {
   return (int)(((int64_t)(x + 1) * G + T - 1) / T) - 1;
 }
 
+// Two waves per SIMD: with the three-slot ring that is 16 tiles (128 KB) in
+// flight per CU, enough to cover HBM latency at full bandwidth.
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void decode_streamk_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
+    DecodeParams p) {
   __shared__ int s_pref[kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
+  __shared__ int s_tab[kStreamKTabCache];      // physical block of flat positions s..
   __shared__ float sm_o[NW][16][kD];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
@@ -137,23 +142,40 @@ __global__ __launch_bounds__(64 * NW) void decode_streamk_kernel(DecodeParams p)
   if (s >= e) return;
 
   auto seg_at = [&](int pos) -> SegInfo {
-    // largest b with s_pref[b] <= pos (s_pref[B] = T > pos)
+    // largest b with s_pref[b] <= pos (s_pref[B] = T > pos); wave-uniform
     int lo = 0, hi = B;  // invariant: s_pref[lo] <= pos < s_pref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= pos) lo = mid; else hi = mid;
     }
     SegInfo S;
-    S.b = lo;
-    S.nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
-    const int off = pos - s_pref[lo];
-    S.kh = off / S.nb;
-    S.row_start = s_pref[lo] + S.kh * S.nb;
+    S.b = __builtin_amdgcn_readfirstlane(lo);
+    const int p0 = __builtin_amdgcn_readfirstlane(s_pref[S.b]);
+    S.nb = (__builtin_amdgcn_readfirstlane(s_pref[S.b + 1]) - p0) / Hkv;
+    S.kh = (pos - p0) / S.nb;
+    S.row_start = p0 + S.kh * S.nb;
     S.j0 = pos - S.row_start;
     S.j1 = min(e, S.row_start + S.nb) - S.row_start;
     S.flat_end = S.row_start + S.j1;
     return S;
   };
+
+  // Stage the physical block ids of this range in LDS (one load per block,
+  // issued together), so no tile load waits on a dependent table read.
+  const bool tab_cached = e - s <= kStreamKTabCache;
+  if (tab_cached) {
+    for (int pos = s + tid; pos < e; pos += 64 * NW) {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= pos) lo = mid; else hi = mid;
+      }
+      const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
+      const int j = (pos - s_pref[lo]) % nb;
+      s_tab[pos - s] = p.block_tables[(int64_t)lo * p.max_blocks_per_seq + j];
+    }
+  }
+  __syncthreads();
 
   // This wave's blocks: in every segment, j0 + w, j0 + w + NW, ... < j1.
   // A cursor is (segment, j); `valid` false past the range.
@@ -201,41 +223,52 @@ __global__ __launch_bounds__(64 * NW) void decode_streamk_kernel(DecodeParams p)
 
   struct Slot {
     KVTile t;
-    bf16x8 q[4];
     int lim;
   };
-  auto load_slot = [&](const Cursor &cu, Slot &sl, const Slot *prev, const Cursor *prev_cu) {
-    int phys = p.block_tables[(int64_t)cu.S.b * p.max_blocks_per_seq + cu.j];
+  auto load_slot = [&](const Cursor &cu, Slot &sl) {
+    const int pos = cu.S.row_start + cu.j;
+    int phys = tab_cached ? s_tab[pos - s] : p.block_tables[(int64_t)cu.S.b * p.max_blocks_per_seq + cu.j];
     const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
     sl.lim = ok ? s_len[cu.S.b] : 0;
     phys = ok ? phys : 0;
     const int64_t base = phys * blk_stride + (int64_t)cu.S.kh * kBS * kD;
     load_kv_tile_d128(sl.t, kc + base, vc + base, r, c);
-    if (prev && prev_cu->S.b == cu.S.b && prev_cu->S.kh == cu.S.kh) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sl.q[i] = prev->q[i];
-    } else {
-      load_q_operand_d128(
-          sl.q, col_ok ? qbase + ((int64_t)cu.S.b * p.num_heads + (int64_t)cu.S.kh * g + c) * kD : nullptr,
-          r);
-    }
   };
+  auto load_q = [&](const SegInfo &Sg, bf16x8 *qo) {
+    load_q_operand_d128(
+        qo, col_ok ? qbase + ((int64_t)Sg.b * p.num_heads + (int64_t)Sg.kh * g + c) * kD : nullptr, r);
+  };
+  Cursor none;
+  none.valid = false;
 
+  // q of the current and of the next segment (double-buffered); K/V tiles in
+  // a ring of three slots, so two tiles are in flight while one is used.
   MfmaAttnState st;
   SegInfo S = seg_at(s);
-  Cursor cur = first_in(S);
-  Slot a;
-  if (cur.valid) load_slot(cur, a, nullptr, nullptr);
+  bf16x8 qc[4], qn[4];
+  load_q(S, qc);
+  bool has_next = S.flat_end < e;
+  SegInfo Sn = S;
+  if (has_next) {
+    Sn = seg_at(S.flat_end);
+    load_q(Sn, qn);
+  }
+  Cursor c0 = first_in(S);
+  Cursor c1 = c0.valid ? advance(c0) : none;
+  Slot s0, s1, s2;
+  if (c0.valid) load_slot(c0, s0);
+  if (c1.valid) load_slot(c1, s1);
 
   while (true) {
     st.init();
-    while (cur.valid && cur.S.row_start == S.row_start && cur.S.b == S.b) {
-      const Cursor nxt = advance(cur);
-      Slot bslot;
-      if (nxt.valid) load_slot(nxt, bslot, &a, &cur);
-      st.step(a.q, a.t, cur.j * kBS, a.lim, sl2, r);
-      cur = nxt;
-      a = bslot;
+    while (c0.valid && c0.S.row_start == S.row_start) {
+      const Cursor c2 = c1.valid ? advance(c1) : none;
+      if (c2.valid) load_slot(c2, s2);
+      st.step(qc, s0.t, c0.j * kBS, s0.lim, sl2, r);
+      c0 = c1;
+      c1 = c2;
+      s0 = s1;
+      s1 = s2;
     }
 
     // -- merge the waves' states for segment S ------------------------------
@@ -308,34 +341,100 @@ __global__ __launch_bounds__(64 * NW) void decode_streamk_kernel(DecodeParams p)
       }
       __syncthreads();
       if (s_last) {
-        for (int idx = tid; idx < g * kD; idx += 64 * NW) {
-          const int cc = idx / kD, d = idx - cc * kD;
-          float M = kNegInf;
-          for (int gg = g_first; gg <= g_last; ++gg) {
-            const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-            M = fmaxf(M, coherent_load(p.sk_ml + (((int64_t)gg * 2 + sl) * g + cc) * 2 + 0));
-          }
-          const float M_use = M == kNegInf ? 0.f : M;
-          float lsum = 0.f, o = 0.f;
-          for (int gg = g_first; gg <= g_last; ++gg) {
+        // All loads of the merge are issued together: (max, sum) of every
+        // (contributor, column) is staged in LDS by one coherent load per
+        // thread, the weights are formed once per (contributor, column), and
+        // each output element fetches its contributors' partials in batches of
+        // eight independent loads.  sm_o is free to reuse here.
+        const int nc = g_last - g_first + 1;
+        float *s_cm = &sm_o[0][0][0];
+        float *s_cl = s_cm + nc * g;
+        float *s_cw = s_cl + nc * g;
+        if (3 * nc * g <= NW * 16 * kD) {
+          for (int idx = tid; idx < nc * g; idx += 64 * NW) {
+            const int k = idx / g, cc = idx - k * g;
+            const int gg = g_first + k;
             const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
             const int64_t base = ((int64_t)gg * 2 + sl) * g + cc;
-            const float wgt = fast_exp2(coherent_load(p.sk_ml + base * 2 + 0) - M_use);
-            lsum += coherent_load(p.sk_ml + base * 2 + 1) * wgt;
-            o += coherent_load(p.sk_part + base * kD + d) * wgt;
+            s_cm[idx] = coherent_load(p.sk_ml + base * 2 + 0);
+            s_cl[idx] = coherent_load(p.sk_ml + base * 2 + 1);
           }
-          const float v = lsum > 0.f ? o / lsum : 0.f;
-          const int64_t oi = (out_row0 + cc) * kD + d;
-          if (p.out_bf16)
-            reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)v;
-          else
-            reinterpret_cast<float *>(p.out)[oi] = v;
+          __syncthreads();
+          for (int cc = tid; cc < g; cc += 64 * NW) {
+            float M = kNegInf;
+            for (int k = 0; k < nc; ++k) M = fmaxf(M, s_cm[k * g + cc]);
+            const float M_use = M == kNegInf ? 0.f : M;
+            float lsum = 0.f;
+            for (int k = 0; k < nc; ++k) {
+              const float wgt = fast_exp2(s_cm[k * g + cc] - M_use);
+              s_cw[k * g + cc] = wgt;
+              lsum += s_cl[k * g + cc] * wgt;
+            }
+            s_cm[cc] = lsum;  // row sum per column (slot 0 of s_cm is no longer needed)
+          }
+          __syncthreads();
+          for (int idx = tid; idx < g * kD; idx += 64 * NW) {
+            const int cc = idx / kD, d = idx - cc * kD;
+            float o = 0.f;
+            for (int k0 = 0; k0 < nc; k0 += 8) {
+              float v[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int k = min(k0 + u, nc - 1);
+                const int gg = g_first + k;
+                const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
+                v[u] = coherent_load(p.sk_part + (((int64_t)gg * 2 + sl) * g + cc) * kD + d);
+              }
+#pragma unroll
+              for (int u = 0; u < 8; ++u)
+                if (k0 + u < nc) o += v[u] * s_cw[(k0 + u) * g + cc];
+            }
+            const float lsum = s_cm[cc];
+            const float val = lsum > 0.f ? o / lsum : 0.f;
+            const int64_t oi = (out_row0 + cc) * kD + d;
+            if (p.out_bf16)
+              reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)val;
+            else
+              reinterpret_cast<float *>(p.out)[oi] = val;
+          }
+        } else {
+          // more contributors than the staging space: plain loop
+          for (int idx = tid; idx < g * kD; idx += 64 * NW) {
+            const int cc = idx / kD, d = idx - cc * kD;
+            float M = kNegInf;
+            for (int gg = g_first; gg <= g_last; ++gg) {
+              const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
+              M = fmaxf(M, coherent_load(p.sk_ml + (((int64_t)gg * 2 + sl) * g + cc) * 2 + 0));
+            }
+            const float M_use = M == kNegInf ? 0.f : M;
+            float lsum = 0.f, o = 0.f;
+            for (int gg = g_first; gg <= g_last; ++gg) {
+              const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
+              const int64_t base = ((int64_t)gg * 2 + sl) * g + cc;
+              const float wgt = fast_exp2(coherent_load(p.sk_ml + base * 2 + 0) - M_use);
+              lsum += coherent_load(p.sk_ml + base * 2 + 1) * wgt;
+              o += coherent_load(p.sk_part + base * kD + d) * wgt;
+            }
+            const float val = lsum > 0.f ? o / lsum : 0.f;
+            const int64_t oi = (out_row0 + cc) * kD + d;
+            if (p.out_bf16)
+              reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)val;
+            else
+              reinterpret_cast<float *>(p.out)[oi] = val;
+          }
         }
       }
     }
     __syncthreads();  // sm_* and s_last are reused by the next segment
-    if (S.flat_end >= e) break;
-    S = seg_at(S.flat_end);
+    if (!has_next) break;
+    S = Sn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qc[i] = qn[i];
+    has_next = S.flat_end < e;
+    if (has_next) {
+      Sn = seg_at(S.flat_end);
+      load_q(Sn, qn);
+    }
   }
 }
 
