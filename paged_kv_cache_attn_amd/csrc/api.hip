@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "paged_attn.h"
 #include "pa_launch.h"
@@ -53,7 +52,7 @@ struct DecodePlan {
   bool too_large = false;
   int ranges = 0, range_blocks = 0;      // balanced path
   int part_blocks = 0, nparts = 1;       // partition-grid path
-  size_t off_part = 0, off_ml = 0, off_tickets = 0, workspace_bytes = 0;
+  size_t off_part = 0, off_ml = 0, off_pref = 0, workspace_bytes = 0;
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -64,17 +63,19 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, block_size) : 0;
   const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
   (void)max_seq_len;
-  // The balanced split merges a row's pieces in the workgroup that finishes
-  // last, one coherent load at a time; that is cheap for a handful of pieces
-  // per row and slow for dozens.  Estimate the pieces per row and keep the
-  // balanced split only when it is small; otherwise the partition grid with a
-  // separate merge kernel (plain loads after the kernel boundary) is faster.
-  const int64_t sk_ranges_default = std::max<int64_t>(1, std::min<int64_t>(pa::kStreamKRanges, t_upper));
+  // The balanced split pays off when the rows are many and split into few
+  // pieces; a long row cut into dozens of balanced pieces is better served by
+  // the partition grid.  Estimate the pieces per row from the host-side bound.
+  // balanced ranges: the default count, or more when that keeps every range
+  // within the blocks a workgroup can stage (t_upper bounds the real total)
+  const int64_t sk_ranges_default = std::max<int64_t>(
+      {1, std::min<int64_t>(pa::kStreamKRanges, t_upper), ceil_div(t_upper, pa::kStreamKTabCache)});
   const int64_t pieces_per_row =
       partition_size > 0 ? ceil_div(std::max<int64_t>(blocks_per_row, 1), partition_size / block_size)
                          : ceil_div(sk_ranges_default, std::max<int64_t>(rows, 1)) + 1;
   if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff &&
-      pieces_per_row <= kStreamKMaxPiecesPerRow) {
+      pieces_per_row <= kStreamKMaxPiecesPerRow &&
+      (partition_size == 0 || partition_size / block_size <= pa::kStreamKTabCache)) {
     pl.streamk = true;
     if (partition_size > 0) {
       pl.range_blocks = partition_size / block_size;
@@ -87,8 +88,8 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     const size_t ml = (size_t)pl.ranges * 2 * g * 2 * sizeof(float);
     pl.off_part = 0;
     pl.off_ml = align256(part);
-    pl.off_tickets = pl.off_ml + align256(ml);
-    pl.workspace_bytes = pl.off_tickets + align256((size_t)rows * sizeof(unsigned long long));
+    pl.off_pref = pl.off_ml + align256(ml);
+    pl.workspace_bytes = pl.off_pref + align256((size_t)(num_seqs + 1) * sizeof(int));
     return pl;
   }
   const int64_t P = effective_partition(partition_size, block_size);
@@ -106,14 +107,6 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     pl.workspace_bytes = pl.off_ml + align256((size_t)num_seqs * num_heads * nparts * 2 * sizeof(float));
   }
   return pl;
-}
-
-// Process-wide call generation for the balanced decode's tickets (never 0).
-uint32_t next_generation() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t g = ++counter;
-  if (g == 0) g = ++counter;
-  return g;
 }
 
 }  // namespace
@@ -212,10 +205,9 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   if (plan.streamk) {
     p.sk_ranges = plan.ranges;
     p.sk_range_blocks = plan.range_blocks;
-    p.sk_gen = next_generation();
     p.sk_part = reinterpret_cast<float *>(ws + plan.off_part);
     p.sk_ml = reinterpret_cast<float *>(ws + plan.off_ml);
-    p.sk_tickets = reinterpret_cast<unsigned long long *>(ws + plan.off_tickets);
+    p.sk_pref = reinterpret_cast<int *>(ws + plan.off_pref);
     return launch_status(pa::launch_decode_streamk(p, s));
   }
   p.part_blocks = plan.part_blocks;

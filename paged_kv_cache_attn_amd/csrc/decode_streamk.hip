@@ -5,28 +5,14 @@
 // one flat index space (sequence-major, then KV head, then logical block) and
 // cut into equal contiguous ranges, one per workgroup, so every workgroup
 // streams the same number of 8 KB K+V tiles whatever the length mix.  A
-// range covers whole rows (whose output it writes directly) and at most two
-// partial rows at its ends.  Each partial row leaves (max, sum, unnormalised
-// output) in the workspace; the contributor that arrives last -- decided by
-// a per-row atomic ticket -- merges the partials in ascending range order
-// with the online-softmax merge rule (Lecture 16 "LLM Serving (1)" §3.3) and
-// writes the row.  The split depends only on logical block positions, so
-// results are bit-identical under any physical block permutation, and there
-// is no second kernel launch.
-//
-// Tickets are 64-bit words (call generation << 32 | arrivals); a word whose
-// generation differs from the current call's counts as zero arrivals, so the
-// workspace needs no clearing between calls.
-//
-// Cross-workgroup hand-off without cache maintenance.  MI355X's eight XCDs
-// each have their own L2, which are not coherent with one another for plain
-// accesses; an agent-scope fence therefore writes back and invalidates the
-// whole L2 and costs microseconds.  Instead every partial is written with an
-// agent-scope atomic store (global_store ... sc1, written through to the
-// level all XCDs share), the stores are drained (s_waitcnt vmcnt(0)) before
-// the workgroup takes its ticket, and the merging workgroup reads the
-// partials with agent-scope atomic loads (global_load ... sc1), which do not
-// hit stale L2 lines.  No plain access ever touches the partials.
+// range covers whole rows, whose output it writes directly, and at most two
+// partial rows at its ends, for which it leaves (max, sum, unnormalised
+// output) in the workspace with plain stores.  A second, small kernel merges
+// the pieces of every row that spans ranges, in ascending range order, with
+// the online-softmax merge rule (Lecture 16 "LLM Serving (1)" §3.3); the
+// kernel boundary makes the pieces visible across XCDs.  The split depends
+// only on logical block positions, so results are bit-identical under any
+// physical block permutation.
 #include "attn_core.h"
 #include "pa_launch.h"
 
@@ -36,23 +22,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kBS = 16;
-constexpr int kStreamKTabCache = 1024;  // block-table entries staged per range
 
-struct SegInfo {
-  int b, kh;
-  int nb;          // blocks of the row
-  int row_start;   // flat index of the row's block 0
-  int j0, j1;      // blocks [j0, j1) of the row inside this range
-  int flat_end;    // flat index just past the segment
-};
-
-// Agent-scope relaxed atomics: coherent across XCDs without L2 maintenance.
-__device__ __forceinline__ void coherent_store(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Range of workgroup gi: [range_begin(gi), range_begin(gi + 1)).
 __device__ __forceinline__ int range_begin(int gi, int T, int G, int R) {
@@ -66,19 +36,40 @@ __device__ __forceinline__ int range_of(int x, int T, int G, int R) {
   return (int)(((int64_t)(x + 1) * G + T - 1) / T) - 1;
 }
 
+// Number of ranges actually used: balanced ranges are never more than the
+// blocks, so every range is non-empty and a row's pieces are exactly the
+// ranges between its first and last block.
+__device__ __forceinline__ int ranges_used(int grid, int T, int R) {
+  return R > 0 ? grid : max(1, min(grid, T));
+}
+
+__device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, float v) {
+  if (out_bf16)
+    reinterpret_cast<__bf16 *>(out)[i] = (__bf16)v;
+  else
+    reinterpret_cast<float *>(out)[i] = v;
+}
+
 // Two waves per SIMD: with the three-slot ring that is 16 tiles (128 KB) in
-// flight per CU, enough to cover HBM latency at full bandwidth.
+// flight per CU.
+//
+// Inside a workgroup every wave owns a contiguous quarter of the range and
+// streams it alone.  A row that lies wholly inside a wave's share is
+// finalised in registers and written out; the (at most two) rows at the ends
+// of a wave's share are parked in LDS and combined, in wave order, once all
+// waves are done.  So no barrier interrupts the stream, and runs of short
+// rows are spread evenly over the waves.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
     DecodeParams p) {
   __shared__ int s_pref[kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
-  __shared__ int s_tab[kStreamKTabCache];      // physical block of flat positions s..
-  __shared__ float sm_o[NW][16][kD];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ int s_last;
+  __shared__ int s_tab[kStreamKTabCache];      // physical block of each position of the range
+  __shared__ int s_prow[kStreamKTabCache + 1]; // row (b * Hkv + kh) of each position, -1 past the end
+  __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
+  __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
+  extern __shared__ float s_park[];            // [NW][2][g][kD + 2]: acc, then max and sum
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -102,6 +93,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       local += ((L + kBS - 1) / kBS) * Hkv;
     }
     s_scan[tid] = local;
+    if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
     __syncthreads();
     for (int off = 1; off < nt; off <<= 1) {
       const int v = tid >= off ? s_scan[tid - off] : 0;
@@ -118,101 +110,49 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __syncthreads();
   }
   const int T = s_pref[B];
-  // Balanced ranges: no more ranges than blocks, so every range is non-empty
-  // and the contributors of a row are exactly the ranges between its first and
-  // last block.  Workgroups past the last range only write zero rows.
-  const int G = R > 0 ? (int)gridDim.x : max(1, min((int)gridDim.x, T));
+  const int G = ranges_used((int)gridDim.x, T, R);
+
+  // workgroup 0 publishes the prefix for the merge kernel
+  if (gi == 0)
+    for (int b = tid; b <= B; b += 64 * NW) p.sk_pref[b] = s_pref[b];
 
   // -- rows with no tokens get zeros (spread over the workgroups) -----------
   for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
     const int b = row / Hkv, kh = row - b * Hkv;
     if (s_len[b] != 0) continue;
-    for (int idx = tid; idx < g * kD; idx += 64 * NW) {
-      const int64_t o = ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx;
-      if (p.out_bf16)
-        reinterpret_cast<__bf16 *>(p.out)[o] = (__bf16)0.f;
-      else
-        reinterpret_cast<float *>(p.out)[o] = 0.f;
-    }
+    for (int idx = tid; idx < g * kD; idx += 64 * NW)
+      store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
   }
 
   if (gi >= G) return;
   const int s = range_begin(gi, T, G, R);
   const int e = range_begin(gi + 1, T, G, R);
-  if (s >= e) return;
+  if (s >= e || e - s > kStreamKTabCache) return;  // the planner keeps ranges within the cache
 
-  auto seg_at = [&](int pos) -> SegInfo {
-    // largest b with s_pref[b] <= pos (s_pref[B] = T > pos); wave-uniform
-    int lo = 0, hi = B;  // invariant: s_pref[lo] <= pos < s_pref[hi]
+  // Stage, for every position of this range, its physical block, its row
+  // and its block index inside the row (one table load per position, all
+  // issued together), so the streaming loop does no searching and no tile
+  // load waits on a dependent table read.  The planner keeps ranges within
+  // kStreamKTabCache positions.
+  for (int pos = s + tid; pos < e; pos += 64 * NW) {
+    int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= pos) lo = mid; else hi = mid;
     }
-    SegInfo S;
-    S.b = __builtin_amdgcn_readfirstlane(lo);
-    const int p0 = __builtin_amdgcn_readfirstlane(s_pref[S.b]);
-    S.nb = (__builtin_amdgcn_readfirstlane(s_pref[S.b + 1]) - p0) / Hkv;
-    S.kh = (pos - p0) / S.nb;
-    S.row_start = p0 + S.kh * S.nb;
-    S.j0 = pos - S.row_start;
-    S.j1 = min(e, S.row_start + S.nb) - S.row_start;
-    S.flat_end = S.row_start + S.j1;
-    return S;
-  };
-
-  // Stage the physical block ids of this range in LDS (one load per block,
-  // issued together), so no tile load waits on a dependent table read.
-  const bool tab_cached = e - s <= kStreamKTabCache;
-  if (tab_cached) {
-    for (int pos = s + tid; pos < e; pos += 64 * NW) {
-      int lo = 0, hi = B;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= pos) lo = mid; else hi = mid;
-      }
-      const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
-      const int j = (pos - s_pref[lo]) % nb;
-      s_tab[pos - s] = p.block_tables[(int64_t)lo * p.max_blocks_per_seq + j];
-    }
+    const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
+    const int off = pos - s_pref[lo];
+    const int kh = off / nb, j = off - kh * nb;
+    s_tab[pos - s] = p.block_tables[(int64_t)lo * p.max_blocks_per_seq + j];
+    s_prow[pos - s] = lo * Hkv + kh;
+    s_pj[pos - s] = j;
   }
+  if (tid == 0) s_prow[e - s] = -1;
   __syncthreads();
 
-  // This wave's blocks: in every segment, j0 + w, j0 + w + NW, ... < j1.
-  // A cursor is (segment, j); `valid` false past the range.
-  struct Cursor {
-    SegInfo S;
-    int j;
-    bool valid;
-  };
-  auto first_in = [&](SegInfo S) -> Cursor {
-    Cursor cu;
-    while (true) {
-      if (S.j0 + w < S.j1) {
-        cu.S = S;
-        cu.j = S.j0 + w;
-        cu.valid = true;
-        return cu;
-      }
-      if (S.flat_end >= e) {
-        cu.valid = false;
-        return cu;
-      }
-      S = seg_at(S.flat_end);
-    }
-  };
-  auto advance = [&](const Cursor &cu) -> Cursor {
-    if (cu.j + NW < cu.S.j1) {
-      Cursor n = cu;
-      n.j += NW;
-      return n;
-    }
-    if (cu.S.flat_end >= e) {
-      Cursor n;
-      n.valid = false;
-      return n;
-    }
-    return first_in(seg_at(cu.S.flat_end));
-  };
+  // this wave's share of the range, in local positions [ls, le)
+  const int ls = (int)((int64_t)(e - s) * w / NW);
+  const int le = (int)((int64_t)(e - s) * (w + 1) / NW);
 
   const float sl2 = p.scale * kLog2e;
   const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
@@ -220,220 +160,240 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(p.q);
   const int64_t blk_stride = (int64_t)Hkv * kBS * kD;
   const bool col_ok = c < g;
+  const int c_ld = c < g ? c : g - 1;  // idle columns read a valid row, never stored
 
+  // A slot holds one tile and the q operand of its row, loaded together at
+  // the same prefetch distance.  An out-of-range table entry is never
+  // dereferenced: the tile is read from block 0 and fully masked.
   struct Slot {
     KVTile t;
+    bf16x8 q[4];
     int lim;
   };
-  auto load_slot = [&](const Cursor &cu, Slot &sl) {
-    const int pos = cu.S.row_start + cu.j;
-    int phys = tab_cached ? s_tab[pos - s] : p.block_tables[(int64_t)cu.S.b * p.max_blocks_per_seq + cu.j];
+  auto load_slot = [&](int li, Slot &sl) {
+    li = li < le ? li : le - 1;  // past the share: reload the last tile (unused)
+    int phys = s_tab[li];
+    const int row = s_prow[li];
+    const int b = row / Hkv, kh = row - b * Hkv;
     const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
-    sl.lim = ok ? s_len[cu.S.b] : 0;
+    sl.lim = ok ? s_len[b] : 0;
     phys = ok ? phys : 0;
-    const int64_t base = phys * blk_stride + (int64_t)cu.S.kh * kBS * kD;
+    const int64_t base = phys * blk_stride + (int64_t)kh * kBS * kD;
     load_kv_tile_d128(sl.t, kc + base, vc + base, r, c);
+    load_q_operand_d128(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
   };
-  auto load_q = [&](const SegInfo &Sg, bf16x8 *qo) {
-    load_q_operand_d128(
-        qo, col_ok ? qbase + ((int64_t)Sg.b * p.num_heads + (int64_t)Sg.kh * g + c) * kD : nullptr, r);
-  };
-  Cursor none;
-  none.valid = false;
 
-  // q of the current and of the next segment (double-buffered); K/V tiles in
-  // a ring of three slots, so two tiles are in flight while one is used.
-  MfmaAttnState st;
-  SegInfo S = seg_at(s);
-  bf16x8 qc[4], qn[4];
-  load_q(S, qc);
-  bool has_next = S.flat_end < e;
-  SegInfo Sn = S;
-  if (has_next) {
-    Sn = seg_at(S.flat_end);
-    load_q(Sn, qn);
-  }
-  Cursor c0 = first_in(S);
-  Cursor c1 = c0.valid ? advance(c0) : none;
-  Slot s0, s1, s2;
-  if (c0.valid) load_slot(c0, s0);
-  if (c1.valid) load_slot(c1, s1);
-
-  while (true) {
+  if (ls < le) {
+    MfmaAttnState st;
     st.init();
-    while (c0.valid && c0.S.row_start == S.row_start) {
-      const Cursor c2 = c1.valid ? advance(c1) : none;
-      if (c2.valid) load_slot(c2, s2);
-      st.step(qc, s0.t, c0.j * kBS, s0.lim, sl2, r);
-      c0 = c1;
-      c1 = c2;
-      s0 = s1;
-      s1 = s2;
+    int slot_used = 0;
+    int seg_j0 = s_pj[ls];  // first block of the current row inside this share
+    // close the current row if position li was its last one in the share;
+    // returns false when the share is done
+    auto after_step = [&](int li) -> bool {
+      const int row = s_prow[li];
+      const bool row_end = li + 1 == le || s_prow[li + 1] != row;
+      if (!row_end) return true;
+      const int b = row / Hkv, kh = row - b * Hkv;
+      const int nb = (s_pref[b + 1] - s_pref[b]) / Hkv;
+      const float lw = row_sum4(st.l);
+      const bool whole = seg_j0 == 0 && s_pj[li] == nb - 1;
+      if (whole) {
+        if (col_ok) {
+          const float inv = lw > 0.f ? 1.f / lw : 0.f;
+          const int64_t orow = ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * kD;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+              store_value(p.out, p.out_bf16, orow + 32 * r + 8 * i + jj, st.acc[jj][i] * inv);
+        }
+      } else {
+        // a wave has at most two boundary rows: its first and its last
+        const int k = slot_used++;
+        float *pc = s_park + (((size_t)w * 2 + k) * g + (col_ok ? c : 0)) * (kD + 2);
+        if (col_ok) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) pc[32 * r + 8 * i + jj] = st.acc[jj][i];
+          if (r == 0) {
+            pc[kD] = st.m;
+            pc[kD + 1] = lw;
+          }
+        }
+        if (lane == 0) s_brow[w][k] = s_pref[b] + kh * nb;
+      }
+      if (li + 1 == le) return false;
+      seg_j0 = s_pj[li + 1];
+      st.init();
+      return true;
+    };
+    // Three fixed slots: position li lives in slot li mod 3 (counting from
+    // ls), so no tile register is copied while its load is in flight.
+    Slot sa, sb, sc;
+    load_slot(ls, sa);
+    load_slot(ls + 1, sb);
+    for (int li = ls;;) {
+      load_slot(li + 2, sc);
+      st.step(sa.q, sa.t, s_pj[li] * kBS, sa.lim, sl2, r);
+      if (!after_step(li++)) break;
+      load_slot(li + 2, sa);
+      st.step(sb.q, sb.t, s_pj[li] * kBS, sb.lim, sl2, r);
+      if (!after_step(li++)) break;
+      load_slot(li + 2, sb);
+      st.step(sc.q, sc.t, s_pj[li] * kBS, sc.lim, sl2, r);
+      if (!after_step(li++)) break;
     }
+  }
+  __syncthreads();
 
-    // -- merge the waves' states for segment S ------------------------------
-    const float lw = row_sum4(st.l);
-    if (col_ok) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sm_o[w][c][32 * r + 8 * i + jj] = st.acc[jj][i];
-      if (r == 0) {
-        sm_m[w][c] = st.m;
-        sm_l[w][c] = lw;
+  // -- combine the parked boundary rows, in wave order -----------------------
+  // Entries (w, k) in order form runs of equal row start; each run is one row.
+  for (int w0 = 0, k0 = 0; w0 < NW;) {
+    const int row_start = s_brow[w0][k0];
+    if (row_start < 0) {  // empty slot: advance
+      if (++k0 == 2) { k0 = 0; ++w0; }
+      continue;
+    }
+    // extent of the run
+    int w1 = w0, k1 = k0;  // last entry of the run (inclusive)
+    {
+      int wn = w0, kn = k0;
+      while (true) {
+        if (++kn == 2) { kn = 0; ++wn; }
+        if (wn >= NW) break;
+        const int rs = s_brow[wn][kn];
+        if (rs < 0) continue;
+        if (rs != row_start) break;
+        w1 = wn;
+        k1 = kn;
       }
     }
-    __syncthreads();
-    const bool whole = S.j0 == 0 && S.j1 == S.nb;
-    const int row = S.b * Hkv + S.kh;
-    const int64_t out_row0 = (int64_t)S.b * p.num_heads + (int64_t)S.kh * g;
-    const int slot = S.row_start <= s ? 0 : 1;
+    const int b = [&] {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= row_start) lo = mid; else hi = mid;
+      }
+      return lo;
+    }();
+    const int nb = (s_pref[b + 1] - s_pref[b]) / Hkv;
+    const int kh = (row_start - s_pref[b]) / nb;
+    const bool whole = row_start >= s && row_start + nb <= e;
+    const int slot = row_start <= s ? 0 : 1;
+    const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
     for (int idx = tid; idx < g * kD; idx += 64 * NW) {
       const int cc = idx / kD, d = idx - cc * kD;
       float M = kNegInf;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][cc]);
+      for (int ww = w0, kk = k0;;) {
+        if (s_brow[ww][kk] == row_start)
+          M = fmaxf(M, s_park[(((size_t)ww * 2 + kk) * g + cc) * (kD + 2) + kD]);
+        if (ww == w1 && kk == k1) break;
+        if (++kk == 2) { kk = 0; ++ww; }
+      }
       const float M_use = M == kNegInf ? 0.f : M;
       float lsum = 0.f, o = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float wgt = fast_exp2(sm_m[ww][cc] - M_use);
-        lsum += sm_l[ww][cc] * wgt;
-        o += sm_o[ww][cc][d] * wgt;
+      for (int ww = w0, kk = k0;;) {
+        if (s_brow[ww][kk] == row_start) {
+          const float *pc = s_park + (((size_t)ww * 2 + kk) * g + cc) * (kD + 2);
+          const float wgt = fast_exp2(pc[kD] - M_use);
+          lsum += pc[kD + 1] * wgt;
+          o += pc[d] * wgt;
+        }
+        if (ww == w1 && kk == k1) break;
+        if (++kk == 2) { kk = 0; ++ww; }
       }
       if (whole) {
-        const float v = lsum > 0.f ? o / lsum : 0.f;
-        const int64_t oi = (out_row0 + cc) * kD + d;
-        if (p.out_bf16)
-          reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)v;
-        else
-          reinterpret_cast<float *>(p.out)[oi] = v;
+        store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o / lsum : 0.f);
       } else {
         const int64_t base = ((int64_t)gi * 2 + slot) * g + cc;
-        coherent_store(p.sk_part + base * kD + d, o);
+        p.sk_part[base * kD + d] = o;
         if (d == 0) {
-          coherent_store(p.sk_ml + base * 2 + 0, M);
-          coherent_store(p.sk_ml + base * 2 + 1, lsum);
+          p.sk_ml[base * 2 + 0] = M;
+          p.sk_ml[base * 2 + 1] = lsum;
         }
       }
     }
+    // next run
+    w0 = w1;
+    k0 = k1;
+    if (++k0 == 2) { k0 = 0; ++w0; }
+  }
+}
 
-    if (!whole) {
-      // publish this partial (stores drained), then take a ticket; the last
-      // arrival merges
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      const int g_first = range_of(S.row_start, T, G, R);
-      const int g_last = range_of(S.row_start + S.nb - 1, T, G, R);
-      if (tid == 0) {
-        const unsigned long long gen = (unsigned long long)p.sk_gen << 32;
-        unsigned long long *tk = p.sk_tickets + row;
-        unsigned long long old = __hip_atomic_load(tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned long long arrived;
-        while (true) {
-          arrived = ((old >> 32) == (unsigned long long)p.sk_gen) ? (old & 0xffffffffull) : 0ull;
-          const unsigned long long want = gen | (arrived + 1);
-          const unsigned long long seen = atomicCAS(tk, old, want);
-          if (seen == old) break;
-          old = seen;
-        }
-        s_last = (int)(arrived + 1) == (g_last - g_first + 1);
-      }
-      __syncthreads();
-      if (s_last) {
-        // All loads of the merge are issued together: (max, sum) of every
-        // (contributor, column) is staged in LDS by one coherent load per
-        // thread, the weights are formed once per (contributor, column), and
-        // each output element fetches its contributors' partials in batches of
-        // eight independent loads.  sm_o is free to reuse here.
-        const int nc = g_last - g_first + 1;
-        float *s_cm = &sm_o[0][0][0];
-        float *s_cl = s_cm + nc * g;
-        float *s_cw = s_cl + nc * g;
-        if (3 * nc * g <= NW * 16 * kD) {
-          for (int idx = tid; idx < nc * g; idx += 64 * NW) {
-            const int k = idx / g, cc = idx - k * g;
-            const int gg = g_first + k;
-            const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-            const int64_t base = ((int64_t)gg * 2 + sl) * g + cc;
-            s_cm[idx] = coherent_load(p.sk_ml + base * 2 + 0);
-            s_cl[idx] = coherent_load(p.sk_ml + base * 2 + 1);
-          }
-          __syncthreads();
-          for (int cc = tid; cc < g; cc += 64 * NW) {
-            float M = kNegInf;
-            for (int k = 0; k < nc; ++k) M = fmaxf(M, s_cm[k * g + cc]);
-            const float M_use = M == kNegInf ? 0.f : M;
-            float lsum = 0.f;
-            for (int k = 0; k < nc; ++k) {
-              const float wgt = fast_exp2(s_cm[k * g + cc] - M_use);
-              s_cw[k * g + cc] = wgt;
-              lsum += s_cl[k * g + cc] * wgt;
-            }
-            s_cm[cc] = lsum;  // row sum per column (slot 0 of s_cm is no longer needed)
-          }
-          __syncthreads();
-          for (int idx = tid; idx < g * kD; idx += 64 * NW) {
-            const int cc = idx / kD, d = idx - cc * kD;
-            float o = 0.f;
-            for (int k0 = 0; k0 < nc; k0 += 8) {
-              float v[8];
+// One workgroup per (sequence, KV head) row; rows that fit one range were
+// written by the main kernel and are skipped.  Pieces are combined in
+// ascending range order, in chunks of 64 pieces.
+__global__ __launch_bounds__(256) void decode_streamk_merge_kernel(DecodeParams p) {
+  constexpr int kChunk = 64;
+  __shared__ float s_w[kChunk][16];  // weight of each (piece, column)
+  __shared__ float s_M[16];
+  __shared__ float s_lsum[16];
+  const int row = blockIdx.x;
+  const int Hkv = p.num_kv_heads;
+  const int g = p.num_heads / Hkv;
+  const int b = row / Hkv, kh = row - b * Hkv;
+  const int B = p.num_seqs;
+  const int T = p.sk_pref[B];
+  const int p0 = p.sk_pref[b];
+  const int nb = (p.sk_pref[b + 1] - p0) / Hkv;
+  if (nb == 0) return;
+  const int R = p.sk_range_blocks;
+  const int G = ranges_used(p.sk_ranges, T, R);
+  const int row_start = p0 + kh * nb;
+  const int g_first = range_of(row_start, T, G, R);
+  const int g_last = range_of(row_start + nb - 1, T, G, R);
+  if (g_first == g_last) return;
+  const int nc = g_last - g_first + 1;
+  const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+  auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
+    const int gg = g_first + k;
+    const int sl = row_start <= range_begin(gg, T, G, R) ? 0 : 1;
+    return ((int64_t)gg * 2 + sl) * g + cc;
+  };
+
+  for (int cc = threadIdx.x; cc < g; cc += blockDim.x) {
+    float M = kNegInf;
+    for (int k = 0; k < nc; ++k) M = fmaxf(M, p.sk_ml[piece(k, cc) * 2]);
+    s_M[cc] = M == kNegInf ? 0.f : M;
+    s_lsum[cc] = 0.f;
+  }
+  __syncthreads();
+  float acc[8];
 #pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                const int k = min(k0 + u, nc - 1);
-                const int gg = g_first + k;
-                const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-                v[u] = coherent_load(p.sk_part + (((int64_t)gg * 2 + sl) * g + cc) * kD + d);
-              }
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  for (int k0 = 0; k0 < nc; k0 += kChunk) {
+    const int n = min(kChunk, nc - k0);
+    for (int idx = threadIdx.x; idx < n * g; idx += blockDim.x) {
+      const int k = idx / g, cc = idx - k * g;
+      s_w[k][cc] = fast_exp2(p.sk_ml[piece(k0 + k, cc) * 2] - s_M[cc]);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < g) {
+      float ls = 0.f;
+      for (int k = 0; k < n; ++k) ls += p.sk_ml[piece(k0 + k, threadIdx.x) * 2 + 1] * s_w[k][threadIdx.x];
+      s_lsum[threadIdx.x] += ls;
+    }
 #pragma unroll
-              for (int u = 0; u < 8; ++u)
-                if (k0 + u < nc) o += v[u] * s_cw[(k0 + u) * g + cc];
-            }
-            const float lsum = s_cm[cc];
-            const float val = lsum > 0.f ? o / lsum : 0.f;
-            const int64_t oi = (out_row0 + cc) * kD + d;
-            if (p.out_bf16)
-              reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)val;
-            else
-              reinterpret_cast<float *>(p.out)[oi] = val;
-          }
-        } else {
-          // more contributors than the staging space: plain loop
-          for (int idx = tid; idx < g * kD; idx += 64 * NW) {
-            const int cc = idx / kD, d = idx - cc * kD;
-            float M = kNegInf;
-            for (int gg = g_first; gg <= g_last; ++gg) {
-              const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-              M = fmaxf(M, coherent_load(p.sk_ml + (((int64_t)gg * 2 + sl) * g + cc) * 2 + 0));
-            }
-            const float M_use = M == kNegInf ? 0.f : M;
-            float lsum = 0.f, o = 0.f;
-            for (int gg = g_first; gg <= g_last; ++gg) {
-              const int sl = S.row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-              const int64_t base = ((int64_t)gg * 2 + sl) * g + cc;
-              const float wgt = fast_exp2(coherent_load(p.sk_ml + base * 2 + 0) - M_use);
-              lsum += coherent_load(p.sk_ml + base * 2 + 1) * wgt;
-              o += coherent_load(p.sk_part + base * kD + d) * wgt;
-            }
-            const float val = lsum > 0.f ? o / lsum : 0.f;
-            const int64_t oi = (out_row0 + cc) * kD + d;
-            if (p.out_bf16)
-              reinterpret_cast<__bf16 *>(p.out)[oi] = (__bf16)val;
-            else
-              reinterpret_cast<float *>(p.out)[oi] = val;
-          }
-        }
+    for (int u = 0; u < 8; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      if (idx < g * kD) {
+        const int cc = idx / kD, d = idx - cc * kD;
+        float o = 0.f;
+        for (int k = 0; k < n; ++k) o += p.sk_part[piece(k0 + k, cc) * kD + d] * s_w[k][cc];
+        acc[u] += o;
       }
     }
-    __syncthreads();  // sm_* and s_last are reused by the next segment
-    if (!has_next) break;
-    S = Sn;
+    __syncthreads();
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qc[i] = qn[i];
-    has_next = S.flat_end < e;
-    if (has_next) {
-      Sn = seg_at(S.flat_end);
-      load_q(Sn, qn);
+  for (int u = 0; u < 8; ++u) {
+    const int idx = threadIdx.x + u * 256;
+    if (idx < g * kD) {
+      const int cc = idx / kD, d = idx - cc * kD;
+      const float ls = s_lsum[cc];
+      store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? acc[u] / ls : 0.f);
     }
   }
 }
@@ -441,8 +401,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }  // namespace
 
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
+  const int g = p.num_heads / p.num_kv_heads;
+  const size_t park = (size_t)PA_DECODE_WAVES * 2 * g * (kD + 2) * sizeof(float);
   hipLaunchKernelGGL(decode_streamk_kernel<PA_DECODE_WAVES>, dim3(p.sk_ranges), dim3(64 * PA_DECODE_WAVES),
-                     0, stream, p);
+                     park, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.num_seqs * p.num_kv_heads), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

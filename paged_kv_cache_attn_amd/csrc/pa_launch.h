@@ -21,6 +21,8 @@ constexpr int kStreamKMaxSeqs = 2048;
 #define PA_STREAMK_RANGES 512
 #endif
 constexpr int kStreamKRanges = PA_STREAMK_RANGES;
+// Largest range (in blocks) a balanced-decode workgroup stages in LDS.
+constexpr int kStreamKTabCache = 1024;
 
 hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
                                  const int64_t *slot_mapping, int num_tokens, int num_blocks,
@@ -52,10 +54,9 @@ struct DecodeParams {
   // balanced (stream-K) path
   int sk_ranges;           // workgroups = ranges of the flat block space
   int sk_range_blocks;     // 0: T / sk_ranges blocks each (balanced); > 0: fixed
-  uint32_t sk_gen;         // call generation tagged into the tickets (never 0)
   float *sk_part;          // [ranges][2][g][D] partial outputs
   float *sk_ml;            // [ranges][2][g][2] partial (max, sum)
-  unsigned long long *sk_tickets;  // [B * Hkv]
+  int *sk_pref;            // [B + 1] first flat block of each sequence
 };
 
 // Library choice of split-K partition size (tokens) for these sizes.
