@@ -192,6 +192,170 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     return res
 
 
+def host_copy(torch, t):
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def bench_prefill(args, torch, pa, W, w, layers):
+    """Chunked prefill: per layer, write the chunk's K/V rows, then causal chunk attention."""
+    dev = "cuda"
+    B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    Tq = w.num_query_tokens
+    shape = (w.layout.num_blocks, Hkv, w.layout.block_size, D)
+    K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+    V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+    q = W.device_values((Tq, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
+    newk = W.device_values((Tq, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
+    newv = W.device_values((Tq, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
+    slots = torch.from_numpy(w.chunk_slots()).to(dev)
+    bt = torch.from_numpy(w.layout.block_tables).to(dev)
+    sl = torch.from_numpy(w.layout.seq_lens.astype(np.int32)).to(dev)
+    qsl = torch.from_numpy(w.query_start_loc).to(dev)
+    out = torch.empty(Tq, Hq, D, device=dev, dtype=torch.float32)
+    max_q, max_len = int(w.chunk_lens.max()), int(w.layout.seq_lens.max())
+
+    def step(ev):
+        for l in range(layers):
+            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+            s_ = ev.start() if ev else None
+            pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len)
+            if ev:
+                ev.stop(s_)
+
+    ms_step, ms_call, wall = time_steps(torch, step, args.steps, args.warmup)
+    flops = w.flops()
+    tflops = flops / (ms_call * 1e-3) / 1e12
+    # sampled parity: the last 8 rows of sequence 0 and the first 8 rows of the last sequence,
+    # each checked as a chunk of its own (a chunk's rows depend only on their positions)
+    pa.paged_attn_prefill_chunk(out, q, K[0], V[0], bt, qsl, sl, w.scale, max_q, max_len)
+    torch.cuda.synchronize()
+    import oracle
+    oracle.build(force=False)
+    hq, hk, hv = host_copy(torch, q), host_copy(torch, K[0]), host_copy(torch, V[0])
+    qsl_h = w.query_start_loc
+    errs = []
+    for b, (i0, i1) in ((0, (504, 512)), (B - 1, (0, 8))):
+        S, n = int(w.layout.seq_lens[b]), int(w.chunk_lens[b])
+        rows = slice(qsl_h[b] + i0, qsl_h[b] + i1)
+        ref = oracle.paged_prefill(hq[rows], hk, hv, w.layout.block_tables[b:b + 1], np.array([0, i1 - i0], np.int32),
+                                   np.array([S - n + i1], np.int32), w.scale)
+        errs.append(float(np.max(np.abs(out[rows].double().cpu().numpy() - ref))))
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        rows_done = 0
+        cores = min(16, os.cpu_count() or 1)
+        b = 0
+        S, n = int(w.layout.seq_lens[b]), int(w.chunk_lens[b])
+
+        def one(i):
+            r_ = slice(qsl_h[b] + i, qsl_h[b] + i + 1)
+            return oracle.paged_prefill(hq[r_], hk, hv, w.layout.block_tables[b:b + 1], np.array([0, 1], np.int32),
+                                        np.array([S - n + i + 1], np.int32), w.scale)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as ex:
+            i = 0
+            while time.perf_counter() - t0 < args.cpu_seconds * 0.5 and i < n:
+                list(ex.map(one, range(i, min(i + 64, n))))
+                rows_done += min(64, n - i)
+                i += 64
+        secs = time.perf_counter() - t0
+        keys = sum((S - n + i + 1) for i in range(rows_done))
+        cpu = {"value": round(4.0 * keys * Hq * D / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+               "kind": "oracle",
+               "sample": "%d chunk rows of sequence 0 (all %d query heads) through the fp64 C oracle, %.1f s, "
+                         "rows spread over %d threads" % (rows_done, Hq, secs, cores)}
+    return {
+        "metric": "chunked prefill attention TFLOP/s and query tokens/s per layer", "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "prefix": int(w.layout.seq_lens[0] - w.chunk_lens[0]),
+                   "chunk": int(w.chunk_lens[0]), "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": w.layout.block_size, "layers": layers},
+        "query_tokens_per_s_per_layer": round(Tq / (ms_call * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "paged_attn_prefill_chunk call", "flops_per_launch": flops,
+                     "avg_launch_ms": round(ms_call, 5)},
+        "cpu_baseline": cpu, "parity_max_abs_err_sampled_rows": max(errs), "wall_s": round(wall, 3),
+    }
+
+
+def bench_shared_prefix(args, torch, pa, W, w, layers):
+    """Parallel sampling over shared prompt blocks: new-token write + decode; CoW block copies timed apart."""
+    dev = "cuda"
+    B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    lens = w.layout.seq_lens
+    max_len = int(lens.max())
+    shape = w.cache_shape()
+    K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+    V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+    q = W.device_values((B, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
+    newk = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
+    newv = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
+    slots = torch.from_numpy(np.asarray(w.extra["new_slots"], np.int64)).to(dev)
+    bt = torch.from_numpy(w.layout.block_tables).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty(B, Hq, D, device=dev, dtype=torch.float32)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, w.block_size, max_len, 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    copies = w.copies
+    pairs = torch.from_numpy(np.asarray(copies, np.int64).reshape(-1, 2)).to(dev)
+
+    def step(ev):
+        for l in range(layers):
+            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+            s_ = ev.start() if ev else None
+            pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, w.scale, max_len, 0, ws)
+            if ev:
+                ev.stop(s_)
+
+    ms_step, ms_call, wall = time_steps(torch, step, args.steps, args.warmup)
+    logical = w.algorithmic_bytes(out_bytes=4)
+    unique = w.extra["unique_blocks"] * w.block_size * Hkv * D * w.elem_bytes * 2
+    copy = None
+    if len(copies):
+        for _ in range(3):
+            pa.block_copy(K[0], V[0], pairs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(layers):
+            pa.block_copy(K[l], V[l], pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / layers
+        cbytes = len(copies) * 2 * 2 * Hkv * w.block_size * D * w.elem_bytes  # K and V, read + write
+        copy = {"pairs": len(copies), "us_per_call": round(us, 3), "GBs": round(cbytes / us / 1e3, 1)}
+    pa.paged_attn_decode(out, q, K[0], V[0], bt, sl, w.scale, max_len, 0, ws)
+    torch.cuda.synchronize()
+    import oracle
+    oracle.build(force=False)
+    sel = np.arange(0, B, max(1, B // 16))
+    ref = oracle.paged_decode(host_copy(torch, q)[sel], host_copy(torch, K[0]), host_copy(torch, V[0]),
+                              w.layout.block_tables[sel], lens[sel], w.scale)
+    err = float(np.max(np.abs(out.double().cpu().numpy()[sel] - ref)))
+    gbs = logical / (ms_call * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(layers * (logical + B * Hkv * D * w.elem_bytes * 4 + 8 * B)
+                                         / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "prompts": w.extra["prompts"], "samples": w.extra["samples"],
+                   "prompt_len": w.extra["prompt_len"], "layers": layers, "total_tokens": int(lens.sum()),
+                   "unique_blocks": w.extra["unique_blocks"], "cow_pairs": len(copies)},
+        "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode call (logical KV bytes)", "bytes_per_launch": logical,
+                     "unique_kv_bytes": unique, "avg_launch_ms": round(ms_call, 5)},
+        "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "wall_s": round(wall, 3),
+    }
+
+
 def bench_copy(args, torch):
     """A plain device copy of known size: the reference for scaling the HBM byte counters."""
     n = 1 << 30
@@ -237,6 +401,12 @@ def main():
         layers = args.layers or 4
         part = 512 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part)
+    elif args.workload == "chunked_prefill":
+        w = W.chunked_prefill()
+        res = bench_prefill(args, torch, pa, W, w, args.layers or 32)
+    elif args.workload in ("shared_prefix", "shared_prefix_cow"):
+        w = W.shared_prefix(prompt_len=512 if args.workload == "shared_prefix" else 500)
+        res = bench_shared_prefix(args, torch, pa, W, w, args.layers or 32)
     elif args.workload == "copy_calibration":
         res = bench_copy(args, torch)
     else:

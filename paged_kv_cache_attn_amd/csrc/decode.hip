@@ -257,9 +257,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 
 // ----------------------------------------------------------------------------
 // Partition merge: one workgroup per (query head, sequence), one thread per
-// output dim; partitions combined in ascending order.
+// output dim; partitions combined in ascending order.  The (max, sum) pairs
+// are staged in LDS once and the partial outputs fetched in batches of eight
+// independent loads, so the merge costs a few memory latencies, not one per
+// partition.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
+  constexpr int kChunk = 256;
+  __shared__ float s_m[kChunk];
+  __shared__ float s_w[kChunk];
+  __shared__ float s_red[128];
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
   const int nblk = (L + p.block_size - 1) / p.block_size;
@@ -267,17 +274,52 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
   if (nparts <= 1) return;
   const int64_t row = (int64_t)b * p.num_heads + h;
   const float *ml = p.ws_ml + row * p.nparts_max * 2;
+  const float *wo = p.ws_o + row * p.nparts_max * p.head_dim;
+  const int tid = threadIdx.x;
+  // global max over partitions
   float M = kNegInf;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
-  const float M_use = M == kNegInf ? 0.f : M;
-  for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
-    float lsum = 0.f, o = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const float wgt = fast_exp2(ml[2 * q] - M_use);
-      lsum += ml[2 * q + 1] * wgt;
-      o += p.ws_o[(row * p.nparts_max + q) * p.head_dim + d] * wgt;
+  for (int q = tid; q < nparts; q += blockDim.x) M = fmaxf(M, ml[2 * q]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int off = 64; off > 0; off >>= 1) {
+    if (tid < off) s_red[tid] = fmaxf(s_red[tid], s_red[tid + off]);
+    __syncthreads();
+  }
+  const float M_use = s_red[0] == kNegInf ? 0.f : s_red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  float acc[2] = {0.f, 0.f};  // head_dim <= 2 * 128 threads... dims tid and tid + 128
+  for (int q0 = 0; q0 < nparts; q0 += kChunk) {
+    const int n = min(kChunk, nparts - q0);
+    for (int q = tid; q < n; q += blockDim.x) {
+      const float wgt = fast_exp2(ml[2 * (q0 + q)] - M_use);
+      s_w[q] = wgt;
+      s_m[q] = ml[2 * (q0 + q) + 1] * wgt;
     }
-    store_out(p.out, p.out_bf16, row * p.head_dim + d, lsum > 0.f ? o / lsum : 0.f);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int d = tid + u * 128;
+      if (d < p.head_dim) {
+        float o = 0.f;
+        for (int k0 = 0; k0 < n; k0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = wo[(int64_t)(q0 + min(k0 + k, n - 1)) * p.head_dim + d];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k0 + k < n) o += v[k] * s_w[k0 + k];
+        }
+        acc[u] += o;
+      }
+    }
+    for (int q = 0; q < n; ++q) lsum += s_m[q];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int d = tid + u * 128;
+    if (d < p.head_dim) store_out(p.out, p.out_bf16, row * p.head_dim + d, lsum > 0.f ? acc[u] / lsum : 0.f);
   }
 }
 

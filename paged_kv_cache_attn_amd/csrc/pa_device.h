@@ -53,17 +53,47 @@ __device__ __forceinline__ floatx4 mfma_16x16x16_bf16(const u32x2 &a, const u32x
 // Lane-crossing helpers (wave64).  xor 16 / xor 32 exchange between rows.
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// The four lanes of a column (c, c+16, c+32, c+48) combine through the
+// gfx950 row swaps: v_permlane16_swap exchanges rows 1 and 3 of its first
+// operand with rows 0 and 2 of its second, v_permlane32_swap the upper half
+// of the first with the lower half of the second.  Fed v twice, the returned
+// pair is, in every lane, {v[l & ~16], v[l | 16]} (resp. bit 32), so both
+// lanes of a partner pair combine the same two values in the same order and
+// agree bit for bit.  (The pair's elements are copied out as integers before
+// the bit cast: a bit cast applied directly to an element of the returned
+// vector reads element 0 whatever the index.)
+__device__ __forceinline__ float xor16_first(float v, float &second) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t s0 = s[0], s1 = s[1];
+  second = __builtin_bit_cast(float, s1);
+  return __builtin_bit_cast(float, s0);
+}
+__device__ __forceinline__ float xor32_first(float v, float &second) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t s0 = s[0], s1 = s[1];
+  second = __builtin_bit_cast(float, s1);
+  return __builtin_bit_cast(float, s0);
+}
+
 __device__ __forceinline__ float row_max4(float v) {
   // max over the four rows (lanes c, c+16, c+32, c+48)
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  v = fmaxf(v, shfl_xor_f(v, 32));
-  return v;
+  float b;
+  const float a = xor16_first(v, b);
+  v = fmaxf(a, b);
+  float d;
+  const float c = xor32_first(v, d);
+  return fmaxf(c, d);
 }
 
 __device__ __forceinline__ float row_sum4(float v) {
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
+  float b;
+  const float a = xor16_first(v, b);
+  v = a + b;
+  float d;
+  const float c = xor32_first(v, d);
+  return c + d;
 }
 
 // 16-byte global load/store through a plain vector type (global_load_dwordx4).

@@ -8,12 +8,21 @@
 // sits at position pos = seq_lens[b] - n_b + i and attends to tokens
 // 0 .. pos through the block table.
 //
-// MFMA kernel: one wave serves 16 columns = (16 / g) consecutive chunk
-// tokens x the g query heads of one KV head, so every K/V tile it reads is
-// shared by the whole GQA group; key blocks are visited in ascending order
-// with a per-column causal bound (the same tile step as decode).
+// MFMA kernel: a wave serves 16 columns = (16 / g) consecutive chunk tokens x
+// the g query heads of one KV head, so every K/V tile it reads is shared by
+// the whole GQA group; eight waves of a workgroup cover consecutive tokens and
+// walk the same key blocks, in ascending order with per-column causal bounds.
+#include <type_traits>
+
 #include "attn_core.h"
 #include "pa_launch.h"
+
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 2
+#endif
 
 namespace pa {
 
@@ -29,78 +38,206 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
   }
 }
 
+// Work items in a 1-D grid: consecutive workgroup ids are dealt round-robin
+// to the eight XCDs, each with its own L2.  Item L is renumbered so that every
+// XCD receives one contiguous run of the (sequence, KV head, query tile)
+// list; the query tiles of one head, which read the same K/V blocks, then
+// share an L2 and run close together in time.
+__device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
+  constexpr unsigned kXcds = 8;
+  const unsigned q = N / kXcds, rem = N % kXcds, xcd = L % kXcds, pos = L / kXcds;
+  return xcd < rem ? xcd * (q + 1) + pos : rem * (q + 1) + (xcd - rem) * q + pos;
+}
+
 // bf16 KV, head_dim 128, block_size 16, g in {1, 2, 4, 8, 16}.
-// grid = (ceil(max_query_len / (16 / g)), Hkv, B), one wave per workgroup.
-__global__ __launch_bounds__(64) void prefill_mfma_d128_kernel(PrefillParams p) {
+//
+// A workgroup of NW waves serves NW * CG * 16 / g consecutive chunk tokens of
+// one KV head.  Wave w owns CG groups of 16 columns (16 / g tokens x the g
+// query heads each).  Keys are taken two blocks (32 keys) at a time: the
+// workgroup loads each pair of K/V tiles from global memory ONCE into LDS,
+// three pairs ahead through registers, and every wave reads its MFMA operands
+// from there, so global/L2 traffic falls by the workgroup's column count.
+//
+// LDS holds three pair stages of four 4 KB tiles (K_a, V_a, K_b, V_b).  A
+// tile's 16-byte chunk k of token t sits at chunk t*16 + (k ^ t), which makes
+// both operand reads conflict-free: the K operand (token c, chunk 4i + r)
+// and the V operand (token 4r + v, chunk c) each touch 16 distinct bank
+// groups per 16 lanes.
+//
+// Block-table entries are read through the scalar cache (the table is not
+// written during the call), so the K/V loads are the only vector-memory
+// operations of the loop and a wait for one pair never waits on table reads.
+//
+// Within a head the query tiles go heaviest (last in the chunk) first; a
+// column group skips the pairs past its causal bound, but every wave joins
+// every barrier.  grid = ntiles * Hkv * B workgroups, ntiles =
+// ceil(max_query_len / (NW * CG * 16 / g)).
+template <int NW, int CG>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_d128_kernel(
+    PrefillParams p, int ntiles) {
   constexpr int D = 128;
   constexpr int BS = 16;
-  const int tile = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  constexpr int kTile = 4096;            // bytes of one K or V tile
+  constexpr int kStage = 4 * kTile;      // K_a, V_a, K_b, V_b
+  constexpr int kChunksPerThread = 4 * 256 / (64 * NW);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+
+  const unsigned item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int tile = ntiles - 1 - (int)(item % (unsigned)ntiles);
+  const int kh = (int)((item / (unsigned)ntiles) % (unsigned)p.num_kv_heads);
+  const int b = (int)(item / (unsigned)ntiles / (unsigned)p.num_kv_heads);
   const int g = p.num_heads / p.num_kv_heads;
-  const int tpw = 16 / g;  // chunk tokens per wave
+  const int tpgrp = 16 / g;              // chunk tokens per column group
+  const int tpw = CG * tpgrp;            // per wave
+  const int tpg = NW * tpw;              // per workgroup
   const int q0 = p.query_start_loc[b];
   const int n_b = p.query_start_loc[b + 1] - q0;
-  if (tile * tpw >= n_b) return;
+  if (tile * tpg >= n_b || q0 < 0) return;  // the whole workgroup leaves together
   const int S = clamp_len(p.seq_lens[b], p.max_len_cap);
-
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4, c = lane & 15;
-  const int ti = c / g, hh = c - (c / g) * g;
-  const int qi = tile * tpw + ti;  // row inside the chunk
-  const bool col_ok = ti < tpw && qi < n_b && q0 >= 0 && (int64_t)q0 + qi < p.num_query_tokens;
-  const int lim = col_ok ? S - n_b + qi + 1 : 0;  // keys < lim are visible
-  const int last_qi = min(tile * tpw + tpw, n_b) - 1;
-  int kend = S - n_b + last_qi + 1;  // wave-wide key bound
-  kend = kend < 0 ? 0 : kend;
-  const int nblk = (kend + BS - 1) / BS;
 
-  bf16x8 qb[4];
-  load_q_operand_d128(qb,
-                      col_ok ? reinterpret_cast<const uint16_t *>(p.q) +
-                                   ((int64_t)(q0 + qi) * p.num_heads + (int64_t)kh * g + hh) * D
-                             : nullptr,
-                      r);
+  // key bound of the whole workgroup (its last valid chunk row)
+  const int last_qi_wg = min(tile * tpg + tpg, n_b) - 1;
+  const int kend_wg = max(0, S - n_b + last_qi_wg + 1);
+  const int nblk = (kend_wg + BS - 1) / BS;
+  const int npair = (nblk + 1) / 2;
+
+  // columns of each group of this wave
+  const int ti = c / g, hh = c - (c / g) * g;
+  int lim[CG], lim_min[CG], kend[CG];
+  bool col_ok[CG];
+  bf16x8 qb[CG][4];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    const int first = tile * tpg + w * tpw + cg * tpgrp;  // first chunk row of the group
+    const int qi = first + ti;
+    col_ok[cg] = qi < n_b && (int64_t)q0 + qi < p.num_query_tokens;
+    lim[cg] = col_ok[cg] ? S - n_b + qi + 1 : 0;
+    lim_min[cg] = S - n_b + first + 1;
+    const int last = min(first + tpgrp, n_b) - 1;
+    kend[cg] = last >= first ? max(0, S - n_b + last + 1) : 0;
+    // idle columns read a valid row (never stored) so every value stays finite
+    // (clamped to the query rows, whatever query_start_loc holds)
+    const int64_t row_ld = min((int64_t)q0 + (col_ok[cg] ? qi : last_qi_wg), (int64_t)p.num_query_tokens - 1);
+    load_q_operand_d128(qb[cg],
+                        reinterpret_cast<const uint16_t *>(p.q) + (row_ld * p.num_heads + (int64_t)kh * g + hh) * D,
+                        r);
+  }
 
   const float sl2 = p.scale * kLog2e;
-  const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(p.k_cache) + (int64_t)kh * BS * D;
-  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(p.v_cache) + (int64_t)kh * BS * D;
-  const int64_t blk_stride = (int64_t)p.num_kv_heads * BS * D;
+  const __attribute__((address_space(4))) int32_t *table =
+      (const __attribute__((address_space(4))) int32_t *)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+  const uint8_t *kbytes = reinterpret_cast<const uint8_t *>(p.k_cache) + (int64_t)kh * BS * D * 2;
+  const uint8_t *vbytes = reinterpret_cast<const uint8_t *>(p.v_cache) + (int64_t)kh * BS * D * 2;
+  const int64_t blk_bytes = (int64_t)p.num_kv_heads * BS * D * 2;
 
-  MfmaAttnState st;
-  st.init();
-  auto load = [&](int j, KVTile &t, bool &ok) {
-    int phys = table[j];
-    ok = (unsigned)phys < (unsigned)p.num_blocks;
-    phys = ok ? phys : 0;
-    load_kv_tile_d128(t, kbase + phys * blk_stride, vbase + phys * blk_stride, r, c);
+  // Cooperative pair load: the 1024 16-byte chunks of a pair, consecutive
+  // threads on consecutive chunks of a tile.  Returns which of the two blocks
+  // hold real data (bit 0: A, bit 1: B); block j >= nblk (the odd tail) and
+  // an out-of-range table entry are read from block 0 and masked later.
+  auto gload = [&](int pr, u32x4 *regs) -> int {
+    pr = min(pr, max(npair - 1, 0));
+    const int ja = 2 * pr, jb = 2 * pr + 1;
+    const int ta = table[ja];
+    const int tb = jb < nblk ? table[jb] : -1;
+    const bool oka = (unsigned)ta < (unsigned)p.num_blocks, okb = (unsigned)tb < (unsigned)p.num_blocks;
+    const int64_t ba = (oka ? ta : 0) * blk_bytes, bb = (okb ? tb : 0) * blk_bytes;
+#pragma unroll
+    for (int k = 0; k < kChunksPerThread; ++k) {
+      const int u = tid + k * 64 * NW;
+      const int kind = u >> 8, q = u & 255;  // kind: 0 K_a, 1 V_a, 2 K_b, 3 V_b
+      const uint8_t *src = ((kind & 1) ? vbytes : kbytes) + (kind < 2 ? ba : bb) + q * 16;
+      regs[k] = ld16(src);
+    }
+    return (int)oka | ((int)okb << 1);
   };
-  if (nblk > 0) {
-    KVTile cur;
-    bool ok;
-    load(0, cur, ok);
-    for (int j = 0;; ++j) {
-      if (j + 1 < nblk) {
-        KVTile nxt;
-        bool okn;
-        load(j + 1, nxt, okn);
-        st.step(qb, cur, j * BS, ok ? lim : 0, sl2, r);
-        cur = nxt;
-        ok = okn;
-      } else {
-        st.step(qb, cur, j * BS, ok ? lim : 0, sl2, r);
-        break;
+  auto lstore = [&](int stage, const u32x4 *regs) {
+#pragma unroll
+    for (int k = 0; k < kChunksPerThread; ++k) {
+      const int u = tid + k * 64 * NW;
+      const int kind = u >> 8, q = u & 255;
+      const int t = q >> 4, kc = q & 15;
+      *reinterpret_cast<u32x4 *>(lds + stage * kStage + kind * kTile + ((t * 16 + (kc ^ t)) << 4)) = regs[k];
+    }
+  };
+  // The operands of one pair for this wave, from LDS stage `stage`.
+  auto lread = [&](int stage, KVTile &ta, KVTile &tb) {
+    const uint8_t *base = lds + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ck = (c * 16 + ((4 * i + r) ^ c)) << 4;
+      ta.k[i] = *reinterpret_cast<const u32x4 *>(base + 0 * kTile + ck);
+      tb.k[i] = *reinterpret_cast<const u32x4 *>(base + 2 * kTile + ck);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * r + v;
+      const int cv = (t * 16 + (c ^ t)) << 4;
+      ta.v[v] = *reinterpret_cast<const u32x4 *>(base + 1 * kTile + cv);
+      tb.v[v] = *reinterpret_cast<const u32x4 *>(base + 3 * kTile + cv);
+    }
+  };
+  auto compute = [&](int stage, int pr, int okbits, MfmaAttnPairState *st) {
+    KVTile ta, tb;
+    lread(stage, ta, tb);
+    const int tok0 = 32 * pr;
+    const bool oka = okbits & 1, okb = okbits & 2;
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      if (tok0 < kend[cg]) {
+        const bool full = tok0 + 32 <= lim_min[cg] && oka && okb;
+        st[cg].step(qb[cg], ta, tb, tok0, oka ? lim[cg] : 0, okb ? lim[cg] : 0, !full, sl2, r);
       }
     }
+  };
+
+  MfmaAttnPairState st[CG];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) st[cg].init();
+
+  if (npair > 0) {
+    // Pair X sits in register set X % 3 and LDS stage X % 3.  Its loads are
+    // issued while pair X - 3 is computed and reach LDS while pair X - 1 is,
+    // so each load has two pairs of work to arrive.
+    u32x4 rs[3][kChunksPerThread];
+    int ok_r[3], ok_s[3];
+    ok_r[0] = gload(0, rs[0]);
+    lstore(0, rs[0]);
+    ok_s[0] = ok_r[0];
+    ok_r[1] = gload(1, rs[1]);
+    ok_r[2] = gload(2, rs[2]);
+    auto iter = [&](int X, auto phase) -> bool {
+      constexpr int j = decltype(phase)::value, j1 = (j + 1) % 3;
+      __syncthreads();
+      if (X + 1 < npair) lstore(j1, rs[j1]);
+      ok_s[j1] = ok_r[j1];
+      ok_r[j] = gload(X + 3, rs[j]);
+      compute(j, X, ok_s[j], st);
+      return X + 1 < npair;
+    };
+    for (int X = 0;; X += 3) {
+      if (!iter(X, std::integral_constant<int, 0>())) break;
+      if (!iter(X + 1, std::integral_constant<int, 1>())) break;
+      if (!iter(X + 2, std::integral_constant<int, 2>())) break;
+    }
   }
-  const float l = row_sum4(st.l);
-  if (!col_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int64_t row = (int64_t)(q0 + qi) * p.num_heads + (int64_t)kh * g + hh;
+
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int cg = 0; cg < CG; ++cg) {
+    const float l = row_sum4(st[cg].l);
+    if (!col_ok[cg]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int qi = tile * tpg + w * tpw + cg * tpgrp + ti;
+    const int64_t row = ((int64_t)q0 + qi) * p.num_heads + (int64_t)kh * g + hh;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      store_out(p.out, p.out_bf16, row * D + 32 * r + 8 * i + jj, st.acc[jj][i] * inv);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        store_out(p.out, p.out_bf16, row * D + 32 * r + 8 * i + jj, st[cg].acc[jj][i] * inv);
+  }
 }
 
 // Generic VALU kernel: any dtype / head_dim 64 or 128 / group size / block
@@ -163,9 +300,13 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
   const bool mfma = p.kv_bf16 && p.head_dim == 128 && p.block_size == 16 && g <= 16 && (16 % g) == 0;
   if (mfma) {
-    const int tpw = 16 / g;
-    dim3 grid((p.max_query_len + tpw - 1) / tpw, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL(prefill_mfma_d128_kernel, grid, dim3(64), 0, stream, p);
+    constexpr int NW = PA_PREFILL_WAVES, CG = PA_PREFILL_GROUPS;
+    const int tpg = NW * CG * (16 / g);
+    const int64_t ntiles = (p.max_query_len + tpg - 1) / tpg;
+    const int64_t items = ntiles * p.num_kv_heads * p.num_seqs;
+    if (items * 64 * NW > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG>), dim3((unsigned)items), dim3(64 * NW), 0, stream, p,
+                       (int)ntiles);
   } else {
     dim3 grid(p.max_query_len, p.num_heads, p.num_seqs);
     if (p.head_dim == 64) {
