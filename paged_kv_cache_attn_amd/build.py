@@ -27,6 +27,9 @@ CFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed-fp32 VALU forms are left to no one: plain fp32 math only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN operands are ever formed on purpose (masked scores are -inf and
+    # every -inf - -inf is guarded), so max/min need no NaN-quieting copies
+    "-fno-honor-nans",
     "-Wall", "-I" + INCLUDE, "-I" + CSRC,
 ]
 

@@ -108,11 +108,16 @@ struct MfmaAttnState {
 // the full-rate v_mfma_f32_16x16x32_bf16 (K = 32 keys).  For a lane the 8
 // contraction indices k = 8r .. 8r+7 stand for keys 4r..4r+3 of block A and
 // 4r..4r+3 of block B; the P^T operand (from the two QK outputs) and the
-// V^T operand (regrouped from the two V tiles) use the same order.  The
-// output is rescaled only when a column's running max grows by more than
+// V^T operand use the same order.  The V^T operand of output dims
+// 16t .. 16t+15 arrives ready-made (vt[t], from LDS transpose reads): lane
+// (r, c) holds V_A[4r..4r+3][16t + c] then V_B[4r..4r+3][16t + c].  So
+//   acc[t][i] = O[column c][dim 16t + 4r + i].
+// The output is rescaled only when a column's running max grows by more than
 // 2^kLazyRescale, so most pairs skip the 32-register rescale; weights can
 // then exceed 1 (by at most that factor), which fp32 sums and the bf16
-// hi + lo split carry without loss.
+// hi + lo split carry without loss.  Scores stay unscaled until the exponent:
+// m is kept in log2 units and each weight is exp2(s * sl2 - m) with one fma
+// (scaling by sl2 > 0 commutes with the max).
 constexpr float kLazyRescale = 8.f;
 
 struct MfmaAttnPairState {
@@ -124,37 +129,39 @@ struct MfmaAttnPairState {
     m = kNegInf;
     l = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Blocks A (keys tok0 .. tok0+15) and B (keys tok0+16 ..); when `mask` is
-  // set (wave-uniform; false when every key of both blocks is visible to
+  // Blocks A (keys tok0 .. tok0+15) and B (keys tok0+16 ..): ka / kb are the
+  // K operands (token c, dims 32i + 8r ..), vt the V^T operands.  When `mask`
+  // is set (wave-uniform; false when every key of both blocks is visible to
   // every column of the wave), keys of A at or past lim_a and keys of B at or
   // past lim_b are masked for this lane's column.
-  __device__ __forceinline__ void step(const bf16x8 qb[4], const KVTile &ta, const KVTile &tb, int tok0,
-                                       int lim_a, int lim_b, bool mask, float sl2, int r) {
+  __device__ __forceinline__ void step(const bf16x8 qb[4], const u32x4 ka[4], const u32x4 kb[4],
+                                       const bf16x8 vt[8], int tok0, int lim_a, int lim_b, bool mask,
+                                       float sl2, int r) {
     floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta.k[i]), qb[i], sa);
-      sb = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, tb.k[i]), qb[i], sb);
+      sa = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[i]), qb[i], sa);
+      sb = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[i]), qb[i], sb);
     }
     float x[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      x[v] = sa[v] * sl2;
-      x[4 + v] = sb[v] * sl2;
+      x[v] = sa[v];
+      x[4 + v] = sb[v];
     }
     if (mask) {
-      const int ka = tok0 + 4 * r, kb = tok0 + 16 + 4 * r;
+      const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        x[v] = ka + v < lim_a ? x[v] : kNegInf;
-        x[4 + v] = kb + v < lim_b ? x[4 + v] : kNegInf;
+        x[v] = ta + v < lim_a ? x[v] : kNegInf;
+        x[4 + v] = tb + v < lim_b ? x[4 + v] : kNegInf;
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = row_max4(mx);
+    mx = row_max4(mx) * sl2;
     // rescale only when some column's max grew by more than the slack
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
       const float m_new = fmaxf(m, mx);
@@ -162,13 +169,13 @@ struct MfmaAttnPairState {
       const float corr = fast_exp2(m - m_use);
       l *= corr;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
+      for (int t = 0; t < 8; ++t) acc[t] *= corr;
       m = m_new;
     }
-    const float m_use = m == kNegInf ? 0.f : m;
+    const float neg_m = m == kNegInf ? 0.f : -m;
     float e[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) e[v] = fast_exp2(x[v] - m_use);
+    for (int v = 0; v < 8; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, neg_m));
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -180,15 +187,9 @@ struct MfmaAttnPairState {
     const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
     const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) {
-      const u32x4 a_lo = {pack_lo_halves(ta.v[0][w2], ta.v[1][w2]), pack_lo_halves(ta.v[2][w2], ta.v[3][w2]),
-                          pack_lo_halves(tb.v[0][w2], tb.v[1][w2]), pack_lo_halves(tb.v[2][w2], tb.v[3][w2])};
-      const u32x4 a_hi = {pack_hi_halves(ta.v[0][w2], ta.v[1][w2]), pack_hi_halves(ta.v[2][w2], ta.v[3][w2]),
-                          pack_hi_halves(tb.v[0][w2], tb.v[1][w2]), pack_hi_halves(tb.v[2][w2], tb.v[3][w2])};
-      acc[2 * w2] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a_lo), pb_hi, acc[2 * w2]);
-      acc[2 * w2] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a_lo), pb_lo, acc[2 * w2]);
-      acc[2 * w2 + 1] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a_hi), pb_hi, acc[2 * w2 + 1]);
-      acc[2 * w2 + 1] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a_hi), pb_lo, acc[2 * w2 + 1]);
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = mfma_16x16x32_bf16(vt[t], pb_hi, acc[t]);
+      acc[t] = mfma_16x16x32_bf16(vt[t], pb_lo, acc[t]);
     }
   }
 };

@@ -20,6 +20,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -45,7 +46,6 @@ __device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const bf16x8 &a, const bf1
 
 __device__ __forceinline__ floatx4 mfma_16x16x16_bf16(const u32x2 &a, const u32x2 &b,
                                                       const floatx4 &c) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }

@@ -58,11 +58,16 @@ __device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
 // three pairs ahead through registers, and every wave reads its MFMA operands
 // from there, so global/L2 traffic falls by the workgroup's column count.
 //
-// LDS holds three pair stages of four 4 KB tiles (K_a, V_a, K_b, V_b).  A
-// tile's 16-byte chunk k of token t sits at chunk t*16 + (k ^ t), which makes
-// both operand reads conflict-free: the K operand (token c, chunk 4i + r)
-// and the V operand (token 4r + v, chunk c) each touch 16 distinct bank
-// groups per 16 lanes.
+// LDS holds three pair stages of four 4 KB tiles (K_a, V_a, K_b, V_b).  In a
+// K tile the 16-byte chunk k of token t sits at chunk t*16 + (k ^ t), so the
+// K operand reads (token c, chunk 4i + r) touch 16 distinct bank groups per
+// 16 lanes.  A V tile is read with ds_read_b64_tr_b16, which hands lane
+// 16r + c element (c mod 4) of the 8-byte word addressed by lane
+// 16r + 4j + (c / 4) as its element j: when lane (r, j, q) addresses
+// V[4r + j][16t + 4q .. +3], lane (r, c) receives V[4r .. 4r+3][16t + c], the
+// V^T operand.  Those reads take 32 contiguous bytes from each of 16 tokens,
+// so a V tile swizzles 32-byte segments: segment s of token t sits at
+// segment t*8 + (s ^ (t & 7)).
 //
 // Block-table entries are read through the scalar cache (the table is not
 // written during the call), so the K/V loads are the only vector-memory
@@ -160,36 +165,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int u = tid + k * 64 * NW;
       const int kind = u >> 8, q = u & 255;
       const int t = q >> 4, kc = q & 15;
-      *reinterpret_cast<u32x4 *>(lds + stage * kStage + kind * kTile + ((t * 16 + (kc ^ t)) << 4)) = regs[k];
+      const int off = (kind & 1) ? t * 256 + ((((kc >> 1) ^ (t & 7)) << 5) | ((kc & 1) << 4))
+                                 : (t * 16 + (kc ^ t)) << 4;
+      *reinterpret_cast<u32x4 *>(lds + stage * kStage + kind * kTile + off) = regs[k];
     }
   };
+  // V^T operand address of this lane inside a V tile for dim tile dt: lane
+  // (r, j, q) = (r, c >> 2, c & 3) points at V[4r + j][16 dt + 4q].
+  const int vtok = 4 * r + (c >> 2);
+  const int vq8 = (c & 3) * 8;
+  auto vt_addr = [&](int dt) -> int { return vtok * 256 + (((dt ^ (vtok & 7)) << 5) | vq8); };
   // The operands of one pair for this wave, from LDS stage `stage`.
-  auto lread = [&](int stage, KVTile &ta, KVTile &tb) {
+  auto lread = [&](int stage, u32x4 *ka, u32x4 *kb, bf16x8 *vt) {
     const uint8_t *base = lds + stage * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ck = (c * 16 + ((4 * i + r) ^ c)) << 4;
-      ta.k[i] = *reinterpret_cast<const u32x4 *>(base + 0 * kTile + ck);
-      tb.k[i] = *reinterpret_cast<const u32x4 *>(base + 2 * kTile + ck);
+      ka[i] = *reinterpret_cast<const u32x4 *>(base + 0 * kTile + ck);
+      kb[i] = *reinterpret_cast<const u32x4 *>(base + 2 * kTile + ck);
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 4 * r + v;
-      const int cv = (t * 16 + (c ^ t)) << 4;
-      ta.v[v] = *reinterpret_cast<const u32x4 *>(base + 1 * kTile + cv);
-      tb.v[v] = *reinterpret_cast<const u32x4 *>(base + 3 * kTile + cv);
+    for (int dt = 0; dt < 8; ++dt) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const int off = vt_addr(dt);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 1 * kTile + off));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 3 * kTile + off));
+      const u32x2 a2 = __builtin_bit_cast(u32x2, va), b2 = __builtin_bit_cast(u32x2, vb);
+      vt[dt] = __builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], b2[0], b2[1]});
     }
   };
   auto compute = [&](int stage, int pr, int okbits, MfmaAttnPairState *st) {
-    KVTile ta, tb;
-    lread(stage, ta, tb);
+    u32x4 ka[4], kb[4];
+    bf16x8 vt[8];
+    lread(stage, ka, kb, vt);
     const int tok0 = 32 * pr;
     const bool oka = okbits & 1, okb = okbits & 2;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       if (tok0 < kend[cg]) {
         const bool full = tok0 + 32 <= lim_min[cg] && oka && okb;
-        st[cg].step(qb[cg], ta, tb, tok0, oka ? lim[cg] : 0, okb ? lim[cg] : 0, !full, sl2, r);
+        st[cg].step(qb[cg], ka, kb, vt, tok0, oka ? lim[cg] : 0, okb ? lim[cg] : 0, !full, sl2, r);
       }
     }
   };
@@ -225,18 +240,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
 
+  // acc[t][i] = O[column c][dim 16t + 4r + i]
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     const float l = row_sum4(st[cg].l);
-    if (!col_ok[cg]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int qi = tile * tpg + w * tpw + cg * tpgrp + ti;
     const int64_t row = ((int64_t)q0 + qi) * p.num_heads + (int64_t)kh * g + hh;
+    if (!col_ok[cg]) continue;
+    if (p.out_bf16) {
+      uint16_t *o = reinterpret_cast<uint16_t *>(p.out) + row * D + 4 * r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int t = 0; t < 8; ++t) {
+        const floatx4 v = st[cg].acc[t] * inv;
+        *reinterpret_cast<u32x2 *>(o + 16 * t) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    } else {
+      float *o = reinterpret_cast<float *>(p.out) + row * D + 4 * r;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        store_out(p.out, p.out_bf16, row * D + 32 * r + 8 * i + jj, st[cg].acc[jj][i] * inv);
+      for (int t = 0; t < 8; ++t) *reinterpret_cast<floatx4 *>(o + 16 * t) = st[cg].acc[t] * inv;
+    }
   }
 }
 
