@@ -81,7 +81,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int R = p.sk_range_blocks;
 
   // -- flat index space: exclusive prefix over sequences of blocks * Hkv ----
-  {
+  if (B <= 64) {
+    // one wave scans with cross-lane adds; a single barrier publishes it
+    if (w == 0) {
+      int L = lane < B ? p.seq_lens[lane] : 0;
+      L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
+      const int v = ((L + kBS - 1) / kBS) * Hkv;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        incl += lane >= off ? t : 0;
+      }
+      if (lane < B) {
+        s_len[lane] = L;
+        s_pref[lane] = incl - v;
+      }
+      if (lane == (B > 0 ? B - 1 : 0)) s_pref[B] = B > 0 ? incl : 0;
+    }
+    if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
+    __syncthreads();
+  } else {
     const int nt = 64 * NW;
     const int per = (B + nt - 1) / nt;
     const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
@@ -323,13 +343,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // One workgroup per (sequence, KV head) row; rows that fit one range were
-// written by the main kernel and are skipped.  Pieces are combined in
-// ascending range order, in chunks of 64 pieces.
+// written by the main kernel and are skipped.  A thread owns output elements
+// (column, dim) and combines the row's pieces for them in ascending range
+// order; it issues the loads of up to kBatch pieces (their max, sum and
+// partial output) before it uses any, so a row costs one dependent memory
+// round trip per kBatch pieces, with no LDS and no barriers.
 __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(DecodeParams p) {
-  constexpr int kChunk = 64;
-  __shared__ float s_w[kChunk][16];  // weight of each (piece, column)
-  __shared__ float s_M[16];
-  __shared__ float s_lsum[16];
+  constexpr int kBatch = 8;
   const int row = blockIdx.x;
   const int Hkv = p.num_kv_heads;
   const int g = p.num_heads / Hkv;
@@ -352,49 +372,35 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(DecodeParams 
     const int sl = row_start <= range_begin(gg, T, G, R) ? 0 : 1;
     return ((int64_t)gg * 2 + sl) * g + cc;
   };
-
-  for (int cc = threadIdx.x; cc < g; cc += blockDim.x) {
-    float M = kNegInf;
-    for (int k = 0; k < nc; ++k) M = fmaxf(M, p.sk_ml[piece(k, cc) * 2]);
-    s_M[cc] = M == kNegInf ? 0.f : M;
-    s_lsum[cc] = 0.f;
-  }
-  __syncthreads();
-  float acc[8];
+  for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x) {
+    const int cc = idx / kD, d = idx - cc * kD;
+    float M = kNegInf, lsum = 0.f, o = 0.f;
+    for (int k0 = 0; k0 < nc; k0 += kBatch) {
+      float pm[kBatch], pl[kBatch], po[kBatch];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-  for (int k0 = 0; k0 < nc; k0 += kChunk) {
-    const int n = min(kChunk, nc - k0);
-    for (int idx = threadIdx.x; idx < n * g; idx += blockDim.x) {
-      const int k = idx / g, cc = idx - k * g;
-      s_w[k][cc] = fast_exp2(p.sk_ml[piece(k0 + k, cc) * 2] - s_M[cc]);
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < g) {
-      float ls = 0.f;
-      for (int k = 0; k < n; ++k) ls += p.sk_ml[piece(k0 + k, threadIdx.x) * 2 + 1] * s_w[k][threadIdx.x];
-      s_lsum[threadIdx.x] += ls;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = threadIdx.x + u * 256;
-      if (idx < g * kD) {
-        const int cc = idx / kD, d = idx - cc * kD;
-        float o = 0.f;
-        for (int k = 0; k < n; ++k) o += p.sk_part[piece(k0 + k, cc) * kD + d] * s_w[k][cc];
-        acc[u] += o;
+      for (int k = 0; k < kBatch; ++k) {
+        const int kk = min(k0 + k, nc - 1);
+        const int64_t pc = piece(kk, cc);
+        pm[k] = k0 + k < nc ? p.sk_ml[pc * 2] : kNegInf;
+        pl[k] = p.sk_ml[pc * 2 + 1];
+        po[k] = p.sk_part[pc * kD + d];
       }
-    }
-    __syncthreads();
-  }
+      float Mb = M;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int idx = threadIdx.x + u * 256;
-    if (idx < g * kD) {
-      const int cc = idx / kD, d = idx - cc * kD;
-      const float ls = s_lsum[cc];
-      store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? acc[u] / ls : 0.f);
+      for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, pm[k]);
+      const float Mu = Mb == kNegInf ? 0.f : Mb;
+      const float cf = fast_exp2(M - Mu);  // rescale what came before (0 at the start)
+      lsum *= cf;
+      o *= cf;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float wgt = fast_exp2(pm[k] - Mu);  // 0 for the padding entries
+        lsum += pl[k] * wgt;
+        o += po[k] * wgt;
+      }
+      M = Mb;
     }
+    store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o / lsum : 0.f);
   }
 }
 
