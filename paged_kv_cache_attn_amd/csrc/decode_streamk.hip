@@ -69,6 +69,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int s_prow[kStreamKTabCache + 1]; // row (b * Hkv + kh) of each position, -1 past the end
   __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
   __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
+  __shared__ int s_brid[NW][2];                // its row, b * Hkv + kh
   extern __shared__ float s_park[];            // [NW][2][g][kD + 2]: acc, then max and sum
 
   const int tid = threadIdx.x;
@@ -242,7 +243,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             pc[kD + 1] = lw;
           }
         }
-        if (lane == 0) s_brow[w][k] = s_pref[b] + kh * nb;
+        if (lane == 0) {
+          s_brow[w][k] = s_pref[b] + kh * nb;
+          s_brid[w][k] = row;
+        }
       }
       if (li + 1 == le) return false;
       seg_j0 = s_pj[li + 1];
@@ -269,60 +273,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __syncthreads();
 
   // -- combine the parked boundary rows, in wave order -----------------------
-  // Entries (w, k) in order form runs of equal row start; each run is one row.
-  for (int w0 = 0, k0 = 0; w0 < NW;) {
-    const int row_start = s_brow[w0][k0];
-    if (row_start < 0) {  // empty slot: advance
-      if (++k0 == 2) { k0 = 0; ++w0; }
-      continue;
-    }
-    // extent of the run
-    int w1 = w0, k1 = k0;  // last entry of the run (inclusive)
-    {
-      int wn = w0, kn = k0;
-      while (true) {
-        if (++kn == 2) { kn = 0; ++wn; }
-        if (wn >= NW) break;
-        const int rs = s_brow[wn][kn];
-        if (rs < 0) continue;
-        if (rs != row_start) break;
-        w1 = wn;
-        k1 = kn;
-      }
-    }
-    const int b = [&] {
-      int lo = 0, hi = B;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= row_start) lo = mid; else hi = mid;
-      }
-      return lo;
-    }();
+  // The 2 * NW entries (w, k), in order, form runs of equal row start, one
+  // run per row.  Every thread reads all entries at once and walks the runs
+  // in the same order; for each of its output elements it loads the members'
+  // max, sum and partial value together and combines them in entry order.
+  constexpr int NE = 2 * NW;
+  int ers[NE], erow[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    ers[i] = s_brow[i >> 1][i & 1];
+    erow[i] = s_brid[i >> 1][i & 1];
+  }
+  int prev_rs = -1;
+#pragma unroll
+  for (int h = 0; h < NE; ++h) {
+    const int rs = ers[h];
+    if (rs < 0 || rs == prev_rs) continue;  // empty, or inside the current run
+    prev_rs = rs;
+    const int row = erow[h];
+    const int b = row / Hkv, kh = row - b * Hkv;
     const int nb = (s_pref[b + 1] - s_pref[b]) / Hkv;
-    const int kh = (row_start - s_pref[b]) / nb;
-    const bool whole = row_start >= s && row_start + nb <= e;
-    const int slot = row_start <= s ? 0 : 1;
+    const bool whole = rs >= s && rs + nb <= e;
+    const int slot = rs <= s ? 0 : 1;
     const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
     for (int idx = tid; idx < g * kD; idx += 64 * NW) {
       const int cc = idx / kD, d = idx - cc * kD;
-      float M = kNegInf;
-      for (int ww = w0, kk = k0;;) {
-        if (s_brow[ww][kk] == row_start)
-          M = fmaxf(M, s_park[(((size_t)ww * 2 + kk) * g + cc) * (kD + 2) + kD]);
-        if (ww == w1 && kk == k1) break;
-        if (++kk == 2) { kk = 0; ++ww; }
+      float mv[NE], lv[NE], ov[NE];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const float *pc = s_park + ((size_t)i * g + cc) * (kD + 2);
+        const bool in = i >= h && ers[i] == rs;
+        mv[i] = in ? pc[kD] : kNegInf;
+        lv[i] = in ? pc[kD + 1] : 0.f;
+        ov[i] = in ? pc[d] : 0.f;
       }
+      float M = kNegInf;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) M = fmaxf(M, mv[i]);
       const float M_use = M == kNegInf ? 0.f : M;
       float lsum = 0.f, o = 0.f;
-      for (int ww = w0, kk = k0;;) {
-        if (s_brow[ww][kk] == row_start) {
-          const float *pc = s_park + (((size_t)ww * 2 + kk) * g + cc) * (kD + 2);
-          const float wgt = fast_exp2(pc[kD] - M_use);
-          lsum += pc[kD + 1] * wgt;
-          o += pc[d] * wgt;
-        }
-        if (ww == w1 && kk == k1) break;
-        if (++kk == 2) { kk = 0; ++ww; }
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        if (i < h) continue;
+        const float wgt = fast_exp2(mv[i] - M_use);  // 0 for entries outside the run
+        lsum += lv[i] * wgt;
+        o += ov[i] * wgt;
       }
       if (whole) {
         store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o / lsum : 0.f);
@@ -335,10 +330,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
       }
     }
-    // next run
-    w0 = w1;
-    k0 = k1;
-    if (++k0 == 2) { k0 = 0; ++w0; }
   }
 }
 
