@@ -32,6 +32,40 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode effective KV GB/s (% of HBM peak) and query tokens/s per layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's sources and build script: counter-derived
+    traffic figures are only reported for the exact code they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    files = []
+    for d in ("paged_kv_cache_attn_amd/csrc", "include"):
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            if name.endswith((".hip", ".h")):
+                files.append(os.path.join(d, name))
+    files.append("paged_kv_cache_attn_amd/build.py")
+    for rel in files:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per call from the FETCH_SIZE / WRITE_SIZE counter runs kept
+    under profiles/ (scaled by the copy-kernel calibration), or None when
+    they were taken on different sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e or t.get("source_sha256") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_call")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
@@ -177,13 +211,14 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": w.block_size, "layers": layers, "total_tokens": int(lens.sum()),
-                   "max_seq_len": max_len, "partition_size": partition or 256,
+                   "max_seq_len": max_len, "partition_size": partition or "auto",
                    "num_blocks_per_layer": w.layout.num_blocks},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_decode call", "bytes_per_launch": dec_bytes,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per call", "kernel": "paged_attn_decode call",
+                     "bytes_per_launch": dec_bytes,
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
@@ -276,7 +311,8 @@ def bench_prefill(args, torch, pa, W, w, layers):
                    "block_size": w.layout.block_size, "layers": layers},
         "query_tokens_per_s_per_layer": round(Tq / (ms_call * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes per call",
                      "kernel": "paged_attn_prefill_chunk call", "flops_per_launch": flops,
                      "avg_launch_ms": round(ms_call, 5)},
         "cpu_baseline": cpu, "parity_max_abs_err_sampled_rows": max(errs), "wall_s": round(wall, 3),
@@ -349,8 +385,8 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
                    "unique_blocks": w.extra["unique_blocks"], "cow_pairs": len(copies)},
         "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_decode call (logical KV bytes)", "bytes_per_launch": logical,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per call", "kernel": "paged_attn_decode call (logical KV bytes)", "bytes_per_launch": logical,
                      "unique_kv_bytes": unique, "avg_launch_ms": round(ms_call, 5)},
         "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "wall_s": round(wall, 3),
     }
@@ -399,7 +435,7 @@ def main():
     elif args.workload == "llama70b_long":
         w = W.llama70b_long()
         layers = args.layers or 4
-        part = 512 if args.partition < 0 else args.partition
+        part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part)
     elif args.workload == "chunked_prefill":
         w = W.chunked_prefill()
