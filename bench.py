@@ -11,7 +11,9 @@ Infinity Cache when it is read again.
 Printed (one JSON line): effective KV GB/s of the whole step (algorithmic bytes
 / time, inputs resident in HBM), query tokens/s per layer, the live roofline of
 the decode call measured with HIP events on the launch stream, and the CPU
-oracle timed on a bounded sample on this host's cores.
+oracle timed on a bounded sample on this host's cores.  A step is captured
+once in a HIP graph and replayed (the default; --no-graph launches every call
+from Python, which on this host is slower than the GPU work it launches).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -82,45 +84,80 @@ def parse():
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every call from Python instead of replaying captured HIP graphs")
     return ap.parse_args()
 
 
-class EventPairs:
-    """Start/stop HIP events recorded on the launch stream around one call."""
+def time_layers(args, torch, layers, write, call, out):
+    """Time one step (every layer: write(l) then call(l)) and the attention call alone.
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
+    Default: each is captured once in a HIP graph (a decode step is a fixed
+    sequence of launches, replayed every token) and the graphs are replayed
+    between two events on the launch stream; per-call time is the replay time
+    of a graph holding the `layers` attention calls alone, divided by
+    `layers`.  Before timing, a replay of the step graph must reproduce the
+    eager result of the last layer bit for bit.  With --no-graph every call is
+    launched from Python and bracketed by pre-created event pairs.
+    Returns (ms per step, ms per call, wall seconds of the timed steps, mode).
+    """
+    def step():
+        for l in range(layers):
+            write(l)
+            call(l)
 
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, s):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append((s, e))
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
-
-
-def time_steps(torch, step, steps, warmup):
-    for _ in range(warmup):
-        step(None)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    ev = EventPairs(torch)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        n = args.steps * layers
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        i = 0
+        for _ in range(args.steps):
+            for l in range(layers):
+                write(l)
+                ev[i][0].record()
+                call(l)
+                ev[i][1].record()
+                i += 1
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        return (t0.elapsed_time(t1) / args.steps, float(np.mean([a.elapsed_time(b) for a, b in ev])), wall,
+                "eager")
+    g_step, g_call = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step()
+    with torch.cuda.graph(g_call):
+        for l in range(layers):
+            call(l)
+    g_step.replay()
+    torch.cuda.synchronize()
+    replayed = out.clone()
+    write(layers - 1)
+    call(layers - 1)
+    torch.cuda.synchronize()
+    if not torch.equal(replayed, out):
+        raise SystemExit("bench.py: graph replay differs from the eager call")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for _ in range(steps):
-        step(ev)
+    for _ in range(args.steps):
+        g_step.replay()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return t0.elapsed_time(t1) / steps, ev.mean_ms(), wall
+    ms_step = t0.elapsed_time(t1) / args.steps
+    t0.record()
+    for _ in range(args.steps):
+        g_call.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_call = t0.elapsed_time(t1) / (args.steps * layers)
+    return ms_step, ms_call, wall, "hip-graph"
 
 
 def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s):
@@ -170,15 +207,9 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     scale = w.scale
 
-    def step(ev):
-        for l in range(layers):
-            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
-            s = ev.start() if ev else None
-            pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws)
-            if ev:
-                ev.stop(s)
-
-    ms_step, ms_decode, wall = time_steps(torch, step, args.steps, args.warmup)
+    ms_step, ms_decode, wall, mode = time_layers(
+        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
+        lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws), out)
     dec_bytes = w.algorithmic_bytes(out_bytes=4)
     write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
     step_bytes = layers * (dec_bytes + write_bytes)
@@ -222,7 +253,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
-        "wall_s": round(wall, 3),
+        "timing": mode, "wall_s": round(wall, 3),
     }
     return res
 
@@ -250,15 +281,9 @@ def bench_prefill(args, torch, pa, W, w, layers):
     out = torch.empty(Tq, Hq, D, device=dev, dtype=torch.float32)
     max_q, max_len = int(w.chunk_lens.max()), int(w.layout.seq_lens.max())
 
-    def step(ev):
-        for l in range(layers):
-            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
-            s_ = ev.start() if ev else None
-            pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len)
-            if ev:
-                ev.stop(s_)
-
-    ms_step, ms_call, wall = time_steps(torch, step, args.steps, args.warmup)
+    ms_step, ms_call, wall, mode = time_layers(
+        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
+        lambda l: pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len), out)
     flops = w.flops()
     tflops = flops / (ms_call * 1e-3) / 1e12
     # sampled parity: the last 8 rows of sequence 0 and the first 8 rows of the last sequence,
@@ -315,7 +340,8 @@ def bench_prefill(args, torch, pa, W, w, layers):
                      "traffic": measured_traffic(w.name), "traffic_unit": "bytes per call",
                      "kernel": "paged_attn_prefill_chunk call", "flops_per_launch": flops,
                      "avg_launch_ms": round(ms_call, 5)},
-        "cpu_baseline": cpu, "parity_max_abs_err_sampled_rows": max(errs), "wall_s": round(wall, 3),
+        "cpu_baseline": cpu, "parity_max_abs_err_sampled_rows": max(errs), "timing": mode,
+        "wall_s": round(wall, 3),
     }
 
 
@@ -340,15 +366,9 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
     copies = w.copies
     pairs = torch.from_numpy(np.asarray(copies, np.int64).reshape(-1, 2)).to(dev)
 
-    def step(ev):
-        for l in range(layers):
-            pa.kv_cache_write(newk, newv, K[l], V[l], slots)
-            s_ = ev.start() if ev else None
-            pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, w.scale, max_len, 0, ws)
-            if ev:
-                ev.stop(s_)
-
-    ms_step, ms_call, wall = time_steps(torch, step, args.steps, args.warmup)
+    ms_step, ms_call, wall, mode = time_layers(
+        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
+        lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, w.scale, max_len, 0, ws), out)
     logical = w.algorithmic_bytes(out_bytes=4)
     unique = w.extra["unique_blocks"] * w.block_size * Hkv * D * w.elem_bytes * 2
     copy = None
@@ -388,7 +408,8 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per call", "kernel": "paged_attn_decode call (logical KV bytes)", "bytes_per_launch": logical,
                      "unique_kv_bytes": unique, "avg_launch_ms": round(ms_call, 5)},
-        "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "wall_s": round(wall, 3),
+        "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "timing": mode,
+        "wall_s": round(wall, 3),
     }
 
 

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int r = lane >> 4, c = lane & 15;
   const int B = p.num_seqs, Hkv = p.num_kv_heads;
   const int g = p.num_heads / Hkv;
-  const int gi = blockIdx.x;
+  const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);  // this workgroup's range
   const int R = p.sk_range_blocks;
 
   // -- flat index space: exclusive prefix over sequences of blocks * Hkv ----

@@ -96,6 +96,17 @@ __device__ __forceinline__ float row_sum4(float v) {
   return c + d;
 }
 
+// Work items in a 1-D grid: consecutive workgroup ids are dealt round-robin
+// to the eight XCDs, each with its own L2.  Item L is renumbered so that every
+// XCD receives one contiguous run of the work list; neighbouring items, which
+// tend to read the same K/V blocks (the query tiles of one head, sequences
+// forked from one prompt), then share an L2 and run close together in time.
+__device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
+  constexpr unsigned kXcds = 8;
+  const unsigned q = N / kXcds, rem = N % kXcds, xcd = L % kXcds, pos = L / kXcds;
+  return xcd < rem ? xcd * (q + 1) + pos : rem * (q + 1) + (xcd - rem) * q + pos;
+}
+
 // 16-byte global load/store through a plain vector type (global_load_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }

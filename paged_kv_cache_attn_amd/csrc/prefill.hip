@@ -38,17 +38,6 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
   }
 }
 
-// Work items in a 1-D grid: consecutive workgroup ids are dealt round-robin
-// to the eight XCDs, each with its own L2.  Item L is renumbered so that every
-// XCD receives one contiguous run of the (sequence, KV head, query tile)
-// list; the query tiles of one head, which read the same K/V blocks, then
-// share an L2 and run close together in time.
-__device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
-  constexpr unsigned kXcds = 8;
-  const unsigned q = N / kXcds, rem = N % kXcds, xcd = L % kXcds, pos = L / kXcds;
-  return xcd < rem ? xcd * (q + 1) + pos : rem * (q + 1) + (xcd - rem) * q + pos;
-}
-
 // bf16 KV, head_dim 128, block_size 16, g in {1, 2, 4, 8, 16}.
 //
 // A workgroup of NW waves serves NW * CG * 16 / g consecutive chunk tokens of
