@@ -52,7 +52,7 @@ struct DecodePlan {
   bool too_large = false;
   int ranges = 0, range_blocks = 0;      // balanced path
   int part_blocks = 0, nparts = 1;       // partition-grid path
-  size_t off_part = 0, off_ml = 0, off_pref = 0, workspace_bytes = 0;
+  size_t off_part = 0, off_ml = 0, off_desc = 0, workspace_bytes = 0;
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -88,8 +88,8 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     const size_t ml = (size_t)pl.ranges * 2 * g * 2 * sizeof(float);
     pl.off_part = 0;
     pl.off_ml = align256(part);
-    pl.off_pref = pl.off_ml + align256(ml);
-    pl.workspace_bytes = pl.off_pref + align256((size_t)(num_seqs + 1) * sizeof(int));
+    pl.off_desc = pl.off_ml + align256(ml);
+    pl.workspace_bytes = pl.off_desc + align256((size_t)pl.ranges * 4 * sizeof(int));
     return pl;
   }
   const int64_t P = effective_partition(partition_size, block_size);
@@ -207,7 +207,7 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
     p.sk_range_blocks = plan.range_blocks;
     p.sk_part = reinterpret_cast<float *>(ws + plan.off_part);
     p.sk_ml = reinterpret_cast<float *>(ws + plan.off_ml);
-    p.sk_pref = reinterpret_cast<int *>(ws + plan.off_pref);
+    p.sk_desc = reinterpret_cast<int4 *>(ws + plan.off_desc);
     return launch_status(pa::launch_decode_streamk(p, s));
   }
   p.part_blocks = plan.part_blocks;

@@ -7,10 +7,12 @@
 // streams the same number of 8 KB K+V tiles whatever the length mix.  A
 // range covers whole rows, whose output it writes directly, and at most two
 // partial rows at its ends, for which it leaves (max, sum, unnormalised
-// output) in the workspace with plain stores.  A second, small kernel merges
-// the pieces of every row that spans ranges, in ascending range order, with
-// the online-softmax merge rule (Lecture 16 "LLM Serving (1)" §3.3); the
-// kernel boundary makes the pieces visible across XCDs.  The split depends
+// output) in the workspace with plain stores, and a range that holds the
+// last piece of such a row writes a descriptor of it.  A second, small
+// kernel (one workgroup per range) merges the pieces of those rows, in
+// ascending range order, with the online-softmax merge rule (Lecture 16 "LLM
+// Serving (1)" §3.3); the kernel boundary makes the pieces visible across
+// XCDs.  The split depends
 // only on logical block positions, so results are bit-identical under any
 // physical block permutation.
 #include "attn_core.h"
@@ -133,9 +135,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int T = s_pref[B];
   const int G = ranges_used((int)gridDim.x, T, R);
 
-  // workgroup 0 publishes the prefix for the merge kernel
-  if (gi == 0)
-    for (int b = tid; b <= B; b += 64 * NW) p.sk_pref[b] = s_pref[b];
+  // no split row ends in this range unless the combine below says so
+  if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
 
   // -- rows with no tokens get zeros (spread over the workgroups) -----------
   for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
@@ -296,6 +297,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool whole = rs >= s && rs + nb <= e;
     const int slot = rs <= s ? 0 : 1;
     const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+    if (!whole && slot == 0 && rs + nb <= e && tid == 0) {
+      // this range holds the last piece of a row that began in an earlier one
+      const int g_first = range_of(rs, T, G, R);
+      p.sk_desc[gi] = int4{row, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
+    }
     for (int idx = tid; idx < g * kD; idx += 64 * NW) {
       const int cc = idx / kD, d = idx - cc * kD;
       float mv[NE], lv[NE], ov[NE];
@@ -333,35 +339,58 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-// One workgroup per (sequence, KV head) row; rows that fit one range were
-// written by the main kernel and are skipped.  A thread owns output elements
-// (column, dim) and combines the row's pieces for them in ascending range
-// order; it issues the loads of up to kBatch pieces (their max, sum and
-// partial output) before it uses any, so a row costs one dependent memory
-// round trip per kBatch pieces, with no LDS and no barriers.
-__global__ __launch_bounds__(256) void decode_streamk_merge_kernel(DecodeParams p) {
+// One workgroup per range gi: if the range holds the last piece of a row
+// that began in an earlier range (its descriptor says so), the row's pieces
+// are merged, in ascending range order, and the row is written.  Most such
+// rows have exactly two pieces -- the end of range gi - 1 and the start of
+// range gi -- so those are loaded together with the descriptor, in one
+// memory round trip; rows with more pieces take a second one.  A thread
+// owns output elements (column, dim).
+__global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
-  const int row = blockIdx.x;
-  const int Hkv = p.num_kv_heads;
-  const int g = p.num_heads / Hkv;
-  const int b = row / Hkv, kh = row - b * Hkv;
-  const int B = p.num_seqs;
-  const int T = p.sk_pref[B];
-  const int p0 = p.sk_pref[b];
-  const int nb = (p.sk_pref[b + 1] - p0) / Hkv;
-  if (nb == 0) return;
-  const int R = p.sk_range_blocks;
-  const int G = ranges_used(p.sk_ranges, T, R);
-  const int row_start = p0 + kh * nb;
-  const int g_first = range_of(row_start, T, G, R);
-  const int g_last = range_of(row_start + nb - 1, T, G, R);
-  if (g_first == g_last) return;
-  const int nc = g_last - g_first + 1;
+  constexpr int kPer = 2;  // the launch uses g * kD / 2 threads: two elements each
+  const int gi = blockIdx.x;
+  const int g = p.num_heads / p.num_kv_heads;
+  const int gp = gi > 0 ? gi - 1 : 0;
+  const int4 dsc = p.sk_desc[gi];
+  // speculative: (gp, slot 0), (gp, slot 1), (gi, slot 0) for both elements
+  float sm[3][kPer], sl[3][kPer], so[3][kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = threadIdx.x + u * blockDim.x;
+    const int cc = idx / kD, d = idx - cc * kD;
+    const int64_t pc[3] = {((int64_t)gp * 2 + 0) * g + cc, ((int64_t)gp * 2 + 1) * g + cc, ((int64_t)gi * 2) * g + cc};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      sm[k][u] = p.sk_ml[pc[k] * 2];
+      sl[k][u] = p.sk_ml[pc[k] * 2 + 1];
+      so[k][u] = p.sk_part[pc[k] * kD + d];
+    }
+  }
+  asm volatile("" ::: "memory");  // keep those loads ahead of the branch below
+  const int row = dsc.x;
+  if (row < 0) return;
+  const int g_first = dsc.y, s_first = dsc.z, nc = dsc.w;
+  const int b = row / p.num_kv_heads, kh = row - b * p.num_kv_heads;
   const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+  if (nc == 2) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x;
+      const int cc = idx / kD, d = idx - cc * kD;
+      const int f = s_first;  // first piece: (gi - 1, s_first); second: (gi, 0)
+      const float m0 = sm[f][u], m1 = sm[2][u];
+      const float M = fmaxf(m0, m1);
+      const float Mu = M == kNegInf ? 0.f : M;
+      const float w0 = fast_exp2(m0 - Mu), w1 = fast_exp2(m1 - Mu);
+      const float ls = sl[f][u] * w0 + sl[2][u] * w1;
+      const float o = so[f][u] * w0 + so[2][u] * w1;
+      store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? o / ls : 0.f);
+    }
+    return;
+  }
   auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
-    const int gg = g_first + k;
-    const int sl = row_start <= range_begin(gg, T, G, R) ? 0 : 1;
-    return ((int64_t)gg * 2 + sl) * g + cc;
+    return ((int64_t)(g_first + k) * 2 + (k == 0 ? s_first : 0)) * g + cc;
   };
   for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x) {
     const int cc = idx / kD, d = idx - cc * kD;
@@ -404,7 +433,7 @@ hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
                      park, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.num_seqs * p.num_kv_heads), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ struct DecodeParams {
   int sk_range_blocks;     // 0: T / sk_ranges blocks each (balanced); > 0: fixed
   float *sk_part;          // [ranges][2][g][D] partial outputs
   float *sk_ml;            // [ranges][2][g][2] partial (max, sum)
-  int *sk_pref;            // [B + 1] first flat block of each sequence
+  int4 *sk_desc;           // [ranges] split row whose last piece the range holds:
+                           // {row or -1, first range, slot of the first piece, pieces}
 };
 
 // Library choice of split-K partition size (tokens) for these sizes.

@@ -103,11 +103,11 @@ def _a256(x):
 
 def test_decode_workspace_size(pa):
     f = pa.paged_attn_decode_workspace_size
-    # 8B shape, library choice: 512 balanced ranges, 2 partial slots each, plus one ticket per row
+    # 8B shape, library choice: 512 balanced ranges, 2 partial slots each, plus a 16-byte descriptor each
     B, Hq, Hkv, D, bs = 64, 32, 8, 128, 16
     g = Hq // Hkv
     ranges = 512
-    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256((B + 1) * 4)
+    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256(ranges * 16)
     grid = _a256(B * Hq * 16 * D * 4) + _a256(B * Hq * 16 * 2 * 4)       # 4096 / 256 partitions
     assert f(B, Hq, Hkv, D, bs, 4096, 0) == max(streamk, grid)
     # fixed 512-token pieces on 32K-token rows: 64 pieces per row, so the partition grid
@@ -117,14 +117,14 @@ def test_decode_workspace_size(pa):
     # fixed 4096-token pieces on the same rows: 8 pieces per row, the balanced split
     g = Hq // Hkv
     ranges = B * Hkv * (32768 // 16) // 256
-    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256((B + 1) * 4)
+    streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256(ranges * 16)
     grid = _a256(B * Hq * 8 * D * 4) + _a256(B * Hq * 8 * 2 * 4)
     assert f(B, Hq, Hkv, D, bs, 32768, 4096) == max(streamk, grid)
     # tiny problem, explicit 64-token pieces: fewer ranges than the default
     t_up = 4 * 2 * 13
     ranges = (t_up + 3) // 4
     assert f(4, 8, 2, 64, 16, 203, 64) == (_a256(ranges * 2 * 4 * 64 * 4) + _a256(ranges * 2 * 4 * 2 * 4)
-                                           + _a256((4 + 1) * 4))
+                                           + _a256(ranges * 16))
     assert f(0, 8, 2, 64, 16, 100, 0) == 0
     assert f(4, 8, 3, 64, 16, 100, 0) == 0          # invalid group
     assert f(4, 8, 2, 64, 16, 100, 24) == 0         # partition not a block multiple
