@@ -14,27 +14,35 @@ namespace pa {
 
 // One thread per 16-byte chunk of one (token, head) row; K and V handled by
 // the same thread.  row_chunks = head_dim * elem_bytes / 16.
+// I: the index type of the chunk arithmetic (32-bit whenever the counts fit,
+// which keeps the divisions short).  The key/value chunk is loaded before the
+// slot is known (its address does not depend on it), so the slot load and the
+// data loads share one memory round trip.
+template <typename I>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const uint8_t *__restrict__ key, const uint8_t *__restrict__ value,
     uint8_t *__restrict__ k_cache, uint8_t *__restrict__ v_cache,
-    const int64_t *__restrict__ slot_mapping, int64_t total_chunks, int num_kv_heads,
+    const int64_t *__restrict__ slot_mapping, I total_chunks, int num_kv_heads,
     int block_size, int row_chunks, int64_t num_slots) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const I gid = (I)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total_chunks) return;
-  const int chunk = (int)(gid % row_chunks);
-  const int64_t row = gid / row_chunks;  // t * num_kv_heads + h
-  const int h = (int)(row % num_kv_heads);
-  const int64_t t = row / num_kv_heads;
+  const I chunk = gid % (I)row_chunks;
+  const I row = gid / (I)row_chunks;  // t * num_kv_heads + h
+  const I h = row % (I)num_kv_heads;
+  const I t = row / (I)num_kv_heads;
+  const int64_t row_bytes = (int64_t)row_chunks * 16;
+  const int64_t src = (int64_t)row * row_bytes + (int64_t)chunk * 16;
+  const u32x4 kv = ld16(key + src);
+  const u32x4 vv = ld16(value + src);
   const int64_t slot = slot_mapping[t];
+  // Consume all three loads before the slot test, so the compiler cannot sink
+  // the data loads behind it: they are issued together, one round trip.
+  asm volatile("" ::"v"(kv), "v"(vv), "v"(slot));
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot - blk * block_size);
   const int64_t dst_row = (blk * num_kv_heads + h) * block_size + off;
-  const int64_t row_bytes = (int64_t)row_chunks * 16;
-  const int64_t src = row * row_bytes + chunk * 16;
-  const int64_t dst = dst_row * row_bytes + chunk * 16;
-  const u32x4 kv = ld16(key + src);
-  const u32x4 vv = ld16(value + src);
+  const int64_t dst = dst_row * row_bytes + (int64_t)chunk * 16;
   st16(k_cache + dst, kv);
   st16(v_cache + dst, vv);
 }
@@ -73,10 +81,15 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cac
   const int64_t total = (int64_t)num_tokens * num_kv_heads * row_chunks;
   if (total == 0) return hipSuccess;
   const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(kv_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const uint8_t *)key, (const uint8_t *)value, (uint8_t *)k_cache,
-                     (uint8_t *)v_cache, slot_mapping, total, num_kv_heads, block_size, row_chunks,
-                     (int64_t)num_blocks * block_size);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (total < INT32_MAX && num_slots < INT32_MAX)
+    hipLaunchKernelGGL(kv_cache_write_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint8_t *)key, (const uint8_t *)value, (uint8_t *)k_cache, (uint8_t *)v_cache,
+                       slot_mapping, (uint32_t)total, num_kv_heads, block_size, row_chunks, num_slots);
+  else
+    hipLaunchKernelGGL(kv_cache_write_kernel<int64_t>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint8_t *)key, (const uint8_t *)value, (uint8_t *)k_cache, (uint8_t *)v_cache,
+                       slot_mapping, total, num_kv_heads, block_size, row_chunks, num_slots);
   return hipGetLastError();
 }
 
