@@ -89,6 +89,57 @@ def parse():
     return ap.parse_args()
 
 
+STEP_STATS = {}  # per-step time distribution (ms) of the last graph-timed run
+
+
+def time_calls(args, torch, layers, call):
+    """Mean ms of call(l) over the layers, timed like the attention calls
+    (a replayed graph of the `layers` calls, or eager events)."""
+    if args.no_graph:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            for l in range(layers):
+                call(l)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (args.steps * layers)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(layers):
+            call(l)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (args.steps * layers)
+
+
+def measured_copy_gbs(torch):
+    """Read + write GB/s of a 1 GiB device-to-device copy on this GPU (the
+    practical bandwidth a streaming kernel can be compared with)."""
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(10):
+        y.copy_(x)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 10 / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def time_layers(args, torch, layers, write, call, out):
     """Time one step (every layer: write(l) then call(l)) and the attention call alone.
 
@@ -142,15 +193,19 @@ def time_layers(args, torch, layers, write, call, out):
     torch.cuda.synchronize()
     if not torch.equal(replayed, out):
         raise SystemExit("bench.py: graph replay differs from the eager call")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         g_step.replay()
-    t1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    STEP_STATS.update(p10=round(float(np.percentile(per, 10)), 4), p50=round(float(np.median(per)), 4),
+                      p90=round(float(np.percentile(per, 90)), 4))
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(args.steps):
         g_call.replay()
@@ -210,6 +265,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     ms_step, ms_decode, wall, mode = time_layers(
         args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
         lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws), out)
+    copy_gbs = measured_copy_gbs(torch)
     dec_bytes = w.algorithmic_bytes(out_bytes=4)
     write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
     step_bytes = layers * (dec_bytes + write_bytes)
@@ -253,7 +309,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
-        "timing": mode, "wall_s": round(wall, 3),
+        "timing": mode, "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")],
+        "copy_GBs_read_plus_write": copy_gbs, "wall_s": round(wall, 3),
     }
     return res
 
@@ -284,6 +341,8 @@ def bench_prefill(args, torch, pa, W, w, layers):
     ms_step, ms_call, wall, mode = time_layers(
         args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
         lambda l: pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len), out)
+    ms_write = time_calls(args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots))
+    write_bytes = Tq * Hkv * D * 2 * 2 * 2 + 8 * Tq  # K and V rows read and written, bf16, + slots
     flops = w.flops()
     tflops = flops / (ms_call * 1e-3) / 1e12
     # sampled parity: the last 8 rows of sequence 0 and the first 8 rows of the last sequence,
@@ -340,7 +399,10 @@ def bench_prefill(args, torch, pa, W, w, layers):
                      "traffic": measured_traffic(w.name), "traffic_unit": "bytes per call",
                      "kernel": "paged_attn_prefill_chunk call", "flops_per_launch": flops,
                      "avg_launch_ms": round(ms_call, 5)},
+        "kv_cache_write": {"rows": Tq * Hkv, "us_per_call": round(ms_write * 1e3, 3),
+                           "GBs": round(write_bytes / (ms_write * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu, "parity_max_abs_err_sampled_rows": max(errs), "timing": mode,
+        "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")],
         "wall_s": round(wall, 3),
     }
 
@@ -407,9 +469,10 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per call", "kernel": "paged_attn_decode call (logical KV bytes)", "bytes_per_launch": logical,
-                     "unique_kv_bytes": unique, "avg_launch_ms": round(ms_call, 5)},
+                     "unique_kv_bytes": unique, "unique_GBs": round(unique / (ms_call * 1e-3) / 1e9, 2),
+                     "avg_launch_ms": round(ms_call, 5)},
         "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "timing": mode,
-        "wall_s": round(wall, 3),
+        "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")], "wall_s": round(wall, 3),
     }
 
 
