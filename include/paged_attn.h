@@ -48,8 +48,11 @@
  *     unspecified.
  *   - Supported shapes.  Attention calls: head_dim in {64, 128}, any
  *     block_size >= 1, num_heads % num_kv_heads == 0 (the MFMA kernels serve
- *     bf16 KV with head_dim 128, block_size 16 and a GQA group of at most 16;
- *     other supported shapes run on plain vector kernels).  kv_cache_write
+ *     bf16 KV with head_dim 128, block_size in {8, 16, 32, 64, 128} and a GQA
+ *     group of at most 16 (prefill: a divisor of 16), walking each sequence
+ *     in 16-token tiles; other supported shapes run on plain vector kernels),
+ *     one physical block of num_kv_heads * block_size * head_dim elements
+ *     below 2^31 and a whole cache (num_blocks such blocks) below 2^41.  kv_cache_write
  *     and block_copy: any block_size >= 1 and any head_dim whose row is a
  *     multiple of 16 bytes.  Anything else returns PA_ERR_UNSUPPORTED.
  */
@@ -145,7 +148,9 @@ PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_
  *                 exponentials, unnormalised output) and the pieces are merged
  *                 by the online-softmax rule ([L16] §3.3) in a fixed order, so
  *                 results are bit-identical for any physical block permutation
- *                 and agree to rounding for any partition_size.
+ *                 and agree to rounding for any partition_size.  On the
+ *                 MFMA kernels a piece is a whole number of 16-token tiles:
+ *                 partition_size is rounded down to one (at least one tile).
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL when
  *                 that size is 0).  Contents on entry are ignored.  Two calls

@@ -40,6 +40,10 @@ int check_attention_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
   if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (!dtype_ok(kv_dtype) || !dtype_ok(out_dtype)) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // one physical block (all KV heads) is addressed with 32-bit element offsets
+  if ((int64_t)num_kv_heads * block_size * head_dim > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  // ... and a whole cache with 8-row offsets in 31 bits (2^41 elements: terabytes)
+  if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim >= ((int64_t)1 << 41)) return PA_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -60,7 +64,10 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   DecodePlan pl;
   const int g = num_heads / num_kv_heads;
   const int64_t rows = (int64_t)num_seqs * num_kv_heads;
-  const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, block_size) : 0;
+  // the unit of the split: 16-token tiles on the MFMA path, blocks otherwise
+  const int unit = mfma_shape ? 16 : block_size;
+  const int64_t part_units = partition_size > 0 ? std::max<int64_t>(1, partition_size / unit) : 0;
+  const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, unit) : 0;
   const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
   (void)max_seq_len;
   // The balanced split pays off when the rows are many and split into few
@@ -71,14 +78,14 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   const int64_t sk_ranges_default = std::max<int64_t>(
       {1, std::min<int64_t>(pa::kStreamKRanges, t_upper), ceil_div(t_upper, pa::kStreamKTabCache)});
   const int64_t pieces_per_row =
-      partition_size > 0 ? ceil_div(std::max<int64_t>(blocks_per_row, 1), partition_size / block_size)
+      partition_size > 0 ? ceil_div(std::max<int64_t>(blocks_per_row, 1), part_units)
                          : ceil_div(sk_ranges_default, std::max<int64_t>(rows, 1)) + 1;
   if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff &&
       pieces_per_row <= kStreamKMaxPiecesPerRow &&
-      (partition_size == 0 || partition_size / block_size <= pa::kStreamKTabCache)) {
+      (partition_size == 0 || part_units <= pa::kStreamKTabCache)) {
     pl.streamk = true;
     if (partition_size > 0) {
-      pl.range_blocks = partition_size / block_size;
+      pl.range_blocks = (int)part_units;
       pl.ranges = (int)std::max<int64_t>(1, ceil_div(t_upper, pl.range_blocks));
     } else {
       pl.range_blocks = 0;
@@ -93,12 +100,13 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     return pl;
   }
   const int64_t P = effective_partition(partition_size, block_size);
-  const int64_t nparts = cap > 0 ? ceil_div(cap, P) : 1;
+  const int64_t pu = std::max<int64_t>(1, P / unit);  // units per partition
+  const int64_t nparts = cap > 0 ? ceil_div(blocks_per_row, pu) : 1;
   if (nparts > 0x7fffffff) {
     pl.too_large = true;
     return pl;
   }
-  pl.part_blocks = (int)(P / block_size);
+  pl.part_blocks = (int)pu;
   pl.nparts = (int)nparts;
   if (nparts > 1) {
     const size_t o = (size_t)num_seqs * num_heads * nparts * head_dim * sizeof(float);
@@ -174,7 +182,7 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
 
   const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
-  const bool mfma_shape = kv_dtype == PA_BF16 && head_dim == 128 && block_size == 16 &&
+  const bool mfma_shape = kv_dtype == PA_BF16 && head_dim == 128 && pa::mfma_block_size(block_size) &&
                           num_heads / num_kv_heads <= 16;
   DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                                 cap, partition_size, mfma_shape);
@@ -210,6 +218,7 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
     p.sk_desc = reinterpret_cast<int4 *>(ws + plan.off_desc);
     return launch_status(pa::launch_decode_streamk(p, s));
   }
+  p.tile_tokens = mfma_shape ? 16 : block_size;
   p.part_blocks = plan.part_blocks;
   p.nparts_max = plan.nparts;
   p.ws_o = plan.workspace_bytes > 0 ? reinterpret_cast<float *>(ws + plan.off_part) : nullptr;

@@ -39,6 +39,73 @@ __device__ __forceinline__ void load_kv_tile_d128(KVTile &t, const uint16_t *kt,
   for (int v = 0; v < 4; ++v) t.v[v] = ld16(vt + (4 * r + v) * 128 + 8 * c);
 }
 
+// -- 16-token tiles over any block size ---------------------------------------
+// The kernels walk a (sequence, KV head) row in tiles of 16 consecutive
+// tokens whatever the cache's block size bs (M2 "PagedAttention" §5.3; the
+// cache is [num_blocks][Hkv][bs][128]).  With bs a multiple of 16, tile j lies
+// in block j / (bs / 16), starting at row (j mod (bs / 16)) * 16.  With bs = 8
+// its first eight tokens are block 2j and the last eight block 2j + 1.  A tile
+// is described by two table-derived entries e0, e1:
+//   bs >= 16: e0 = physical block, e1 = sub-tile index inside it;
+//   bs == 8:  e0, e1 = physical blocks of its two halves.
+// An entry out of range is replaced by block 0 and reported, so the caller
+// masks the tile instead of dereferencing it.  nblk_tab = ceil(L / bs) is the
+// number of table entries the row uses; the second half of a bs = 8 tile past
+// it is never read (its tokens are past L and masked).
+struct TileRows {
+  int64_t lo, hi;  // element offsets (from the cache base) of the tile's rows 0 and 8
+};
+struct TileMap {
+  int sh;        // log2(bs / 16) for bs >= 16, -1 for bs == 8
+  int num_blocks;
+  int hstride;   // elements of one KV head inside a block (bs * 128)
+  int blk;       // elements of one physical block (all KV heads; < 2^31 by the host checks)
+  __device__ __forceinline__ TileMap(int bs, int num_kv_heads, int nb) {
+    constexpr int D = 128;
+    sh = bs >= 16 ? __builtin_ctz((unsigned)bs) - 4 : -1;
+    num_blocks = nb;
+    hstride = bs * D;
+    blk = num_kv_heads * hstride;
+  }
+  // (TablePtr: a generic or a constant-address-space pointer to int32 entries.)
+  // Branch-free: both table reads are issued for every block size (for
+  // bs >= 16 the second one repeats the first address), so a loop that calls
+  // this stays one basic block.
+  template <typename TablePtr>
+  __device__ __forceinline__ bool entries(TablePtr table, int j, int nblk_tab, int &e0, int &e1) const {
+    const bool halves = sh < 0;
+    const int i0 = halves ? 2 * j : j >> (sh & 31);
+    const int i1 = halves && 2 * j + 1 < nblk_tab ? 2 * j + 1 : i0;
+    const int t0 = table[i0], t1 = table[i1];
+    const bool ok = (unsigned)t0 < (unsigned)num_blocks && (!halves || (unsigned)t1 < (unsigned)num_blocks);
+    e0 = ok ? t0 : 0;
+    e1 = halves ? (ok ? t1 : 0) : j & ((1 << (sh & 31)) - 1);
+    return ok;
+  }
+  // the rows of the tile with entries e0, e1 in KV head kh (32-bit selects
+  // only, then one multiply-add per row, so nothing here becomes a branch)
+  __device__ __forceinline__ TileRows rows(int e0, int e1, int kh) const {
+    constexpr int D = 128;
+    const int head = kh * hstride;
+    const bool halves = sh < 0;
+    const int blk_hi = halves ? e1 : e0;
+    const int off_lo = halves ? head : head + e1 * 16 * D;
+    const int off_hi = halves ? head : off_lo + 8 * D;
+    return {(int64_t)e0 * blk + off_lo, (int64_t)blk_hi * blk + off_hi};
+  }
+};
+
+// The operands of one tile (see load_kv_tile_d128) from its two row bases.
+__device__ __forceinline__ void load_kv_tile_rows(KVTile &t, const uint16_t *kc, const uint16_t *vc,
+                                                  const TileRows &tr, int r, int c) {
+  const int64_t kr = (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.k[i] = ld16(kc + kr + 32 * i + 8 * r);
+  const int64_t vr = r < 2 ? tr.lo : tr.hi;  // tokens 4r .. 4r+3 share a half
+#pragma unroll
+  for (int v = 0; v < 4; ++v) t.v[v] = ld16(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+}
+
 // Q^T operand for column c from a query row of 128 bf16 (nullptr -> zeros).
 __device__ __forceinline__ void load_q_operand_d128(bf16x8 qb[4], const uint16_t *qrow, int r) {
 #pragma unroll

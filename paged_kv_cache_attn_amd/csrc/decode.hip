@@ -41,10 +41,13 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 }
 
 // ----------------------------------------------------------------------------
-// MFMA kernel: bf16 KV, head_dim 128, block_size 16, g <= 16.
+// MFMA kernel: bf16 KV, head_dim 128, block size 8, 16, 32, 64 or 128
+// (walked in 16-token tiles), g <= 16.
 // Lane (r, c) = (lane >> 4, lane & 15); column c is query head kh*g + c.
+// The block size BSZ is a template argument so the table walk folds to
+// constants for each supported size.
 // ----------------------------------------------------------------------------
-template <int NW>
+template <int NW, int BSZ>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams p) {
   constexpr int D = 128;
   constexpr int BS = 16;
@@ -71,21 +74,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
 
   const float sl2 = p.scale * kLog2e;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(p.k_cache) + (int64_t)kh * BS * D;
-  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(p.v_cache) + (int64_t)kh * BS * D;
-  const int64_t blk_stride = (int64_t)p.num_kv_heads * BS * D;
+  const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
+  const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+  const int nblk_tab = (L + BSZ - 1) / BSZ;
+  const TileMap map(BSZ, p.num_kv_heads, p.num_blocks);
 
   MfmaAttnState st;
   st.init();
 
-  // An out-of-range table entry is never dereferenced: the tile is read from
-  // block 0 and fully masked.
+  // 16-token tile j (any supported block size).  An out-of-range table entry
+  // is never dereferenced: the tile is read from block 0 and fully masked.
   auto load = [&](int j, KVTile &t, int &lim) {
-    int phys = table[j];
-    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    int e0, e1;
+    const bool ok = map.entries(table, j, nblk_tab, e0, e1);
     lim = ok ? L : 0;
-    phys = ok ? phys : 0;
-    load_kv_tile_d128(t, kbase + phys * blk_stride, vbase + phys * blk_stride, r, c);
+    load_kv_tile_rows(t, kc, vc, map.rows(e0, e1, kh), r, c);
   };
 
   // Two-deep software pipeline: the next tile's loads are in flight while
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
   __shared__ float s_red[128];
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
-  const int nblk = (L + p.block_size - 1) / p.block_size;
+  const int nblk = (L + p.tile_tokens - 1) / p.tile_tokens;
   const int nparts = nblk == 0 ? 1 : (nblk + p.part_blocks - 1) / p.part_blocks;
   if (nparts <= 1) return;
   const int64_t row = (int64_t)b * p.num_heads + h;
@@ -339,12 +342,18 @@ size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int npa
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
-  const bool mfma = p.kv_bf16 && p.head_dim == 128 && p.block_size == 16 && g <= 16;
+  const bool mfma = p.kv_bf16 && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16;
   if (p.num_seqs == 0) return hipSuccess;
   if (mfma) {
-    dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL(decode_mfma_d128_kernel<PA_DECODE_WAVES>, grid, dim3(64 * PA_DECODE_WAVES), 0,
-                       stream, p);
+    const dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs), block(64 * PA_DECODE_WAVES);
+    constexpr int NW = PA_DECODE_WAVES;
+    switch (p.block_size) {
+      case 8: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 8>), grid, block, 0, stream, p); break;
+      case 16: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 16>), grid, block, 0, stream, p); break;
+      case 32: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 32>), grid, block, 0, stream, p); break;
+      case 64: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 64>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 128>), grid, block, 0, stream, p); break;
+    }
   } else {
     dim3 grid(p.nparts_max, p.num_heads, p.num_seqs);
     if (p.head_dim == 64) {

@@ -23,7 +23,7 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kBS = 16;
+constexpr int kBS = 16;  // tokens per tile: the unit of the flat space, whatever the block size
 
 
 // Range of workgroup gi: [range_begin(gi), range_begin(gi + 1)).
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int s_pref[kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
-  __shared__ int s_tab[kStreamKTabCache];      // physical block of each position of the range
+  __shared__ int2 s_rows[kStreamKTabCache];    // each position's tile rows 0 and 8, in 8-row
+                                               //   units (x = -1: a table entry out of range)
   __shared__ int s_prow[kStreamKTabCache + 1]; // row (b * Hkv + kh) of each position, -1 past the end
   __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
   __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
@@ -151,11 +152,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int e = range_begin(gi + 1, T, G, R);
   if (s >= e || e - s > kStreamKTabCache) return;  // the planner keeps ranges within the cache
 
-  // Stage, for every position of this range, its physical block, its row
-  // and its block index inside the row (one table load per position, all
-  // issued together), so the streaming loop does no searching and no tile
-  // load waits on a dependent table read.  The planner keeps ranges within
-  // kStreamKTabCache positions.
+  const TileMap map(p.block_size, Hkv, p.num_blocks);
+  // Stage, for every position of this range, where its tile's rows 0 and 8
+  // start (element offsets / 1024, exact: both are multiples of 8 rows of
+  // 128), its (sequence, KV head) row and its tile index inside the row (the
+  // table loads of all positions issued together), so the streaming loop does
+  // no searching and no tile load waits on a dependent table read.  The
+  // planner keeps ranges within kStreamKTabCache positions; the host keeps a
+  // cache below 2^41 elements, so the offsets / 1024 fit in 31 bits.
   for (int pos = s + tid; pos < e; pos += 64 * NW) {
     int lo = 0, hi = B;
     while (hi - lo > 1) {
@@ -165,7 +169,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
     const int off = pos - s_pref[lo];
     const int kh = off / nb, j = off - kh * nb;
-    s_tab[pos - s] = p.block_tables[(int64_t)lo * p.max_blocks_per_seq + j];
+    int e0, e1;
+    const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
+                                (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
+    const TileRows tr = map.rows(e0, e1, kh);
+    s_rows[pos - s] = ok ? int2{(int)(tr.lo >> 10), (int)(tr.hi >> 10)} : int2{-1, 0};
     s_prow[pos - s] = lo * Hkv + kh;
     s_pj[pos - s] = j;
   }
@@ -180,7 +188,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
   const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(p.q);
-  const int64_t blk_stride = (int64_t)Hkv * kBS * kD;
   const bool col_ok = c < g;
   const int c_ld = c < g ? c : g - 1;  // idle columns read a valid row, never stored
 
@@ -194,14 +201,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   auto load_slot = [&](int li, Slot &sl) {
     li = li < le ? li : le - 1;  // past the share: reload the last tile (unused)
-    int phys = s_tab[li];
+    const int2 u = s_rows[li];
     const int row = s_prow[li];
     const int b = row / Hkv, kh = row - b * Hkv;
-    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    const bool ok = u.x >= 0;
     sl.lim = ok ? s_len[b] : 0;
-    phys = ok ? phys : 0;
-    const int64_t base = phys * blk_stride + (int64_t)kh * kBS * kD;
-    load_kv_tile_d128(sl.t, kc + base, vc + base, r, c);
+    // a masked tile reads the first rows of the cache
+    load_kv_tile_rows(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
     load_q_operand_d128(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
   };
 

@@ -14,6 +14,10 @@
 
 namespace pa {
 
+// Block sizes the MFMA kernels take (they walk rows in 16-token tiles; a
+// tile is a whole block, part of one, or two blocks of 8).
+inline bool mfma_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
 // Balanced (stream-K) decode: largest batch whose per-sequence prefix fits the
 // workgroup's LDS, and the number of ranges the library picks by default.
 constexpr int kStreamKMaxSeqs = 2048;
@@ -47,7 +51,9 @@ struct DecodeParams {
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int max_len_cap;         // min(max_seq_len, max_blocks_per_seq * block_size)
   float scale;
-  int part_blocks;         // blocks per split-K partition
+  int tile_tokens;         // tokens per unit of part_blocks / the flat space: 16 on the MFMA
+                           // path (16-token tiles), block_size on the vector path
+  int part_blocks;         // units per split-K partition
   int nparts_max;          // ceil(ceil(max_len_cap / bs) / part_blocks), >= 1
   float *ws_o;             // [B][Hq][nparts_max][D]   (unused when nparts_max == 1)
   float *ws_ml;            // [B][Hq][nparts_max][2]   (max in log2 units, sum)

@@ -38,7 +38,8 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
   }
 }
 
-// bf16 KV, head_dim 128, block_size 16, g in {1, 2, 4, 8, 16}.
+// bf16 KV, head_dim 128, block size 8, 16, 32, 64 or 128 (walked in
+// 16-token tiles), g in {1, 2, 4, 8, 16}.
 //
 // A workgroup of NW waves serves NW * CG * 16 / g consecutive chunk tokens of
 // one KV head.  Wave w owns CG groups of 16 columns (16 / g tokens x the g
@@ -65,8 +66,9 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // Within a head the query tiles go heaviest (last in the chunk) first; a
 // column group skips the pairs past its causal bound, but every wave joins
 // every barrier.  grid = ntiles * Hkv * B workgroups, ntiles =
-// ceil(max_query_len / (NW * CG * 16 / g)).
-template <int NW, int CG>
+// ceil(max_query_len / (NW * CG * 16 / g)).  The block size BSZ is a template
+// argument so the table walk folds to constants for each supported size.
+template <int NW, int CG, int BSZ>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_d128_kernel(
     PrefillParams p, int ntiles) {
   constexpr int D = 128;
@@ -124,27 +126,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float sl2 = p.scale * kLog2e;
   const __attribute__((address_space(4))) int32_t *table =
       (const __attribute__((address_space(4))) int32_t *)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
-  const uint8_t *kbytes = reinterpret_cast<const uint8_t *>(p.k_cache) + (int64_t)kh * BS * D * 2;
-  const uint8_t *vbytes = reinterpret_cast<const uint8_t *>(p.v_cache) + (int64_t)kh * BS * D * 2;
-  const int64_t blk_bytes = (int64_t)p.num_kv_heads * BS * D * 2;
+  const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
+  const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+  const TileMap map(BSZ, p.num_kv_heads, p.num_blocks);
+  const int nblk_tab = (S + BSZ - 1) / BSZ;  // table entries the sequence uses
 
-  // Cooperative pair load: the 1024 16-byte chunks of a pair, consecutive
-  // threads on consecutive chunks of a tile.  Returns which of the two blocks
-  // hold real data (bit 0: A, bit 1: B); block j >= nblk (the odd tail) and
-  // an out-of-range table entry are read from block 0 and masked later.
+  // Cooperative pair load: the 1024 16-byte chunks of a pair of 16-token
+  // tiles, consecutive threads on consecutive chunks of a tile.  Returns
+  // which of the two tiles hold real data (bit 0: A, bit 1: B); tile
+  // j >= nblk (the odd tail) and a tile with an out-of-range table entry are
+  // read from block 0 and masked later.  Which tile, K or V, and which half
+  // of the tile (rows 0-7 or 8-15) a thread loads is the same for its whole
+  // wave, so the two row bases are selected in scalar registers.
   auto gload = [&](int pr, u32x4 *regs) -> int {
     pr = min(pr, max(npair - 1, 0));
     const int ja = 2 * pr, jb = 2 * pr + 1;
-    const int ta = table[ja];
-    const int tb = jb < nblk ? table[jb] : -1;
-    const bool oka = (unsigned)ta < (unsigned)p.num_blocks, okb = (unsigned)tb < (unsigned)p.num_blocks;
-    const int64_t ba = (oka ? ta : 0) * blk_bytes, bb = (okb ? tb : 0) * blk_bytes;
+    int a0, a1, b0, b1;
+    const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
+    const bool okb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1) && jb < nblk;
+    const TileRows ra = map.rows(a0, a1, kh);
+    const TileRows rb = map.rows(b0, b1, kh);  // the odd tail repeats tile nblk - 1, masked
 #pragma unroll
     for (int k = 0; k < kChunksPerThread; ++k) {
-      const int u = tid + k * 64 * NW;
-      const int kind = u >> 8, q = u & 255;  // kind: 0 K_a, 1 V_a, 2 K_b, 3 V_b
-      const uint8_t *src = ((kind & 1) ? vbytes : kbytes) + (kind < 2 ? ba : bb) + q * 16;
-      regs[k] = ld16(src);
+      const int uw = w * 64 + k * 64 * NW;  // first chunk of the wave (a multiple of 64)
+      const int kind = uw >> 8;             // 0 K_a, 1 V_a, 2 K_b, 3 V_b
+      const TileRows &tr = kind < 2 ? ra : rb;
+      // rows 8-15 start 8 rows after their own base: rebase so chunk q sits at q * 8
+      const int64_t base = (uw & 128) == 0 ? tr.lo : tr.hi - 8 * D;
+      regs[k] = ld16(((kind & 1) ? vc : kc) + base + ((uw & 255) + lane) * 8);
     }
     return (int)oka | ((int)okb << 1);
   };
@@ -310,15 +319,21 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_query_len == 0) return hipSuccess;
   const int g = p.num_heads / p.num_kv_heads;
-  const bool mfma = p.kv_bf16 && p.head_dim == 128 && p.block_size == 16 && g <= 16 && (16 % g) == 0;
+  const bool mfma = p.kv_bf16 && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16 && (16 % g) == 0;
   if (mfma) {
     constexpr int NW = PA_PREFILL_WAVES, CG = PA_PREFILL_GROUPS;
     const int tpg = NW * CG * (16 / g);
     const int64_t ntiles = (p.max_query_len + tpg - 1) / tpg;
     const int64_t items = ntiles * p.num_kv_heads * p.num_seqs;
     if (items * 64 * NW > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG>), dim3((unsigned)items), dim3(64 * NW), 0, stream, p,
-                       (int)ntiles);
+    const dim3 grid((unsigned)items), block(64 * NW);
+    switch (p.block_size) {
+      case 8: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 8>), grid, block, 0, stream, p, (int)ntiles); break;
+      case 16: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 16>), grid, block, 0, stream, p, (int)ntiles); break;
+      case 32: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 32>), grid, block, 0, stream, p, (int)ntiles); break;
+      case 64: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 64>), grid, block, 0, stream, p, (int)ntiles); break;
+      default: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 128>), grid, block, 0, stream, p, (int)ntiles); break;
+    }
   } else {
     dim3 grid(p.max_query_len, p.num_heads, p.num_seqs);
     if (p.head_dim == 64) {

@@ -157,6 +157,66 @@ def test_decode_other_block_sizes(pa, dtype, bs):
     assert max_err(out, ref) <= TOL[dtype]
 
 
+MFMA_BLOCK_SIZES = [8, 32, 64, 128]
+
+
+@pytest.mark.parametrize("bs", MFMA_BLOCK_SIZES)
+def test_decode_mfma_block_sizes(pa, bs):
+    """bf16 / head_dim 128 at every block size the MFMA kernels walk in 16-token
+    tiles: lengths around the block and tile edges, on the balanced split (auto
+    and explicit pieces) and on the partition grid (one-tile pieces of a long row)."""
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, bs - 1, bs, bs + 1, 2 * bs + 3, 333, 1000]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, bs, "bf16", seed=400 + bs)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.09)
+    for part in (0, max(bs, 64), 4 * bs, bs):
+        out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.09, "f32", part))
+        err = max_err(out, ref)
+        assert err <= TOL["bf16"], (part, err)
+        assert np.all(out[0] == 0)
+    # a long row cut into one-tile pieces takes the partition grid
+    lens = [3000, 5, 2049]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, bs, "bf16", seed=500 + bs)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.09)
+    out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.09, "f32", bs))
+    assert max_err(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("bs", [8, 64])
+def test_decode_block_size_permutation_bit_exact(pa, bs):
+    lens = [33, 700, 5, 1029]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, bs, "bf16", seed=78)
+    lay2 = synth.build_paged_layout(lens, bs, seed=4321, pool_factor=1.9)
+    k2 = np.zeros((lay2.num_blocks,) + k.shape[1:], k.dtype)
+    v2 = np.zeros_like(k2)
+    for b, L in enumerate(lens):
+        for j in range((L + bs - 1) // bs):
+            k2[lay2.block_tables[b, j]] = k[lay.block_tables[b, j]]
+            v2[lay2.block_tables[b, j]] = v[lay.block_tables[b, j]]
+    for part in (0, 128):
+        o1 = gpu_decode(pa, lay, q, k, v, 0.1, "f32", part).cpu().numpy()
+        o2 = gpu_decode(pa, lay2, q, k2, v2, 0.1, "f32", part).cpu().numpy()
+        assert np.array_equal(o1, o2), part
+
+
+@pytest.mark.parametrize("bs", [8, 16, 64])
+def test_decode_bad_table_entry_is_contained(pa, bs):
+    """An out-of-range block id is masked, never dereferenced: the other
+    sequences still match the oracle and every output is finite."""
+    lens = [500, 300, 77, 1000]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, bs, "bf16", seed=90 + bs)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.1)
+    bad = lay.block_tables.copy()
+    bad[1, 3] = lay.num_blocks + 5
+    bad[3, (1000 // bs) - 1] = -3
+    lay_bad = synth.PagedLayout(seq_lens=lay.seq_lens, block_tables=bad, num_blocks=lay.num_blocks,
+                                block_size=bs)
+    for part in (0, 16 if bs <= 16 else bs):
+        out = out_to_f64(gpu_decode(pa, lay_bad, q, k, v, 0.1, "f32", part))
+        assert np.isfinite(out).all(), part
+        for b in (0, 2):
+            assert max_err(out[b], ref[b]) <= TOL["bf16"], (part, b)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_permutation_bit_exact(pa, dtype):
     """Same logical K/V under another physical permutation: identical bits."""
@@ -235,6 +295,19 @@ def test_prefill_parity(pa, dtype, D, Hq, Hkv):
     out, _ = gpu_prefill(pa, lay, chunk, q, k, v, scale)
     err = max_err(out_to_f64(out), ref)
     assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("bs", MFMA_BLOCK_SIZES)
+def test_prefill_mfma_block_sizes(pa, bs):
+    total = [40, 64, 17, 5, 300, 1, 129, 2 * bs + 3]
+    chunk = [13, 64, 1, 5, 37, 1, 128, bs + 2]
+    lay, _, k, v = rand_problem(total, 32, 8, 128, bs, "bf16", seed=600 + bs)
+    q = W.host_values((sum(chunk), 32, 128), 1.0, 4343 + bs, "bf16")
+    qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    ref = oracle.paged_prefill(q, k, v, lay.block_tables, qsl, lay.seq_lens, 0.088)
+    out, _ = gpu_prefill(pa, lay, chunk, q, k, v, 0.088)
+    err = max_err(out_to_f64(out), ref)
+    assert err <= TOL["bf16"], err
 
 
 def test_prefill_one_row_equals_decode(pa):
