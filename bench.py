@@ -79,7 +79,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
                     choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
-                             "chunked_prefill", "copy_calibration"])
+                             "chunked_prefill", "block_size_sweep", "copy_calibration"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
@@ -476,6 +476,55 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
     }
 
 
+def slot_waste(layout):
+    """Internal fragmentation of a layout: the unused slots of every sequence's last block."""
+    lens = layout.seq_lens.astype(np.int64)
+    alloc = int((((lens + layout.block_size - 1) // layout.block_size) * layout.block_size).sum())
+    return alloc - int(lens.sum()), alloc
+
+
+def bench_block_sizes(args, torch, pa, W):
+    """The 8B decode batch and the chunked prefill at block sizes 8 ... 128: kernel
+    time, effective bandwidth / MFMA rate, and the slots the block size wastes
+    (the unused tail of each sequence's last block)."""
+    import copy as _copy
+    sub = _copy.copy(args)
+    sub.no_cpu_baseline = True
+    rows = []
+    for bs in (8, 16, 32, 64, 128):
+        w = W.llama8b_decode(block_size=bs)
+        d = bench_decode(sub, torch, pa, W, w, args.layers or 32, 0)
+        p_w = W.chunked_prefill(block_size=bs)
+        p = bench_prefill(sub, torch, pa, W, p_w, args.layers or 32)
+        waste, alloc = slot_waste(w.layout)
+        rows.append({
+            "block_size": bs,
+            "decode_us_per_call": round(d["roofline"]["avg_launch_ms"] * 1e3, 3),
+            "decode_kernel_GBs": d["roofline"]["achieved"], "decode_step_GBs": d["value"],
+            "decode_ms_per_step_p50": d["ms_per_step_p10_p50_p90"][1],
+            "prefill_us_per_call": round(p["roofline"]["avg_launch_ms"] * 1e3, 3),
+            "prefill_TFLOPs": p["roofline"]["achieved"],
+            "decode_slots_allocated": alloc, "decode_slots_wasted": waste,
+            "waste_frac": round(waste / alloc, 4), "table_entries": int(alloc // bs),
+            "prefill_parity_max_abs_err_sampled_rows": p["parity_max_abs_err_sampled_rows"],
+        })
+        print("block size %d: decode %.1f us, prefill %.1f us, waste %.2f%%" % (
+            bs, rows[-1]["decode_us_per_call"], rows[-1]["prefill_us_per_call"], 100 * rows[-1]["waste_frac"]),
+            file=sys.stderr, flush=True)
+        del d, p
+        torch.cuda.empty_cache()
+    ref = next(r for r in rows if r["block_size"] == 16)
+    return {
+        "metric": METRIC, "value": ref["decode_step_GBs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ref["decode_ms_per_step_p50"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "block_size_sweep", "decode": "llama8b_decode_bf16 lengths at each block size",
+                   "prefill": "chunked_prefill_bf16 at each block size", "layers": args.layers or 32,
+                   "value_is": "decode step GB/s at block size 16"},
+        "sweep": rows, "cpu_baseline": None,
+    }
+
+
 def bench_copy(args, torch):
     """A plain device copy of known size: the reference for scaling the HBM byte counters."""
     n = 1 << 30
@@ -527,6 +576,8 @@ def main():
     elif args.workload in ("shared_prefix", "shared_prefix_cow"):
         w = W.shared_prefix(prompt_len=512 if args.workload == "shared_prefix" else 500)
         res = bench_shared_prefix(args, torch, pa, W, w, args.layers or 32)
+    elif args.workload == "block_size_sweep":
+        res = bench_block_sizes(args, torch, pa, W)
     elif args.workload == "copy_calibration":
         res = bench_copy(args, torch)
     else:

@@ -131,10 +131,12 @@ def tiny_decode() -> DecodeWorkload:
     return DecodeWorkload("tiny_decode_fp32", lay, 8, 2, 64, "f32", 1.0, seed=1)
 
 
-def llama8b_decode(batch: int = 64, seed: int = 2) -> DecodeWorkload:
+def llama8b_decode(batch: int = 64, seed: int = 2, block_size: int = 16) -> DecodeWorkload:
+    """The same lengths at any block size (the pool is 1.25x the blocks they need)."""
     lens = lognormal_lengths(batch, 390, SIGMA_8B, 16, 4096, seed=seed)
-    lay = build_paged_layout(lens, 16, seed=seed + 1000, pool_factor=1.25)
-    return DecodeWorkload("llama8b_decode_bf16", lay, 32, 8, 128, "bf16", 0.5, seed=seed)
+    lay = build_paged_layout(lens, block_size, seed=seed + 1000, pool_factor=1.25)
+    name = "llama8b_decode_bf16" + ("" if block_size == 16 else "_bs%d" % block_size)
+    return DecodeWorkload(name, lay, 32, 8, 128, "bf16", 0.5, seed=seed)
 
 
 def llama70b_long(batch: int = 8, seq_len: int = 32768, seed: int = 4) -> DecodeWorkload:
@@ -184,10 +186,11 @@ def shared_prefix(prompts: int = 16, prompt_len: int = 512, samples: int = 8, ma
     return w
 
 
-def chunked_prefill(batch: int = 16, prefix: int = 1024, chunk: int = 512, seed: int = 5) -> PrefillWorkload:
-    lay = build_paged_layout([prefix + chunk] * batch, 16, seed=seed + 1000, pool_factor=1.0)
-    return PrefillWorkload("chunked_prefill_bf16", lay, np.full(batch, chunk, np.int32), 32, 8, 128, "bf16",
-                           1.0, seed=seed)
+def chunked_prefill(batch: int = 16, prefix: int = 1024, chunk: int = 512, seed: int = 5,
+                    block_size: int = 16) -> PrefillWorkload:
+    lay = build_paged_layout([prefix + chunk] * batch, block_size, seed=seed + 1000, pool_factor=1.0)
+    name = "chunked_prefill_bf16" + ("" if block_size == 16 else "_bs%d" % block_size)
+    return PrefillWorkload(name, lay, np.full(batch, chunk, np.int32), 32, 8, 128, "bf16", 1.0, seed=seed)
 
 
 # ----------------------------------------------------------------------------- values

@@ -154,3 +154,19 @@ def test_layout_is_a_permutation_and_deterministic():
     assert len(used) == 26 and len(set(used.tolist())) == 26
     lay2 = synth.build_paged_layout([17, 64, 100, 203], 16, seed=1, num_blocks=64)
     np.testing.assert_array_equal(lay.block_tables, lay2.block_tables)
+
+
+def test_block_size_sweep_waste_accounting():
+    """The sweep's fragmentation figure: unused slots of each sequence's last block."""
+    import bench
+    lay = synth.build_paged_layout([1, 16, 17, 0], 16, seed=3)
+    assert bench.slot_waste(lay) == (15 + 0 + 15, 16 + 16 + 32)
+    lay8 = synth.build_paged_layout([1, 16, 17, 0], 8, seed=3)
+    assert bench.slot_waste(lay8) == (7 + 0 + 7, 8 + 16 + 24)
+    # the sweep's decode workload keeps its lengths at every block size
+    from synth import workloads as W
+    base = W.llama8b_decode().layout.seq_lens
+    for bs in (8, 32, 128):
+        w = W.llama8b_decode(block_size=bs)
+        assert np.array_equal(w.layout.seq_lens, base) and w.block_size == bs
+        assert w.name.endswith("_bs%d" % bs)
