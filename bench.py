@@ -79,7 +79,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
                     choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
-                             "chunked_prefill", "block_size_sweep", "copy_calibration"])
+                             "chunked_prefill", "block_size_sweep", "swap", "copy_calibration"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
@@ -525,6 +525,88 @@ def bench_block_sizes(args, torch, pa, W):
     }
 
 
+def bench_swap(args, torch, pa, W):
+    """Swap one 4K-token sequence (Llama-3.1-8B shape, 32 layers) out to pinned host memory and back
+    in, with kv_swap_out / kv_swap_in (one gather kernel + one DMA copy per layer), against one
+    DMA copy per block (the per-copy cost model of the pages)."""
+    import synth
+    dev = "cuda"
+    layers = args.layers or 32
+    Hkv, D, bs, tokens = 8, 128, 16, 4096
+    nblk = tokens // bs
+    NB = 4 * nblk
+    shape = (NB, Hkv, bs, D)
+    K = [W.device_values(shape, 0.5, 7000 + 2 * l, "bf16") for l in range(layers)]
+    V = [W.device_values(shape, 0.5, 7001 + 2 * l, "bf16") for l in range(layers)]
+    perm = synth.shuffled_block_ids(NB, 77)
+    ids_out = torch.from_numpy(np.asarray(perm[:nblk], np.int64)).to(dev)
+    ids_in = torch.from_numpy(np.asarray(perm[nblk:2 * nblk], np.int64)).to(dev)
+    blk = Hkv * bs * D * 2                       # bytes of one block of K (or V), one layer
+    per_layer = nblk * 2 * blk
+    host = torch.empty(layers * per_layer, dtype=torch.uint8, pin_memory=True)
+    staging = torch.empty(per_layer, dtype=torch.uint8, device=dev)
+
+    def swap(out):
+        for l in range(layers):
+            h = host[l * per_layer:(l + 1) * per_layer]
+            if out:
+                pa.kv_swap_out(K[l], V[l], ids_out, h, staging)
+            else:
+                pa.kv_swap_in(K[l], V[l], ids_in, h, staging)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, (time.perf_counter() - w0) * 1e3 / reps
+
+    reps = max(1, min(args.steps, 10))
+    ms_out, wall_out = timed(lambda: swap(True), reps)
+    ms_in, wall_in = timed(lambda: swap(False), reps)
+    # the blocks that went out came back, into other physical blocks, bit for bit
+    ok = all(torch.equal(K[l][ids_in], K[l][ids_out]) and torch.equal(V[l][ids_in], V[l][ids_out])
+             for l in range(layers))
+    if not ok:
+        raise SystemExit("bench.py: swapped-in blocks differ from the swapped-out ones")
+    # one DMA copy per block per layer and per K / V (layers x 2 x blocks copies)
+    hv = host.view(layers, nblk, 2, blk)
+    ids_h = perm[:nblk]
+
+    def per_block():
+        for l in range(layers):
+            kb, vb = K[l].view(torch.uint8).view(NB, blk), V[l].view(torch.uint8).view(NB, blk)
+            for i, b in enumerate(ids_h):
+                hv[l, i, 0].copy_(kb[b], non_blocking=True)
+                hv[l, i, 1].copy_(vb[b], non_blocking=True)
+    ms_pb, wall_pb = timed(per_block, 1)
+    total = layers * per_layer
+    copies = layers * 2 * nblk
+    link = total / (ms_out * 1e-3)
+    model = synth.swap_time_model(tokens, bs, layers, Hkv, D, 2, link, 0.0)
+    return {
+        "metric": "swap of one 4K-token sequence's KV blocks between HBM and pinned host memory, ms",
+        "value": round(ms_out, 3), "unit": "ms (swap-out, 32 layers)", "n_gpus": 1, "steps": reps,
+        "warmup": 2, "ms_per_step": round(ms_out, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap_llama8b_4k", "tokens": tokens, "block_size": bs, "num_kv_heads": Hkv,
+                   "head_dim": D, "layers": layers, "bytes_each_way": total, "staging_bytes": per_layer},
+        "swap_out_ms": round(ms_out, 3), "swap_in_ms": round(ms_in, 3),
+        "swap_out_GBs": round(total / (ms_out * 1e-3) / 1e9, 2),
+        "swap_in_GBs": round(total / (ms_in * 1e-3) / 1e9, 2),
+        "host_wall_ms_out_in": [round(wall_out, 3), round(wall_in, 3)],
+        "per_block_copies": {"copies": copies, "ms": round(ms_pb, 3), "host_wall_ms": round(wall_pb, 3),
+                             "overhead_us_per_copy": round((ms_pb - model[2] * 1e3) * 1e3 / copies, 3)},
+        "pages_estimate_ms": 16.0, "round_trip_bit_exact": ok, "cpu_baseline": None,
+    }
+
+
 def bench_copy(args, torch):
     """A plain device copy of known size: the reference for scaling the HBM byte counters."""
     n = 1 << 30
@@ -578,6 +660,8 @@ def main():
         res = bench_shared_prefix(args, torch, pa, W, w, args.layers or 32)
     elif args.workload == "block_size_sweep":
         res = bench_block_sizes(args, torch, pa, W)
+    elif args.workload == "swap":
+        res = bench_swap(args, torch, pa, W)
     elif args.workload == "copy_calibration":
         res = bench_copy(args, torch)
     else:

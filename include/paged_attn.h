@@ -3,8 +3,9 @@
  *
  * Attention for decode and chunked-prefill queries over a KV cache kept in
  * fixed-size physical blocks that each sequence reaches through its own
- * block table, plus the two fused memory kernels that go with it: writing
- * new K/V rows into their slots and copying whole blocks for copy-on-write.
+ * block table, plus the memory kernels that go with it: writing new K/V
+ * rows into their slots, copying whole blocks for copy-on-write, and
+ * swapping blocks between HBM and host memory.
  *
  * Sources (web pages on KV-cache management; sections named as on the page):
  *   [L7]  Lecture 7 "KV Cache Management: PagedAttention and Mooncake"
@@ -46,14 +47,15 @@
  *     block-table entry is not dereferenced (its tokens contribute nothing),
  *     so bad ids never fault the GPU, but the result for that sequence is then
  *     unspecified.
+ *   - The swap calls also take one HOST pointer (stated where it appears).
  *   - Supported shapes.  Attention calls: head_dim in {64, 128}, any
  *     block_size >= 1, num_heads % num_kv_heads == 0 (the MFMA kernels serve
  *     bf16 KV with head_dim 128, block_size in {8, 16, 32, 64, 128} and a GQA
  *     group of at most 16 (prefill: a divisor of 16), walking each sequence
  *     in 16-token tiles; other supported shapes run on plain vector kernels),
  *     one physical block of num_kv_heads * block_size * head_dim elements
- *     below 2^31 and a whole cache (num_blocks such blocks) below 2^41.  kv_cache_write
- *     and block_copy: any block_size >= 1 and any head_dim whose row is a
+ *     below 2^31 and a whole cache (num_blocks such blocks) below 2^41.
+ *     kv_cache_write, block_copy and the swap calls: any block_size >= 1 and any head_dim whose row is a
  *     multiple of 16 bytes.  Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PAGED_ATTN_H
@@ -210,6 +212,49 @@ PA_EXPORT int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void 
 PA_EXPORT int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_pairs,
                int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                int32_t dtype, void *stream);
+
+/*
+ * kv_swap_out -- copy whole physical blocks of one layer from the K and V
+ * caches to host memory, for preemption by swapping ([L7] §6.2: a preempted
+ * sequence group's blocks are copied to CPU memory and back, at the cost of
+ * PCIe bandwidth plus a fixed cost per copy; [M2] §8.1: a 4K-token sequence
+ * is swapped as one unit and the swap should run ahead, asynchronously).
+ *
+ *   block_ids  [num_ids] int64, DEVICE: the physical blocks to copy out, in
+ *              the order they are packed.  An id outside [0, num_blocks)
+ *              yields a zero-filled piece.
+ *   host_dst   HOST memory of num_ids * 2 * block_bytes bytes, where
+ *              block_bytes = num_kv_heads * block_size * head_dim * elem:
+ *              piece i holds K[block_ids[i]] then V[block_ids[i]].  Pinned
+ *              memory (hipHostMalloc) keeps the call asynchronous; pageable
+ *              memory works but the copies then block the host.
+ *   staging    DEVICE scratch of staging_bytes >= 2 * block_bytes (else
+ *              PA_ERR_WORKSPACE).  The listed blocks are packed into it with
+ *              one kernel per chunk of floor(staging_bytes / (2 * block_bytes))
+ *              ids (at most 65535), and each chunk goes to the host with one
+ *              DMA copy, so the per-copy cost is paid per chunk, not per
+ *              block.  Contents on entry are ignored; two calls that may run
+ *              at the same time need separate staging buffers.
+ * Bit-exact.  num_ids == 0 is a no-op.  Host memory and the caches may be
+ * reused once the stream has passed the call.
+ */
+PA_EXPORT int kv_swap_out(const void *k_cache, const void *v_cache, const int64_t *block_ids,
+                          int32_t num_ids, void *host_dst, void *staging, size_t staging_bytes,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                          int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * kv_swap_in -- the reverse of kv_swap_out: piece i of host_src (K then V,
+ * as kv_swap_out packs them) is written to physical block block_ids[i] of
+ * the K and V caches ([L7] §6.2: swapped-in blocks may land in any free
+ * physical blocks; the block table is updated by the caller).  An id outside
+ * [0, num_blocks) is skipped.  No id may appear twice.  Same staging rules.
+ * Bit-exact.  num_ids == 0 is a no-op.
+ */
+PA_EXPORT int kv_swap_in(void *k_cache, void *v_cache, const int64_t *block_ids, int32_t num_ids,
+                         const void *host_src, void *staging, size_t staging_bytes,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim, int32_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

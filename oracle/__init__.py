@@ -91,7 +91,10 @@ def _bind(lib):
     lib.oracle_blockwise_decode_row.argtypes = ([_dbl_p, _vp, ctypes.c_int64, _vp, _vp, ctypes.c_int,
                                                  _i32_p] + [ctypes.c_int] * 6
                                                 + [ctypes.c_double, ctypes.c_int, _i32_p])
-    for name in ("oracle_kv_cache_write", "oracle_block_copy", "oracle_paged_decode",
+    lib.oracle_swap_out.argtypes = [_vp, _vp, _i64_p, ctypes.c_int, _vp] + [ctypes.c_int] * 5
+    lib.oracle_swap_in.argtypes = [_vp, _vp, _i64_p, ctypes.c_int, _vp] + [ctypes.c_int] * 5
+    for name in ("oracle_kv_cache_write", "oracle_block_copy", "oracle_swap_out", "oracle_swap_in",
+                 "oracle_paged_decode",
                  "oracle_paged_prefill", "oracle_contiguous_attention",
                  "oracle_blockwise_decode_row"):
         getattr(lib, name).restype = ctypes.c_int
@@ -152,6 +155,33 @@ def block_copy(k_cache, v_cache, pairs):
                                pairs.ctypes.data_as(_i64_p), pairs.shape[0], NB, Hkv, bs, D,
                                _dtype_code(k_cache))
     _check(rc, "oracle_block_copy")
+
+
+def swap_out(k_cache, v_cache, ids) -> np.ndarray:
+    """Host image of blocks ``ids``: uint8 [n, 2, block_bytes] (K then V per block; zeros for a bad id)."""
+    lib = _load()
+    NB, Hkv, bs, D = k_cache.shape
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    ids = _c(np.asarray(ids).reshape(-1), np.int64)
+    blk_bytes = Hkv * bs * D * k_cache.itemsize
+    host = np.empty((ids.shape[0], 2, blk_bytes), np.uint8)
+    rc = lib.oracle_swap_out(k_cache.ctypes.data, v_cache.ctypes.data, ids.ctypes.data_as(_i64_p), ids.shape[0],
+                             host.ctypes.data, NB, Hkv, bs, D, _dtype_code(k_cache))
+    _check(rc, "oracle_swap_out")
+    return host
+
+
+def swap_in(k_cache, v_cache, ids, host):
+    """In-place: piece i of the host image goes to block ids[i] of both caches (a bad id is skipped)."""
+    lib = _load()
+    NB, Hkv, bs, D = k_cache.shape
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    ids = _c(np.asarray(ids).reshape(-1), np.int64)
+    host = _c(host, np.uint8)
+    assert host.size >= ids.shape[0] * 2 * Hkv * bs * D * k_cache.itemsize
+    rc = lib.oracle_swap_in(k_cache.ctypes.data, v_cache.ctypes.data, ids.ctypes.data_as(_i64_p), ids.shape[0],
+                            host.ctypes.data, NB, Hkv, bs, D, _dtype_code(k_cache))
+    _check(rc, "oracle_swap_in")
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale):

@@ -120,6 +120,43 @@ int oracle_block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int N,
 }
 
 /*
+ * Swapping (Lecture 7 §6.2: a preempted sequence group's blocks are copied to
+ * CPU memory and later copied back, into whatever physical blocks are free;
+ * Month 2 §8.1: the blocks of a sequence move together).  The host image is
+ * a sequence of pieces, piece i = K block ids[i] followed by V block ids[i]
+ * (blk_bytes each).  Out: an id outside [0, num_blocks) gives a zero piece.
+ * In: such an id is skipped.  Byte copies, in order.
+ */
+int oracle_swap_out(const void *k_cache, const void *v_cache, const int64_t *ids, int n, void *host,
+                    int num_blocks, int Hkv, int bs, int D, int dtype) {
+  if (!k_cache || !v_cache || ((!ids || !host) && n > 0)) return ORC_ERR_ARG;
+  size_t blk_bytes = (size_t)Hkv * bs * D * elem_bytes(dtype);
+  for (int i = 0; i < n; ++i) {
+    char *piece = (char *)host + (size_t)i * 2 * blk_bytes;
+    if (ids[i] < 0 || ids[i] >= num_blocks) {
+      memset(piece, 0, 2 * blk_bytes);
+      continue;
+    }
+    memcpy(piece, (const char *)k_cache + ids[i] * blk_bytes, blk_bytes);
+    memcpy(piece + blk_bytes, (const char *)v_cache + ids[i] * blk_bytes, blk_bytes);
+  }
+  return ORC_OK;
+}
+
+int oracle_swap_in(void *k_cache, void *v_cache, const int64_t *ids, int n, const void *host,
+                   int num_blocks, int Hkv, int bs, int D, int dtype) {
+  if (!k_cache || !v_cache || ((!ids || !host) && n > 0)) return ORC_ERR_ARG;
+  size_t blk_bytes = (size_t)Hkv * bs * D * elem_bytes(dtype);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= num_blocks) continue;
+    const char *piece = (const char *)host + (size_t)i * 2 * blk_bytes;
+    memcpy((char *)k_cache + ids[i] * blk_bytes, piece, blk_bytes);
+    memcpy((char *)v_cache + ids[i] * blk_bytes, piece + blk_bytes, blk_bytes);
+  }
+  return ORC_OK;
+}
+
+/*
  * One attention row by the definition (Month 2 §2.1): the query q (length D)
  * against the first n_keys tokens of sequence b, reached through the block
  * table (Month 2 §5.4: logical block j lives in physical block

@@ -18,7 +18,8 @@ import os
 __all__ = [
     "PA_F32", "PA_BF16", "PagedAttnError", "lib", "library_path", "pa_status_string",
     "pa_abi_version", "kv_cache_write", "paged_attn_decode_workspace_size", "paged_attn_decode",
-    "paged_attn_prefill_chunk", "block_copy", "EXPORTED_SYMBOLS",
+    "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in", "swap_host_bytes",
+    "EXPORTED_SYMBOLS",
 ]
 
 PA_F32 = 0
@@ -28,7 +29,7 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpage
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
-                    "paged_attn_prefill_chunk", "block_copy")
+                    "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in")
 
 
 class PagedAttnError(RuntimeError):
@@ -59,6 +60,10 @@ def _load():
     L.paged_attn_prefill_chunk.restype = ctypes.c_int
     L.block_copy.argtypes = [vp, vp, vp] + [i32] * 6 + [vp]
     L.block_copy.restype = ctypes.c_int
+    L.kv_swap_out.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
+    L.kv_swap_out.restype = ctypes.c_int
+    L.kv_swap_in.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
+    L.kv_swap_in.restype = ctypes.c_int
     return L
 
 
@@ -212,3 +217,40 @@ def block_copy(k_cache, v_cache, pairs, stream=None):
     st = _L().block_copy(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs", torch.int64),
                         pairs.shape[0], NB, Hkv, bs, D, _dtype_code(k_cache), _stream(stream))
     _check("block_copy", st)
+
+
+def swap_host_bytes(k_cache, num_ids: int) -> int:
+    """Bytes of host memory kv_swap_out fills for num_ids blocks of these caches (K then V per block)."""
+    NB, Hkv, bs, D = k_cache.shape
+    return int(num_ids) * 2 * Hkv * bs * D * k_cache.element_size()
+
+
+def _swap(fn: str, k_cache, v_cache, block_ids, host, staging, stream):
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("caches must match")
+    if block_ids.dim() != 1:
+        raise ValueError("block_ids must be [num_ids]")
+    n = block_ids.shape[0]
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("the host buffer must be a contiguous CPU tensor (pinned for an asynchronous call)")
+    if host.numel() * host.element_size() < swap_host_bytes(k_cache, n):
+        raise ValueError("host buffer too small: %d < %d bytes" % (host.numel() * host.element_size(),
+                                                                   swap_host_bytes(k_cache, n)))
+    st = getattr(_L(), fn)(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(block_ids, "block_ids", torch.int64), n, ctypes.c_void_p(host.data_ptr()),
+                           _dev(staging, "staging"), staging.numel() * staging.element_size(), NB, Hkv, bs, D,
+                           _dtype_code(k_cache), _stream(stream))
+    _check(fn, st)
+
+
+def kv_swap_out(k_cache, v_cache, block_ids, host_dst, staging, stream=None):
+    """Copy blocks block_ids (GPU int64) of both caches into host_dst (CPU, pinned), K then V per block,
+    through the GPU staging buffer (uint8, at least 2 blocks' bytes)."""
+    _swap("kv_swap_out", k_cache, v_cache, block_ids, host_dst, staging, stream)
+
+
+def kv_swap_in(k_cache, v_cache, block_ids, host_src, staging, stream=None):
+    """Write the pieces of host_src (as kv_swap_out packs them) to blocks block_ids of both caches."""
+    _swap("kv_swap_in", k_cache, v_cache, block_ids, host_src, staging, stream)

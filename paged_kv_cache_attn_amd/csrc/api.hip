@@ -281,4 +281,60 @@ int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_p
                                              static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Shared by both swap directions: checks, then per chunk of staging-sized
+// id runs, the gather kernel + a device-to-host copy, or a host-to-device
+// copy + the scatter kernel, all on `stream`.
+int swap_blocks(bool out, void *k_cache, void *v_cache, const int64_t *block_ids, int32_t num_ids,
+                void *host, void *staging, size_t staging_bytes, int32_t num_blocks, int32_t num_kv_heads,
+                int32_t block_size, int32_t head_dim, int32_t dtype, void *stream) {
+  if (num_ids < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes / 16 > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  if (num_ids == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_ids || !host) return PA_ERR_NULL;
+  const int64_t per_id = 2 * block_bytes;
+  if (!staging || staging_bytes < (size_t)per_id) return PA_ERR_WORKSPACE;
+  const int64_t chunk = std::min<int64_t>({(int64_t)(staging_bytes / per_id), num_ids, 65535});
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t i0 = 0; i0 < num_ids; i0 += chunk) {
+    const int n = (int)std::min<int64_t>(chunk, num_ids - i0);
+    uint8_t *h = static_cast<uint8_t *>(host) + i0 * per_id;
+    hipError_t e;
+    if (out) {
+      e = pa::launch_swap_blocks(true, k_cache, v_cache, block_ids + i0, n, staging, num_blocks,
+                                 (int)(block_bytes / 16), s);
+      if (e == hipSuccess) e = hipMemcpyAsync(h, staging, n * per_id, hipMemcpyDeviceToHost, s);
+    } else {
+      e = hipMemcpyAsync(staging, h, n * per_id, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess)
+        e = pa::launch_swap_blocks(false, k_cache, v_cache, block_ids + i0, n, staging, num_blocks,
+                                   (int)(block_bytes / 16), s);
+    }
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+int kv_swap_out(const void *k_cache, const void *v_cache, const int64_t *block_ids, int32_t num_ids,
+                void *host_dst, void *staging, size_t staging_bytes, int32_t num_blocks, int32_t num_kv_heads,
+                int32_t block_size, int32_t head_dim, int32_t dtype, void *stream) {
+  return swap_blocks(true, const_cast<void *>(k_cache), const_cast<void *>(v_cache), block_ids, num_ids,
+                     host_dst, staging, staging_bytes, num_blocks, num_kv_heads, block_size, head_dim, dtype,
+                     stream);
+}
+
+int kv_swap_in(void *k_cache, void *v_cache, const int64_t *block_ids, int32_t num_ids, const void *host_src,
+               void *staging, size_t staging_bytes, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+               int32_t head_dim, int32_t dtype, void *stream) {
+  return swap_blocks(false, k_cache, v_cache, block_ids, num_ids, const_cast<void *>(host_src), staging,
+                     staging_bytes, num_blocks, num_kv_heads, block_size, head_dim, dtype, stream);
+}
+
 }  // extern "C"

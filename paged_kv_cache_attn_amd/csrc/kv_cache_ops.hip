@@ -4,6 +4,11 @@
 //     §4.1 and of Lecture 16 "LLM Serving (1)" §3.3);
 //   block_copy: batched whole-block copies for copy-on-write (Lecture 7 §4.3,
 //     third fused kernel, and §5.1).
+//   swap gather / scatter: the listed blocks of one layer packed into (or
+//     unpacked from) a contiguous staging buffer, so a swap between HBM and
+//     host memory is one DMA copy per chunk instead of one per block
+//     (Lecture 7 §6.2: swapping costs PCIe bandwidth plus a fixed cost per
+//     copy; Month 2 §8.1: a 4K-token sequence's blocks are swapped together).
 // Both are pure HBM streams: each thread moves 16-byte chunks with
 // global_load_dwordx4 / global_store_dwordx4, consecutive threads take
 // consecutive chunks of a row so every wave touches whole 256-byte rows.
@@ -71,6 +76,52 @@ __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t *__restrict__ k
     st16(d + (int64_t)(i + 768) * 16, e);
   }
   for (; i < block_chunks; i += 256) st16(d + (int64_t)i * 16, ld16(s + (int64_t)i * 16));
+}
+
+// Swap staging.  Gather: staging piece (i, kv) = block ids[i] of the K
+// (kv = 0) or V (kv = 1) cache; an id outside [0, num_blocks) gives a zero
+// piece.  Scatter: the reverse, skipping such ids.  One workgroup per piece,
+// grid (n, 2); `ids` points at the first id of this chunk.
+template <bool kGather>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(uint8_t *__restrict__ k_cache,
+                                                          uint8_t *__restrict__ v_cache,
+                                                          const int64_t *__restrict__ ids,
+                                                          uint8_t *__restrict__ staging,
+                                                          int64_t num_blocks, int block_chunks) {
+  const int64_t id = ids[blockIdx.x];
+  const bool ok = id >= 0 && id < num_blocks;
+  if (!kGather && !ok) return;
+  const int64_t bytes = (int64_t)block_chunks * 16;
+  uint8_t *blk = (blockIdx.y == 0 ? k_cache : v_cache) + (ok ? id : 0) * bytes;
+  uint8_t *stg = staging + ((int64_t)blockIdx.x * 2 + blockIdx.y) * bytes;
+  const uint8_t *s = kGather ? blk : stg;
+  uint8_t *d = kGather ? stg : blk;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  int i = threadIdx.x;
+  for (; i + 3 * 256 < block_chunks; i += 4 * 256) {
+    u32x4 a = ld16(s + (int64_t)i * 16), b = ld16(s + (int64_t)(i + 256) * 16);
+    u32x4 c = ld16(s + (int64_t)(i + 512) * 16), e = ld16(s + (int64_t)(i + 768) * 16);
+    st16(d + (int64_t)i * 16, ok ? a : zero);
+    st16(d + (int64_t)(i + 256) * 16, ok ? b : zero);
+    st16(d + (int64_t)(i + 512) * 16, ok ? c : zero);
+    st16(d + (int64_t)(i + 768) * 16, ok ? e : zero);
+  }
+  for (; i < block_chunks; i += 256) {
+    const u32x4 a = ld16(s + (int64_t)i * 16);
+    st16(d + (int64_t)i * 16, ok ? a : zero);
+  }
+}
+
+hipError_t launch_swap_blocks(bool gather, void *k_cache, void *v_cache, const int64_t *ids, int n,
+                              void *staging, int num_blocks, int block_chunks, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (gather)
+    hipLaunchKernelGGL(swap_blocks_kernel<true>, dim3((unsigned)n, 2), dim3(256), 0, stream, (uint8_t *)k_cache,
+                       (uint8_t *)v_cache, ids, (uint8_t *)staging, (int64_t)num_blocks, block_chunks);
+  else
+    hipLaunchKernelGGL(swap_blocks_kernel<false>, dim3((unsigned)n, 2), dim3(256), 0, stream, (uint8_t *)k_cache,
+                       (uint8_t *)v_cache, ids, (uint8_t *)staging, (int64_t)num_blocks, block_chunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,

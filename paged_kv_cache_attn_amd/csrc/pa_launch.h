@@ -33,6 +33,10 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cac
                                  int num_kv_heads, int block_size, int head_dim, int elem_bytes,
                                  hipStream_t stream);
 
+// gather (true): ids[0..n) of the K and V caches -> staging [n][2][block];
+// scatter (false): the reverse.  block_chunks = 16-byte chunks per block.
+hipError_t launch_swap_blocks(bool gather, void *k_cache, void *v_cache, const int64_t *ids, int n,
+                              void *staging, int num_blocks, int block_chunks, hipStream_t stream);
 hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int num_pairs,
                              int num_blocks, int num_kv_heads, int block_size, int head_dim,
                              int elem_bytes, hipStream_t stream);

@@ -103,6 +103,17 @@ def block_bytes(block_size: int, num_kv_heads: int, head_dim: int, dtype_bytes: 
     return block_size * num_kv_heads * head_dim * dtype_bytes * 2
 
 
+def swap_time_model(tokens: int, block_size: int, layers: int, kv_heads: int, head_dim: int, dtype_bytes: int,
+                    bytes_per_s: float, per_copy_s: float):
+    """The per-copy swap cost model (Lecture 7 "KV Cache Management" §6.2): every layer's K and V
+    blocks are separate copies, each costing a fixed overhead plus its bytes over the link.
+    Returns (copies, bytes per copy, seconds for one direction)."""
+    blocks = -(-tokens // block_size)
+    copies = layers * 2 * blocks
+    per_copy = block_size * kv_heads * head_dim * dtype_bytes
+    return copies, per_copy, copies * (per_copy_s + per_copy / bytes_per_s)
+
+
 @dataclass
 class PagedLayout:
     """Where every sequence's tokens live: lengths, block tables and the pool size."""

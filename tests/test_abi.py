@@ -156,6 +156,27 @@ def test_block_copy_validation(pa):
     assert f(N, N, N, 0, 64, 8, 16, 128, 1, N) == PA_OK
 
 
+def test_swap_validation(pa):
+    # k, v, ids, n, host, staging, staging_bytes, NB, Hkv, bs, D, dtype, stream
+    blk = 8 * 16 * 128 * 2
+    for f in (pa.lib.kv_swap_out, pa.lib.kv_swap_in):
+        args = [P, P, P, 3, P, P, 2 * blk, 64, 8, 16, 128, 1, N]
+        a = list(args); a[3] = -1
+        assert f(*a) == PA_ERR_SHAPE
+        a = list(args); a[11] = 9
+        assert f(*a) == PA_ERR_UNSUPPORTED
+        a = list(args); a[10] = 4          # 4 bf16 = 8 bytes: not a multiple of 16
+        assert f(*a) == PA_ERR_UNSUPPORTED
+        for i in (0, 1, 2, 4):
+            a = list(args); a[i] = N
+            assert f(*a) == PA_ERR_NULL
+        a = list(args); a[5] = N
+        assert f(*a) == PA_ERR_WORKSPACE
+        a = list(args); a[6] = 2 * blk - 1
+        assert f(*a) == PA_ERR_WORKSPACE
+        assert f(N, N, N, 0, N, N, 0, 64, 8, 16, 128, 1, N) == PA_OK
+
+
 def test_binding_refuses_cpu_tensors(pa):
     import torch
     k = torch.zeros(4, 2, 16, 64)

@@ -86,6 +86,33 @@ def test_block_copy_bit_exact(pa, dtype):
     assert np.array_equal(to_host(vg), vc)
 
 
+@pytest.mark.parametrize("dtype,bs,staging_blocks", [("bf16", 16, 3), ("f32", 8, 1000), ("bf16", 128, 1)])
+def test_swap_out_in_bit_exact(pa, dtype, bs, staging_blocks):
+    """Swap-out image and swap-in result against the oracle, bit for bit; the staging
+    buffer forces several chunks; bad ids give zero pieces out and are skipped in."""
+    torch = torch_mod()
+    NB, Hkv, D = 40, 4, 128
+    k = W.host_values((NB, Hkv, bs, D), 1.0, 31, dtype)
+    v = W.host_values((NB, Hkv, bs, D), 1.0, 32, dtype)
+    ids = np.array([17, 3, 39, 0, NB + 2, 25, 8, -1, 30, 11], np.int64)
+    new = np.array([5, 6, 7, 9, 12, 13, 14, 15, 1, -4], np.int64)
+    blk = Hkv * bs * D * k.itemsize
+    kg, vg = to_gpu(k), to_gpu(v)
+    staging = torch.empty(staging_blocks * 2 * blk, dtype=torch.uint8, device="cuda")
+    host = torch.empty(len(ids) * 2 * blk, dtype=torch.uint8, pin_memory=True)
+    host.fill_(0xCD)
+    pa.kv_swap_out(kg, vg, to_gpu(ids), host, staging)
+    torch.cuda.synchronize()
+    img = oracle.swap_out(k, v, ids)
+    assert np.array_equal(host.numpy().reshape(img.shape), img)
+    # swap the image back into other blocks of the caches
+    pa.kv_swap_in(kg, vg, to_gpu(new), host, staging)
+    torch.cuda.synchronize()
+    k2, v2 = k.copy(), v.copy()
+    oracle.swap_in(k2, v2, new, img)
+    assert np.array_equal(to_host(kg), k2) and np.array_equal(to_host(vg), v2)
+
+
 def test_empty_calls_are_noops(pa):
     torch = torch_mod()
     kc = torch.zeros(4, 2, 16, 64, device="cuda")

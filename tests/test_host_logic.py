@@ -170,3 +170,42 @@ def test_block_size_sweep_waste_accounting():
         w = W.llama8b_decode(block_size=bs)
         assert np.array_equal(w.layout.seq_lens, base) and w.block_size == bs
         assert w.name.endswith("_bs%d" % bs)
+
+
+def test_swap_cost_model_exercise6():
+    """The pages' worked swap-vs-recompute example, through the model the swap benchmark reports."""
+    g = load("swap_exercise6.json")
+    m = g["model"]
+    args = (m["layers"], m["kv_heads"], m["head_dim"], m["dtype_bytes"], g["pcie_bytes_per_s"], g["per_copy_s"])
+    copies, per_copy, secs = synth.swap_time_model(g["tokens"], g["block_size"], *args)
+    assert copies == g["copies"] and per_copy == g["bytes_per_copy"]
+    assert round((g["per_copy_s"] + per_copy / g["pcie_bytes_per_s"]) * 1e6, 1) == g["us_per_copy"]
+    assert round(secs * 1e3, 1) == g["swap_out_ms"]
+    assert round(2 * secs * 1e3, 1) == g["swap_out_and_in_ms"]
+    assert (2 * secs * 1e3 < g["recompute_ms"]) == g["swap_faster_than_recompute"]
+    lo, hi = g["crossover_between_block_sizes"]
+    assert 2 * synth.swap_time_model(g["tokens"], lo, *args)[2] * 1e3 > g["recompute_ms"]
+    assert 2 * synth.swap_time_model(g["tokens"], hi, *args)[2] * 1e3 < g["recompute_ms"]
+
+
+def test_oracle_swap_image_and_round_trip():
+    """Swap-out packs K then V of each listed block; swap-in to other ids equals block copies."""
+    NB, Hkv, bs, D = 9, 2, 4, 8
+    for dt in ("f32", "bf16"):
+        kc = synth.normal_f32((NB, Hkv, bs, D), 1.0, 11)
+        vc = synth.normal_f32((NB, Hkv, bs, D), 1.0, 12)
+        if dt == "bf16":
+            kc, vc = synth.round_to_bf16_bits(kc), synth.round_to_bf16_bits(vc)
+        ids = [4, 0, 7, 99, -2]
+        img = oracle.swap_out(kc, vc, ids)
+        nb = Hkv * bs * D * kc.itemsize
+        assert img.shape == (5, 2, nb)
+        for i, b in enumerate(ids[:3]):
+            assert img[i, 0].tobytes() == kc[b].tobytes() and img[i, 1].tobytes() == vc[b].tobytes()
+        assert not img[3:].any()                        # bad ids give zero pieces
+        # swap in to other blocks == copying those blocks there
+        k1, v1, k2, v2 = kc.copy(), vc.copy(), kc.copy(), vc.copy()
+        new = [1, 5, 8]
+        oracle.swap_in(k1, v1, new + [-1, NB], img)      # pieces 3 and 4: bad target ids, skipped
+        oracle.block_copy(k2, v2, list(zip(ids[:3], new)))
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
