@@ -79,7 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
                     choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
-                             "chunked_prefill", "block_size_sweep", "swap", "copy_calibration"])
+                             "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
+                             "copy_calibration"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
@@ -525,6 +526,112 @@ def bench_block_sizes(args, torch, pa, W):
     }
 
 
+def bench_mixed_decode(args, torch, pa, W):
+    """32 decode steps of one batch mixing beam search (16 groups x 4 beams), parallel sampling
+    (8 groups x 4 samples) and 32 greedy rows, 32 layers: per step and layer, the step's
+    copy-on-write block copies (one block_copy), the new tokens' K/V (kv_cache_write), then
+    decode attention through that step's block tables.  The whole trace is captured in one HIP
+    graph and replayed; layer 0 of an eager pass is checked against the oracle replaying the
+    same copies and writes on the host."""
+    import oracle
+    dev = "cuda"
+    tr = W.mixed_decode_trace()
+    layers = args.layers or 32
+    B, Hq, Hkv, D, bs = tr.batch, tr.num_heads, tr.num_kv_heads, tr.head_dim, tr.block_size
+    shape = (tr.num_blocks, Hkv, bs, D)
+    K = [W.device_values(shape, tr.std, tr.seed * 1000 + 2 * l, tr.dtype) for l in range(layers)]
+    V = [W.device_values(shape, tr.std, tr.seed * 1000 + 2 * l + 1, tr.dtype) for l in range(layers)]
+    k0, v0 = host_copy(torch, K[0]), host_copy(torch, V[0])
+    q = W.device_values((B, Hq, D), tr.std, tr.seed * 1000 - 1, tr.dtype)
+    newk = W.device_values((B, Hkv, D), tr.std, tr.seed * 1000 - 2, tr.dtype)
+    newv = W.device_values((B, Hkv, D), tr.std, tr.seed * 1000 - 3, tr.dtype)
+    S = len(tr.tables)
+    bt = [torch.from_numpy(t).to(dev) for t in tr.tables]
+    sl = [torch.from_numpy(x).to(dev) for x in tr.seq_lens]
+    slots = [torch.from_numpy(x).to(dev) for x in tr.slots]
+    pairs = [torch.from_numpy(np.asarray(c, np.int64).reshape(-1, 2)).to(dev) for c in tr.copies]
+    max_len = int(max(int(x.max()) for x in tr.seq_lens))
+    out = torch.empty(B, Hq, D, device=dev, dtype=torch.float32)
+    wsb = pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, bs, max_len, 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def step(s, l):
+        if len(tr.copies[s]):
+            pa.block_copy(K[l], V[l], pairs[s])
+        pa.kv_cache_write(newk, newv, K[l], V[l], slots[s])
+        pa.paged_attn_decode(out, q, K[l], V[l], bt[s], sl[s], tr.scale, max_len, 0, ws)
+
+    # eager pass of the whole trace; layer 0's last decode against the oracle's replay
+    for s in range(S):
+        for l in range(layers):
+            step(s, l)
+            if l == 0 and s == S - 1:
+                torch.cuda.synchronize()
+                gpu_last = out.double().cpu().numpy()
+    hk, hv = host_copy(torch, newk), host_copy(torch, newv)
+    for s in range(S):
+        if len(tr.copies[s]):
+            oracle.block_copy(k0, v0, tr.copies[s])
+        oracle.kv_cache_write(hk, hv, k0, v0, tr.slots[s])
+    sel = np.concatenate([np.arange(0, 64, 5), np.arange(64, 96, 3), np.arange(96, B, 4)])
+    ref = oracle.paged_decode(host_copy(torch, q)[sel], k0, v0, tr.tables[-1][sel], tr.seq_lens[-1][sel], tr.scale)
+    err = float(np.max(np.abs(gpu_last[sel] - ref)))
+    if err > 2e-3:
+        raise SystemExit("bench.py: mixed-mode decode differs from the oracle (%.3e)" % err)
+
+    def trace():
+        for s in range(S):
+            for l in range(layers):
+                step(s, l)
+    trace()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        trace()
+    reps = max(1, min(args.steps, 5))
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * S)
+    # the copies alone, same graph treatment
+    gc = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gc):
+        for s in range(S):
+            if len(tr.copies[s]):
+                for l in range(layers):
+                    pa.block_copy(K[l], V[l], pairs[s])
+    gc.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        gc.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_copy = e0.elapsed_time(e1) / (reps * S)
+    n_copies = sum(len(c) for c in tr.copies)
+    kv_row = Hkv * D * 2 * 2                         # K + V bytes of one token, one layer
+    logical = sum(int(x.astype(np.int64).sum()) for x in tr.seq_lens) / S * kv_row
+    step_bytes = layers * (logical + B * Hq * D * (2 + 4) + B * kv_row * 2 + n_copies / S * 2 * 2 * Hkv * bs * D * 2)
+    return {
+        "metric": METRIC, "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": reps * S, "warmup": 2, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": tr.dtype, "data": "synthetic",
+        "config": {"workload": tr.name, "batch": B, "beam_groups": 16, "beam_width": 4, "sample_groups": 8,
+                   "samples": 4, "greedy_rows": 32, "decode_steps": S, "layers": layers, "block_size": bs,
+                   "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "num_blocks_per_layer": tr.num_blocks},
+        "cow": {"copies": n_copies, "copied_tokens": n_copies * bs,
+                "whole_copy_tokens": tr.whole_copy_tokens,
+                "copy_us_per_step_all_layers": round(ms_copy * 1e3, 3)},
+        "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
+        "parity_max_abs_err_sampled_rows": err, "cpu_baseline": None, "timing": "hip-graph",
+    }
+
+
 def bench_swap(args, torch, pa, W):
     """Swap one 4K-token sequence (Llama-3.1-8B shape, 32 layers) out to pinned host memory and back
     in, with kv_swap_out / kv_swap_in (one gather kernel + one DMA copy per layer), against one
@@ -660,6 +767,8 @@ def main():
         res = bench_shared_prefix(args, torch, pa, W, w, args.layers or 32)
     elif args.workload == "block_size_sweep":
         res = bench_block_sizes(args, torch, pa, W)
+    elif args.workload == "mixed_decode":
+        res = bench_mixed_decode(args, torch, pa, W)
     elif args.workload == "swap":
         res = bench_swap(args, torch, pa, W)
     elif args.workload == "copy_calibration":

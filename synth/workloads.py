@@ -208,3 +208,123 @@ def device_values(shape, std: float, seed: int, dtype: str, device="cuda"):
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     x.mul_(std)
     return x if dtype == "f32" else x.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- mixed decoding modes
+@dataclass
+class MixedDecodeTrace:
+    """Decode steps of one batch that mixes beam search, parallel sampling and
+    greedy sequences (Lecture 7 "KV Cache Management" §5.1-§5.3: the kernels
+    only see each row's list of physical blocks, so the modes share a batch).
+
+    Row order is fixed: the beams of each beam group, then the samples of each
+    sampling group, then the greedy rows.  Per step: ``copies`` (src, dst)
+    pairs to run first, then every row's new token goes to ``slots[row]``, then
+    attention over ``seq_lens`` through ``tables`` (all padded to one width)."""
+    name: str
+    num_blocks: int
+    block_size: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    std: float
+    seed: int
+    modes: List[str]
+    tables: List[np.ndarray]            # per step, int32 [B, W]
+    seq_lens: List[np.ndarray]          # per step, int32 [B]
+    slots: List[np.ndarray]             # per step, int64 [B]
+    copies: List[List[Tuple[int, int]]]  # per step
+    whole_copy_tokens: int = 0          # tokens a copy-the-parent scheme would have copied
+
+    @property
+    def batch(self) -> int:
+        return len(self.modes)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def beam_parents(rng, k: int) -> np.ndarray:
+    """Parents of the k new beams among the k old ones, drawn independently and
+    uniformly: some old beams get several children and others none, as in a
+    beam step (Lecture 7 §5.2).  With k = 4 this averages 4 - 4(1 - (3/4)^4)
+    = 1.27 copy-on-write copies per step, close to the pages' demo (35 copies
+    over 32 steps)."""
+    return np.sort(rng.integers(0, k, size=k))
+
+
+def mixed_decode_trace(beam_groups: int = 16, beam_width: int = 4, sample_groups: int = 8, samples: int = 4,
+                       greedy: int = 32, steps: int = 32, block_size: int = 16, seed: int = 6,
+                       beam_prompt: Optional[int] = None, sample_prompt: int = 100,
+                       num_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,
+                       dtype: str = "bf16") -> MixedDecodeTrace:
+    """Build the trace with the block manager.  Prompts: the beam groups' from the
+    length model (or ``beam_prompt`` tokens each), the sampling groups' of
+    ``sample_prompt`` tokens (a partially filled last block, so the first write
+    copies it n - 1 times), greedy rows from the length model."""
+    rng = np.random.default_rng(seed)
+    bp = (lognormal_lengths(beam_groups, 390, SIGMA_8B, 16, 2048, seed=seed + 1) if beam_prompt is None
+          else np.full(beam_groups, beam_prompt, np.int32))
+    gl = lognormal_lengths(greedy, 390, SIGMA_8B, 16, 4096, seed=seed + 2)
+    bs = block_size
+    need = (sum(-(-int(L) // bs) + beam_width * (steps // bs + 2) for L in bp)
+            + sample_groups * (-(-sample_prompt // bs) + samples * (steps // bs + 2))
+            + sum(-(-int(L) // bs) + steps // bs + 2 for L in gl))
+    nb = int(math.ceil(1.25 * need)) + 8
+    mgr = BlockManager(nb, bs, free_order=shuffled_block_ids(nb, seed + 1000))
+    groups = []                                        # (mode, [seq ids])
+    for L in bp:
+        s = mgr.new_sequence()
+        mgr.append(s, int(L))
+        groups.append(("beam", [s]))
+    for _ in range(sample_groups):
+        s = mgr.new_sequence()
+        mgr.append(s, sample_prompt)
+        groups.append(("sample", mgr.fork(s, samples)))
+    for L in gl:
+        s = mgr.new_sequence()
+        mgr.append(s, int(L))
+        groups.append(("greedy", [s]))
+    mgr.take_copies()
+    modes = []
+    for mode, seqs in groups:
+        modes += [mode] * (beam_width if mode == "beam" else len(seqs))
+    whole = 0
+    tables, lens, slots, copies = [], [], [], []
+    for step in range(steps):
+        rows = []
+        for gi, (mode, seqs) in enumerate(groups):
+            if mode == "beam":
+                if step == 0:
+                    new = mgr.fork(seqs[0], beam_width)     # the prompt fans out into k beams
+                else:
+                    par = beam_parents(rng, beam_width)
+                    counts = np.bincount(par, minlength=beam_width)
+                    new = []
+                    for b, c in zip(seqs, counts):
+                        if c == 0:
+                            mgr.free_sequence(b)
+                    for b, c in zip(seqs, counts):
+                        if c > 0:
+                            new += mgr.fork(b, int(c))
+                # a copy-the-parent scheme copies every new beam's whole history
+                whole += beam_width * mgr.lengths[new[0]] if step == 0 else sum(mgr.lengths[s] for s in new)
+                groups[gi] = (mode, new)
+                seqs = new
+            rows += seqs
+        step_slots = [mgr.append(s, 1)[0] for s in rows]
+        copies.append(mgr.take_copies())
+        slots.append(np.asarray(step_slots, np.int64))
+        lens.append(np.asarray([mgr.lengths[s] for s in rows], np.int32))
+        tables.append([list(mgr.tables[s]) for s in rows])
+    width = max(len(t) for st in tables for t in st)
+    tabs = []
+    for st in tables:
+        a = np.full((len(st), width), -1, np.int32)
+        for i, t in enumerate(st):
+            a[i, :len(t)] = t
+        tabs.append(a)
+    return MixedDecodeTrace("mixed_beam_sample_greedy", nb, bs, num_heads, num_kv_heads, head_dim, dtype, 0.5,
+                            seed, modes, tabs, lens, slots, copies, whole)

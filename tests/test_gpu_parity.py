@@ -288,6 +288,37 @@ def test_decode_deterministic(pa):
     assert np.array_equal(o1, o2)
 
 
+@pytest.mark.parametrize("bs", [16, 8])
+def test_mixed_modes_trace(pa, bs):
+    """Beam search, parallel sampling and greedy rows in one batch over 24 steps: every step's
+    copy-on-write copies, new-token writes and decode match the oracle replaying the same trace."""
+    torch = torch_mod()
+    tr = W.mixed_decode_trace(beam_groups=3, beam_width=4, sample_groups=2, samples=3, greedy=3, steps=24,
+                              block_size=bs, seed=9, num_heads=16, num_kv_heads=4)
+    B, Hq, Hkv, D = tr.batch, tr.num_heads, tr.num_kv_heads, tr.head_dim
+    k = W.host_values((tr.num_blocks, Hkv, bs, D), 0.5, 61, "bf16")
+    v = W.host_values((tr.num_blocks, Hkv, bs, D), 0.5, 62, "bf16")
+    q = W.host_values((B, Hq, D), 0.5, 63, "bf16")
+    nk = W.host_values((B, Hkv, D), 0.5, 64, "bf16")
+    nv = W.host_values((B, Hkv, D), 0.5, 65, "bf16")
+    kg, vg, qg, nkg, nvg = to_gpu(k), to_gpu(v), to_gpu(q), to_gpu(nk), to_gpu(nv)
+    max_len = int(max(int(x.max()) for x in tr.seq_lens))
+    ws = torch.empty(max(pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, bs, max_len, 0), 1),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, D, device="cuda")
+    assert sum(len(c) for c in tr.copies) > 0
+    for s in range(len(tr.tables)):
+        if tr.copies[s]:
+            pa.block_copy(kg, vg, to_gpu(np.asarray(tr.copies[s], np.int64)))
+            oracle.block_copy(k, v, tr.copies[s])
+        pa.kv_cache_write(nkg, nvg, kg, vg, to_gpu(tr.slots[s]))
+        oracle.kv_cache_write(nk, nv, k, v, tr.slots[s])
+        pa.paged_attn_decode(out, qg, kg, vg, to_gpu(tr.tables[s]), to_gpu(tr.seq_lens[s]), tr.scale, max_len, 0, ws)
+        ref = oracle.paged_decode(q, k, v, tr.tables[s], tr.seq_lens[s], tr.scale)
+        assert max_err(out_to_f64(out), ref) <= TOL["bf16"], s
+    assert np.array_equal(to_host(kg), k) and np.array_equal(to_host(vg), v)
+
+
 # ----------------------------------------------------------------------------- prefill
 def gpu_prefill(pa, lay, chunk_lens, q, k, v, scale, out_dtype="f32"):
     torch = torch_mod()

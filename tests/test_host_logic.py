@@ -209,3 +209,30 @@ def test_oracle_swap_image_and_round_trip():
         oracle.swap_in(k1, v1, new + [-1, NB], img)      # pieces 3 and 4: bad target ids, skipped
         oracle.block_copy(k2, v2, list(zip(ids[:3], new)))
         assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_beam_search_copy_counts():
+    """Copy-the-parent beam search copies the closed-form 10,176 tokens (L7 §14 exercise 5);
+    with forked blocks only shared, partially filled last blocks are copied, at most k - 1 per
+    step, and each copy is the block the writer was about to write into."""
+    from synth import workloads as W
+    g = load("beam_copies.json")
+    k, bs = g["beam_width"], g["block_size"]
+    counts = []
+    for seed in range(8):
+        tr = W.mixed_decode_trace(beam_groups=1, beam_width=k, sample_groups=0, greedy=0, beam_prompt=g["prompt"],
+                                  steps=g["steps"], block_size=bs, seed=seed)
+        assert tr.whole_copy_tokens == g["whole_copy_tokens"]
+        for step, (cp, slots, lens) in enumerate(zip(tr.copies, tr.slots, tr.seq_lens)):
+            assert len(cp) <= k - 1
+            if (g["prompt"] + step) % bs == 0:       # the new token opens a fresh block: nothing shared to copy
+                assert not cp
+            dsts = {d for _, d in cp}
+            assert len(dsts) == len(cp) and not dsts & {s for s, _ in cp}
+            for _, d in cp:                            # a copy's target receives this step's token
+                assert d in set(int(s) // bs for s in slots)
+        counts.append(sum(len(c) for c in tr.copies))
+    # the demo's 35 copies (560 tokens) sit inside the spread of seeded trajectories
+    assert min(counts) <= g["demo_paged_copies"] <= max(counts)
+    assert g["demo_paged_copies"] * bs == g["demo_paged_copy_tokens"]
+    assert all(c * bs * 10 < g["whole_copy_tokens"] for c in counts)
