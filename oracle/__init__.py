@@ -11,7 +11,9 @@ numpy arrays into it.
 Array conventions
 -----------------
 * bf16 data is passed as ``numpy.uint16`` arrays holding the raw bf16 bit
-  patterns; fp32 data as ``numpy.float32``.  q, K and V share one dtype.
+  patterns; fp32 data as ``numpy.float32``; FP8 E4M3 caches as ``numpy.uint8``
+  codes (with a K scale and a V scale).  q, K and V share one dtype, except
+  that an FP8 cache is read with fp32 or bf16 queries.
 * Caches are ``[num_blocks, Hkv, block_size, D]``; q for decode is
   ``[B, Hq, D]``; q for prefill is ``[Tq, Hq, D]``.
 * Attention outputs come back as ``numpy.float64``.
@@ -91,9 +93,22 @@ def _bind(lib):
     lib.oracle_blockwise_decode_row.argtypes = ([_dbl_p, _vp, ctypes.c_int64, _vp, _vp, ctypes.c_int,
                                                  _i32_p] + [ctypes.c_int] * 6
                                                 + [ctypes.c_double, ctypes.c_int, _i32_p])
+    lib.oracle_kv_cache_write_fp8.argtypes = ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64_p] + [ctypes.c_int] * 5
+                                              + [ctypes.c_float, ctypes.c_float])
+    lib.oracle_paged_decode_ex.argtypes = ([_dbl_p, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_double,
+                                            ctypes.c_double, _i32_p, ctypes.c_int, _i32_p]
+                                           + [ctypes.c_int] * 6 + [ctypes.c_double])
+    lib.oracle_paged_prefill_ex.argtypes = ([_dbl_p, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_double,
+                                             ctypes.c_double, _i32_p, ctypes.c_int, _i32_p, _i32_p]
+                                            + [ctypes.c_int] * 6 + [ctypes.c_double])
+    lib.oracle_fp8_decode.argtypes = [_vp, _dbl_p, ctypes.c_int64]
+    lib.oracle_fp8_decode.restype = None
+    lib.oracle_fp8_encode.argtypes = [_vp, _vp, ctypes.c_int64]
+    lib.oracle_fp8_encode.restype = None
     lib.oracle_swap_out.argtypes = [_vp, _vp, _i64_p, ctypes.c_int, _vp] + [ctypes.c_int] * 5
     lib.oracle_swap_in.argtypes = [_vp, _vp, _i64_p, ctypes.c_int, _vp] + [ctypes.c_int] * 5
-    for name in ("oracle_kv_cache_write", "oracle_block_copy", "oracle_swap_out", "oracle_swap_in",
+    for name in ("oracle_kv_cache_write", "oracle_kv_cache_write_fp8", "oracle_paged_decode_ex",
+                 "oracle_paged_prefill_ex", "oracle_block_copy", "oracle_swap_out", "oracle_swap_in",
                  "oracle_paged_decode",
                  "oracle_paged_prefill", "oracle_contiguous_attention",
                  "oracle_blockwise_decode_row"):
@@ -106,7 +121,10 @@ def _dtype_code(a: np.ndarray) -> int:
         return 0
     if a.dtype == np.uint16:
         return 1
-    raise TypeError("oracle takes float32 or uint16 (bf16 bit patterns), got %s" % a.dtype)
+    if a.dtype == np.uint8:
+        return 2
+    raise TypeError("oracle takes float32, uint16 (bf16 bit patterns) or uint8 (fp8 E4M3 codes), got %s"
+                    % a.dtype)
 
 
 def _c(a, dtype=None):
@@ -184,43 +202,91 @@ def swap_in(k_cache, v_cache, ids, host):
     _check(rc, "oracle_swap_in")
 
 
-def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale):
-    """fp64 [B, Hq, D] decode attention through the block tables."""
+def _kv_args(q, k_cache, v_cache, k_scale, v_scale):
+    """dtype codes and scales of one attention call; an FP8 cache needs both scales."""
+    kd = _dtype_code(k_cache)
+    assert k_cache.dtype == v_cache.dtype
+    if kd == 2:
+        assert k_scale is not None and v_scale is not None, "an FP8 cache needs k_scale and v_scale"
+        assert q.dtype in (np.float32, np.uint16)
+        return _dtype_code(q), kd, float(k_scale), float(v_scale)
+    assert q.dtype == k_cache.dtype and k_scale is None and v_scale is None
+    return kd, kd, 1.0, 1.0
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=None, v_scale=None):
+    """fp64 [B, Hq, D] decode attention through the block tables (FP8 caches: value(code) * scale)."""
     lib = _load()
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     NB, Hkv, bs, D = k_cache.shape
     B, Hq, Dq = q.shape
-    assert Dq == D and q.dtype == k_cache.dtype == v_cache.dtype
+    assert Dq == D
+    qd, kd, ks, vs = _kv_args(q, k_cache, v_cache, k_scale, v_scale)
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     out = np.zeros((B, Hq, D), np.float64)
-    rc = lib.oracle_paged_decode(out.ctypes.data_as(_dbl_p), q.ctypes.data, k_cache.ctypes.data,
-                                 v_cache.ctypes.data, _dtype_code(q), bt.ctypes.data_as(_i32_p),
-                                 bt.shape[1], sl.ctypes.data_as(_i32_p), B, Hq, Hkv, D, bs, NB,
-                                 float(scale))
+    rc = lib.oracle_paged_decode_ex(out.ctypes.data_as(_dbl_p), q.ctypes.data, qd, k_cache.ctypes.data,
+                                    v_cache.ctypes.data, kd, ks, vs, bt.ctypes.data_as(_i32_p),
+                                    bt.shape[1], sl.ctypes.data_as(_i32_p), B, Hq, Hkv, D, bs, NB,
+                                    float(scale))
     _check(rc, "oracle_paged_decode")
     return out
 
 
-def paged_prefill(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, scale):
+def paged_prefill(q, k_cache, v_cache, block_tables, query_start_loc, seq_lens, scale, k_scale=None,
+                  v_scale=None):
     """fp64 [Tq, Hq, D] causal chunk attention over the paged cache."""
     lib = _load()
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     NB, Hkv, bs, D = k_cache.shape
     Tq, Hq, Dq = q.shape
-    assert Dq == D and q.dtype == k_cache.dtype == v_cache.dtype
+    assert Dq == D
+    qd, kd, ks, vs = _kv_args(q, k_cache, v_cache, k_scale, v_scale)
     bt = _c(block_tables, np.int32)
     qsl = _c(query_start_loc, np.int32)
     sl = _c(seq_lens, np.int32)
     B = sl.shape[0]
     assert qsl.shape[0] == B + 1 and qsl[-1] <= Tq
     out = np.zeros((Tq, Hq, D), np.float64)
-    rc = lib.oracle_paged_prefill(out.ctypes.data_as(_dbl_p), q.ctypes.data, k_cache.ctypes.data,
-                                  v_cache.ctypes.data, _dtype_code(q), bt.ctypes.data_as(_i32_p),
-                                  bt.shape[1], qsl.ctypes.data_as(_i32_p), sl.ctypes.data_as(_i32_p),
-                                  B, Hq, Hkv, D, bs, NB, float(scale))
+    rc = lib.oracle_paged_prefill_ex(out.ctypes.data_as(_dbl_p), q.ctypes.data, qd, k_cache.ctypes.data,
+                                     v_cache.ctypes.data, kd, ks, vs, bt.ctypes.data_as(_i32_p),
+                                     bt.shape[1], qsl.ctypes.data_as(_i32_p), sl.ctypes.data_as(_i32_p),
+                                     B, Hq, Hkv, D, bs, NB, float(scale))
     _check(rc, "oracle_paged_prefill")
     return out
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """fp64 values of E4M3 codes (uint8)."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib.oracle_fp8_decode(c.ctypes.data, out.ctypes.data_as(_dbl_p), c.size)
+    return out
+
+
+def fp8_encode(x) -> np.ndarray:
+    """E4M3 codes (uint8) of fp32 values: nearest, ties to even, saturating at 448."""
+    lib = _load()
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib.oracle_fp8_encode(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def kv_cache_write_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale):
+    """In-place: key/value [T, Hkv, D] (fp32 or bf16 bits) quantised into the uint8 FP8 caches."""
+    lib = _load()
+    NB, Hkv, bs, D = k_cache.shape
+    assert k_cache.dtype == v_cache.dtype == np.uint8
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    key, value = _c(key), _c(value)
+    assert key.dtype == value.dtype
+    slots = _c(slot_mapping, np.int64)
+    rc = lib.oracle_kv_cache_write_fp8(key.ctypes.data, value.ctypes.data, _dtype_code(key), k_cache.ctypes.data,
+                                       v_cache.ctypes.data, slots.ctypes.data_as(_i64_p), key.shape[0], NB, Hkv,
+                                       bs, D, float(k_scale), float(v_scale))
+    _check(rc, "oracle_kv_cache_write_fp8")
 
 
 def contiguous_attention(q, K, V, n_keys, scale):

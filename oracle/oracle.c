@@ -39,7 +39,18 @@
  *  - cache layout [num_blocks][Hkv][block_size][D], K and V separate;
  *  - slot = block * block_size + offset, slot < 0 means "skip this row".
  *
- * dtype codes: 0 = fp32, 1 = bf16 (stored as raw 16-bit patterns).
+ * dtype codes: 0 = fp32, 1 = bf16 (stored as raw 16-bit patterns), 2 = fp8
+ * E4M3 (raw 8-bit codes; the KV cache only).
+ *
+ * FP8 KV cache (Lecture 7 §10: KV quantised to FP8 / INT8 / INT4 shrinks
+ * memory and bandwidth by the bit count; the pages fix no format or scale,
+ * so the reading taken is): E4M3 as in the OCP 8-bit floating-point
+ * definition -- sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals at exponent 0, no infinities, S.1111.111 is NaN, largest finite
+ * magnitude 448 -- and one fp32 scale per tensor for K and one for V.  A row
+ * is stored as code(x / scale), the quotient in fp32, rounded to the nearest
+ * code (ties to the even code), magnitudes above 448 saturated to 448, NaN
+ * to the NaN code; it is read back as value(code) * scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,15 +62,52 @@
 #define ORC_ERR_RANGE (-2)
 #define ORC_ERR_NOMEM (-3)
 
+/* The value of an E4M3 code, by the definition above. */
+static double fp8_value(uint8_t c) {
+  int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* The code of an fp32 value: nearest of the 127 finite magnitudes (a plain
+ * search), ties to the even code, saturating at 448; the sign is kept (a
+ * negative value that rounds to zero gives negative zero). */
+static uint8_t fp8_code(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return sign | 0x7F;
+  double a = fabs((double)x);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < 127; ++c) {
+    double dd = fabs(a - fp8_value((uint8_t)c));
+    if (dd < best_d || (dd == best_d && (c & 1) == 0)) {
+      best_d = dd;
+      best = c;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
 static double elem(const void *base, int64_t i, int dtype) {
   if (dtype == 0) return (double)((const float *)base)[i];
+  if (dtype == 2) return fp8_value(((const uint8_t *)base)[i]);
   uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
   return (double)f;
 }
 
-static int elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
+static int elem_bytes(int dtype) { return dtype == 0 ? 4 : dtype == 1 ? 2 : 1; }
+
+/* Exposed for the pins: decode n codes / encode n fp32 values. */
+void oracle_fp8_decode(const uint8_t *codes, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = fp8_value(codes[i]);
+}
+void oracle_fp8_encode(const float *x, uint8_t *codes, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = fp8_code(x[i]);
+}
 
 /* Index of element (blk, h, off, d) in a [NB][Hkv][bs][D] cache. */
 static int64_t cache_index(int64_t blk, int h, int off, int d, int Hkv, int bs,
@@ -94,6 +142,40 @@ int oracle_kv_cache_write(const void *key, const void *value, void *k_cache,
       int64_t dst = cache_index(blk, h, off, 0, Hkv, bs, D);
       memcpy((char *)k_cache + dst * eb, (const char *)key + src * eb, (size_t)D * eb);
       memcpy((char *)v_cache + dst * eb, (const char *)value + src * eb, (size_t)D * eb);
+    }
+  }
+  return rc;
+}
+
+/*
+ * KV write into an FP8 cache (the write above, with the quantisation of the
+ * header): key and value rows are fp32 (src_dtype 0) or bf16 (1); every
+ * element x of a key row is stored as fp8_code((float)x / k_scale), of a
+ * value row as fp8_code((float)x / v_scale), the quotient an fp32 division.
+ */
+int oracle_kv_cache_write_fp8(const void *key, const void *value, int src_dtype, uint8_t *k_cache,
+                              uint8_t *v_cache, const int64_t *slot_mapping, int T, int num_blocks,
+                              int Hkv, int bs, int D, float k_scale, float v_scale) {
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return ORC_ERR_ARG;
+  if (src_dtype != 0 && src_dtype != 1) return ORC_ERR_ARG;
+  int rc = ORC_OK;
+  for (int t = 0; t < T; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t blk = s / bs;
+    int off = (int)(s % bs);
+    if (blk >= num_blocks) {
+      rc = ORC_ERR_RANGE;
+      continue;
+    }
+    for (int h = 0; h < Hkv; ++h) {
+      int64_t src = ((int64_t)t * Hkv + h) * D;
+      int64_t dst = cache_index(blk, h, off, 0, Hkv, bs, D);
+      for (int d = 0; d < D; ++d) {
+        float kx = (float)elem(key, src + d, src_dtype), vx = (float)elem(value, src + d, src_dtype);
+        k_cache[dst + d] = fp8_code(kx / k_scale);
+        v_cache[dst + d] = fp8_code(vx / v_scale);
+      }
     }
   }
   return rc;
@@ -165,10 +247,10 @@ int oracle_swap_in(void *k_cache, void *v_cache, const int64_t *ids, int n, cons
  *   out = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
  * Two passes over the scores, fp64 throughout.  n_keys == 0 gives zeros.
  */
-static int attend_row(double *out, const void *q, int64_t q_off, const void *k_cache,
-                      const void *v_cache, int dtype, const int32_t *table,
-                      int max_blocks, int n_keys, int kh, int Hkv, int D, int bs,
-                      int num_blocks, double scale, double *scores) {
+static int attend_row(double *out, const void *q, int64_t q_off, int q_dtype, const void *k_cache,
+                      const void *v_cache, int dtype, double k_scale, double v_scale,
+                      const int32_t *table, int max_blocks, int n_keys, int kh, int Hkv, int D,
+                      int bs, int num_blocks, double scale, double *scores) {
   for (int d = 0; d < D; ++d) out[d] = 0.0;
   if (n_keys <= 0) return ORC_OK;
   if ((n_keys + bs - 1) / bs > max_blocks) return ORC_ERR_RANGE;
@@ -178,7 +260,7 @@ static int attend_row(double *out, const void *q, int64_t q_off, const void *k_c
     if (phys < 0 || phys >= num_blocks) return ORC_ERR_RANGE;
     int64_t base = cache_index(phys, kh, t % bs, 0, Hkv, bs, D);
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, dtype) * elem(k_cache, base + d, dtype);
+    for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, q_dtype) * (elem(k_cache, base + d, dtype) * k_scale);
     scores[t] = scale * dot;
     if (scores[t] > m) m = scores[t];
   }
@@ -187,7 +269,7 @@ static int attend_row(double *out, const void *q, int64_t q_off, const void *k_c
     double e = exp(scores[t] - m);
     l += e;
     int64_t base = cache_index(table[t / bs], kh, t % bs, 0, Hkv, bs, D);
-    for (int d = 0; d < D; ++d) out[d] += e * elem(v_cache, base + d, dtype);
+    for (int d = 0; d < D; ++d) out[d] += e * (elem(v_cache, base + d, dtype) * v_scale);
   }
   for (int d = 0; d < D; ++d) out[d] /= l;
   return ORC_OK;
@@ -199,10 +281,10 @@ static int attend_row(double *out, const void *q, int64_t q_off, const void *k_c
  * of KV head h / (Hq / Hkv).  out is fp64 [B][Hq][D]; q has the KV dtype and
  * layout [B][Hq][D]; block_tables is [B][max_blocks].
  */
-int oracle_paged_decode(double *out, const void *q, const void *k_cache,
-                        const void *v_cache, int dtype, const int32_t *block_tables,
-                        int max_blocks, const int32_t *seq_lens, int B, int Hq,
-                        int Hkv, int D, int bs, int num_blocks, double scale) {
+int oracle_paged_decode_ex(double *out, const void *q, int q_dtype, const void *k_cache,
+                           const void *v_cache, int dtype, double k_scale, double v_scale,
+                           const int32_t *block_tables, int max_blocks, const int32_t *seq_lens,
+                           int B, int Hq, int Hkv, int D, int bs, int num_blocks, double scale) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return ORC_ERR_ARG;
   if (Hkv <= 0 || Hq % Hkv != 0 || bs <= 0 || D <= 0) return ORC_ERR_ARG;
   int g = Hq / Hkv;
@@ -215,13 +297,22 @@ int oracle_paged_decode(double *out, const void *q, const void *k_cache,
   for (int b = 0; b < B && rc == ORC_OK; ++b) {
     for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
       int64_t row = (int64_t)b * Hq + h;
-      rc = attend_row(out + row * D, q, row * D, k_cache, v_cache, dtype,
+      rc = attend_row(out + row * D, q, row * D, q_dtype, k_cache, v_cache, dtype, k_scale, v_scale,
                       block_tables + (int64_t)b * max_blocks, max_blocks, seq_lens[b],
                       h / g, Hkv, D, bs, num_blocks, scale, scores);
     }
   }
   free(scores);
   return rc;
+}
+
+/* q and the caches in one dtype (fp32 or bf16), no scales. */
+int oracle_paged_decode(double *out, const void *q, const void *k_cache,
+                        const void *v_cache, int dtype, const int32_t *block_tables,
+                        int max_blocks, const int32_t *seq_lens, int B, int Hq,
+                        int Hkv, int D, int bs, int num_blocks, double scale) {
+  return oracle_paged_decode_ex(out, q, dtype, k_cache, v_cache, dtype, 1.0, 1.0, block_tables,
+                                max_blocks, seq_lens, B, Hq, Hkv, D, bs, num_blocks, scale);
 }
 
 /*
@@ -233,11 +324,11 @@ int oracle_paged_decode(double *out, const void *q, const void *k_cache,
  * pos = seq_lens[b] - n_b + i and attends to tokens 0..pos (causal).
  * q and out are [Tq][Hq][D].
  */
-int oracle_paged_prefill(double *out, const void *q, const void *k_cache,
-                         const void *v_cache, int dtype, const int32_t *block_tables,
-                         int max_blocks, const int32_t *query_start_loc,
-                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
-                         int bs, int num_blocks, double scale) {
+int oracle_paged_prefill_ex(double *out, const void *q, int q_dtype, const void *k_cache,
+                            const void *v_cache, int dtype, double k_scale, double v_scale,
+                            const int32_t *block_tables, int max_blocks,
+                            const int32_t *query_start_loc, const int32_t *seq_lens, int B,
+                            int Hq, int Hkv, int D, int bs, int num_blocks, double scale) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens)
     return ORC_ERR_ARG;
   if (Hkv <= 0 || Hq % Hkv != 0 || bs <= 0 || D <= 0) return ORC_ERR_ARG;
@@ -258,14 +349,24 @@ int oracle_paged_prefill(double *out, const void *q, const void *k_cache,
       int pos = seq_lens[b] - n_b + i;
       for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
         int64_t row = (int64_t)(q0 + i) * Hq + h;
-        rc = attend_row(out + row * D, q, row * D, k_cache, v_cache, dtype,
-                        block_tables + (int64_t)b * max_blocks, max_blocks, pos + 1,
+        rc = attend_row(out + row * D, q, row * D, q_dtype, k_cache, v_cache, dtype, k_scale,
+                        v_scale, block_tables + (int64_t)b * max_blocks, max_blocks, pos + 1,
                         h / g, Hkv, D, bs, num_blocks, scale, scores);
       }
     }
   }
   free(scores);
   return rc;
+}
+
+int oracle_paged_prefill(double *out, const void *q, const void *k_cache,
+                         const void *v_cache, int dtype, const int32_t *block_tables,
+                         int max_blocks, const int32_t *query_start_loc,
+                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                         int bs, int num_blocks, double scale) {
+  return oracle_paged_prefill_ex(out, q, dtype, k_cache, v_cache, dtype, 1.0, 1.0, block_tables,
+                                 max_blocks, query_start_loc, seq_lens, B, Hq, Hkv, D, bs,
+                                 num_blocks, scale);
 }
 
 /*

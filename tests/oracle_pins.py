@@ -23,7 +23,17 @@ What each pin rests on:
                       attention; a chunk of one row equals decode;
   cache_vs_recompute -- decoding with the paged cache gives the same logits and
                       the same greedy tokens as recomputing without a cache
-                      (Lecture 16 §1.1; Lecture 7 §4.2, block sizes 1/4/16/64).
+                      (Lecture 16 §1.1; Lecture 7 §4.2, block sizes 1/4/16/64);
+  fp8_codec        -- E4M3 decode of all 256 codes and the quantiser (nearest,
+                      ties to even, saturating at 448) against torch's
+                      float8_e4m3fn conversions (a library routine), plus
+                      codes with known values;
+  fp8_attention    -- attention over an FP8 cache equals attention over the
+                      dequantised values: exactly, through the fp32 path, when
+                      the scales are powers of two; against torch SDPA in fp64
+                      for other scales (decode and prefill);
+  fp8_write        -- the quantising KV write stores torch's codes of
+                      fp32(x) / fp32(scale) at the slots, and nothing else.
 """
 from __future__ import annotations
 
@@ -351,6 +361,101 @@ def pin_cache_vs_recompute(orc, block_sizes=(1, 4, 16, 64), steps=20):
             assert_close(np.array(lgs[i]), np.array(ref_logits[i]), 1e-12, "logits bs=%d" % bs)
 
 
+def _torch_fp8_codes(x_f32):
+    """torch's E4M3 codes of fp32 values after clamping to the finite range."""
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_fp8_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_fp8_codec(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    val = orc.fp8_decode(codes)
+    ref = _torch_fp8_values(codes)
+    assert np.array_equal(np.isnan(val), np.isnan(ref)) and np.isnan(val).sum() == 2
+    ok = ~np.isnan(ref)
+    assert np.array_equal(val[ok], ref[ok]) and np.array_equal(np.signbit(val[ok]), np.signbit(ref[ok]))
+    # known codes: 1.0, the largest finite value, the smallest subnormal, ties to the even code
+    known = {1.0: 0x38, 448.0: 0x7E, 2.0 ** -9: 0x01, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
+             1.0625: 0x38, 1.1875: 0x3A, 1000.0: 0x7E, -1.0: 0xB8, -0.0: 0x80}
+    xs = np.array(list(known), np.float32)
+    assert orc.fp8_encode(xs).tolist() == list(known.values())
+    # every midpoint between neighbouring codes, a hair either side, and random magnitudes
+    pos = np.sort(ref[:127])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(8)
+    x = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                        np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+                        rng.lognormal(-3.0, 3.0, 20000), [449.0, 463.99, 464.0, 464.01, 1e30, 1e-30]]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(orc.fp8_encode(x), _torch_fp8_codes(x))
+
+
+def _fp8_problem(lens, Hq, Hkv, D, bs, seed, ks, vs):
+    layout, q, k, v = make_problem(lens, Hq, Hkv, D, bs, seed=seed)
+    kc = _torch_fp8_codes(k / np.float32(ks))
+    vc = _torch_fp8_codes(v / np.float32(vs))
+    return layout, q, kc, vc
+
+
+def pin_fp8_attention(orc):
+    lens = [17, 64, 100, 5, 1]
+    Hq, Hkv, D, bs = 8, 2, 64, 16
+    for ks, vs in ((2.0 ** -6, 2.0 ** -5), (0.0123, 0.0377)):
+        layout, q, kc, vc = _fp8_problem(lens, Hq, Hkv, D, bs, 21, ks, vs)
+        out = orc.paged_decode(q, kc, vc, layout.block_tables, layout.seq_lens, 0.125, k_scale=ks, v_scale=vs)
+        kd, vd = _torch_fp8_values(kc) * ks, _torch_fp8_values(vc) * vs
+        if ks == 2.0 ** -6:
+            # power-of-two scales: the dequantised values are exact in fp32
+            ref = orc.paged_decode(q, kd.astype(np.float32), vd.astype(np.float32), layout.block_tables,
+                                   layout.seq_lens, 0.125)
+            assert_close(out, ref, 1e-15, "fp8 decode == fp32 decode of the dequantised cache")
+        for b, L in enumerate(lens):
+            K = gather_contiguous(kd, layout.block_tables[b], L).transpose(1, 0, 2).copy()
+            V = gather_contiguous(vd, layout.block_tables[b], L).transpose(1, 0, 2).copy()
+            ref = _sdpa(q[b].astype(np.float64)[:, None, :].copy(), K, V, 0.125)[:, 0, :]
+            assert_close(out[b], ref, 1e-12, "fp8 decode vs sdpa b=%d" % b)
+    # prefill: a chunk of 7 rows at the end of a 40-token sequence
+    layout, _, kc, vc = _fp8_problem([40], Hq, Hkv, D, bs, 22, 0.02, 0.03)
+    qp = synth.normal_f32((7, Hq, D), 1.0, 23)
+    out = orc.paged_prefill(qp, kc, vc, layout.block_tables, np.array([0, 7], np.int32), layout.seq_lens, 0.125,
+                            k_scale=0.02, v_scale=0.03)
+    K = gather_contiguous(_torch_fp8_values(kc) * 0.02, layout.block_tables[0], 40).transpose(1, 0, 2).copy()
+    V = gather_contiguous(_torch_fp8_values(vc) * 0.03, layout.block_tables[0], 40).transpose(1, 0, 2).copy()
+    mask = np.arange(40)[None, :] <= (33 + np.arange(7))[:, None]
+    ref = _sdpa(qp.astype(np.float64).transpose(1, 0, 2).copy(), K, V, 0.125, mask=mask).transpose(1, 0, 2)
+    assert_close(out, ref, 1e-12, "fp8 prefill vs sdpa")
+
+
+def pin_fp8_write(orc):
+    NB, Hkv, bs, D, T = 7, 2, 4, 16, 9
+    for dt in ("f32", "bf16"):
+        key = synth.normal_f32((T, Hkv, D), 3.0, 31)
+        val = synth.normal_f32((T, Hkv, D), 0.2, 32)
+        if dt == "bf16":
+            key, val = synth.round_to_bf16_bits(key), synth.round_to_bf16_bits(val)
+        kc = np.full((NB, Hkv, bs, D), 0x55, np.uint8)
+        vc = kc.copy()
+        slots = np.array([3, 27, -1, 0, 12, 5, 26, 17, 8], np.int64)
+        orc.kv_cache_write_fp8(key, val, kc, vc, slots, 0.011, 0.0007)
+        kf = to_f64(key).astype(np.float32)
+        vf = to_f64(val).astype(np.float32)
+        touched = set()
+        for t, s in enumerate(slots):
+            if s < 0:
+                continue
+            touched.add((s // bs, s % bs))
+            assert np.array_equal(kc[s // bs, :, s % bs], _torch_fp8_codes(kf[t] / np.float32(0.011)))
+            assert np.array_equal(vc[s // bs, :, s % bs], _torch_fp8_codes(vf[t] / np.float32(0.0007)))
+        for blk in range(NB):
+            for off in range(bs):
+                if (blk, off) not in touched:
+                    assert (kc[blk, :, off] == 0x55).all() and (vc[blk, :, off] == 0x55).all()
+
+
 ALL_PINS = [pin_brute_force, pin_torch_sdpa_decode, pin_torch_sdpa_prefill, pin_paged_vs_contiguous,
             pin_permutation_bit_exact, pin_blockwise_online, pin_gqa_as_mha, pin_closed_forms,
-            pin_prefill_rows, pin_cache_vs_recompute]
+            pin_prefill_rows, pin_cache_vs_recompute, pin_fp8_codec, pin_fp8_attention, pin_fp8_write]

@@ -16,8 +16,8 @@ from oracle_pins import ALL_PINS
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTATIONS = {
-    "gqa_modulo_mapping": ("h / g, Hkv, D, bs, num_blocks, scale, scores);\n    }\n  }\n  free(scores);\n  return rc;\n}\n\n/*\n * Chunked",
-                           "h % Hkv, Hkv, D, bs, num_blocks, scale, scores);\n    }\n  }\n  free(scores);\n  return rc;\n}\n\n/*\n * Chunked"),
+    "gqa_modulo_mapping": ("h / g, Hkv, D, bs, num_blocks, scale, scores);\n    }\n  }\n  free(scores);\n  return rc;\n}\n\n/* q and",
+                           "h % Hkv, Hkv, D, bs, num_blocks, scale, scores);\n    }\n  }\n  free(scores);\n  return rc;\n}\n\n/* q and"),
     "wrong_offset_in_block": ("int64_t base = cache_index(phys, kh, t % bs, 0, Hkv, bs, D);",
                               "int64_t base = cache_index(phys, kh, (t + 1) % bs, 0, Hkv, bs, D);"),
     "floor_loop_bound": ("  for (int d = 0; d < D; ++d) out[d] = 0.0;\n  if (n_keys <= 0) return ORC_OK;\n  if ((n_keys",
@@ -30,11 +30,17 @@ MUTATIONS = {
                               "return (((blk * bs + off) * (int64_t)Hkv + h) * D) + d;"),
     "softmax_sign": ("    double e = exp(scores[t] - m);\n    l += e;\n    int64_t base",
                      "    double e = exp(m - scores[t]);\n    l += e;\n    int64_t base"),
-    "v_read_from_k": ("out[d] += e * elem(v_cache, base + d, dtype);\n  }\n  for (int d = 0; d < D; ++d) out[d] /= l;",
-                      "out[d] += e * elem(k_cache, base + d, dtype);\n  }\n  for (int d = 0; d < D; ++d) out[d] /= l;"),
+    "v_read_from_k": ("out[d] += e * (elem(v_cache, base + d, dtype) * v_scale);\n  }\n  for (int d = 0; d < D; ++d) out[d] /= l;",
+                      "out[d] += e * (elem(k_cache, base + d, dtype) * v_scale);\n  }\n  for (int d = 0; d < D; ++d) out[d] /= l;"),
     "kv_write_swapped": ("memcpy((char *)k_cache + dst * eb, (const char *)key + src * eb",
                          "memcpy((char *)k_cache + dst * eb, (const char *)value + src * eb"),
     "prefill_position_from_zero": ("int pos = seq_lens[b] - n_b + i;", "int pos = i;"),
+    "fp8_exponent_bias_8": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "fp8_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "fp8_ties_to_odd": ("(dd == best_d && (c & 1) == 0)", "(dd == best_d && (c & 1) == 1)"),
+    "fp8_search_misses_largest_code": ("for (int c = 0; c < 127; ++c) {\n    double dd", "for (int c = 0; c < 126; ++c) {\n    double dd"),
+    "fp8_k_scaled_by_v_scale": ("(elem(k_cache, base + d, dtype) * k_scale)", "(elem(k_cache, base + d, dtype) * v_scale)"),
+    "fp8_write_multiplies_scale": ("fp8_code(kx / k_scale)", "fp8_code(kx * k_scale)"),
 }
 
 
