@@ -32,7 +32,10 @@
  *     enqueues work on it and returns; results are ready when the stream
  *     reaches that point.
  *   - dtype codes: PA_F32 (IEEE fp32) or PA_BF16 (bfloat16).  q, K and V
- *     share one dtype; accumulation is always fp32.
+ *     share one dtype; accumulation is always fp32.  PA_FP8_E4M3 (8-bit
+ *     codes, see the _fp8 calls) is a KV-cache storage format: the byte-moving
+ *     calls (kv_cache_write as a plain copy, block_copy, the swaps) take it
+ *     like any other dtype.
  *   - KV cache layout, one layer: [num_blocks][num_kv_heads][block_size][head_dim],
  *     K and V in separate arrays ([M2] §5.2; head-major inside a block so one
  *     (block, head) tile is contiguous).
@@ -76,7 +79,7 @@ extern "C" {
 #define PA_EXPORT
 #endif
 
-enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 };
+enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 };
 
 enum pa_status {
   PA_OK = 0,
@@ -195,6 +198,65 @@ PA_EXPORT int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void 
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, int32_t num_blocks, int32_t max_query_len,
                              int32_t max_seq_len, float scale, void *stream);
+
+/*
+ * FP8 KV cache ([L7] §10: storing KV in 8 bits shrinks its memory and the
+ * bandwidth attention needs by the bit count; the pages fix neither format
+ * nor scaling, so this library's convention is):
+ *   - codes are E4M3 as in the OCP 8-bit floating-point formats: sign, 4
+ *     exponent bits (bias 7), 3 mantissa bits, subnormals, no infinities,
+ *     S.1111.111 = NaN, largest magnitude 448;
+ *   - one fp32 scale per tensor: K = value(code) * k_scale and
+ *     V = value(code) * v_scale (scales finite and > 0, else PA_ERR_SHAPE);
+ *   - attention reads bf16 q and computes exactly as on a bf16 cache holding
+ *     value(code) (every E4M3 value is a bf16 value), with k_scale folded into
+ *     the score scale and v_scale into the final normalisation;
+ *   - the FP8 attention calls serve head_dim 128, block_size in
+ *     {8, 16, 32, 64, 128} and num_heads / num_kv_heads <= 16 (prefill: a
+ *     divisor of 16); other shapes return PA_ERR_UNSUPPORTED.
+ *
+ * kv_cache_write_fp8 -- kv_cache_write into FP8 caches: key and value rows
+ * ([num_tokens][num_kv_heads][head_dim], src_dtype PA_F32 or PA_BF16) are
+ * quantised on the way: element x of a key row becomes the code nearest to
+ * the fp32 quotient x / k_scale (IEEE division, round to nearest), ties to
+ * the even code, magnitudes beyond 448 saturated to 448 (values likewise
+ * with v_scale); a NaN element gives an unspecified code.  Caches
+ * [num_blocks][num_kv_heads][block_size][head_dim] bytes.  head_dim must be
+ * a multiple of 16 (else PA_ERR_UNSUPPORTED).  Slots as in kv_cache_write.
+ */
+PA_EXPORT int kv_cache_write_fp8(const void *key, const void *value, int32_t src_dtype, void *k_cache,
+                                 void *v_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                                 int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                                 int32_t head_dim, float k_scale, float v_scale, void *stream);
+
+/*
+ * paged_attn_decode_fp8 -- paged_attn_decode over FP8 caches (q bf16
+ * [num_seqs][num_heads][head_dim], out PA_F32 or PA_BF16).  All other
+ * arguments, the workspace (paged_attn_decode_workspace_size covers it) and
+ * the guarantees are those of paged_attn_decode.
+ */
+PA_EXPORT int paged_attn_decode_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                                    const void *v_cache, float k_scale, float v_scale,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_seq_len, float scale,
+                                    int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
+ * paged_attn_prefill_chunk_fp8 -- paged_attn_prefill_chunk over FP8 caches
+ * (q bf16 [num_query_tokens][num_heads][head_dim]); otherwise as
+ * paged_attn_prefill_chunk.
+ */
+PA_EXPORT int paged_attn_prefill_chunk_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                                           const void *v_cache, float k_scale, float v_scale,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *query_start_loc, const int32_t *seq_lens,
+                                           int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_query_len, int32_t max_seq_len,
+                                           float scale, void *stream);
 
 /*
  * block_copy -- batched copy of whole physical blocks for copy-on-write

@@ -19,17 +19,20 @@ __all__ = [
     "PA_F32", "PA_BF16", "PagedAttnError", "lib", "library_path", "pa_status_string",
     "pa_abi_version", "kv_cache_write", "paged_attn_decode_workspace_size", "paged_attn_decode",
     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in", "swap_host_bytes",
+    "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
     "EXPORTED_SYMBOLS",
 ]
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
-                    "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in")
+                    "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
+                    "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8")
 
 
 class PagedAttnError(RuntimeError):
@@ -60,6 +63,15 @@ def _load():
     L.paged_attn_prefill_chunk.restype = ctypes.c_int
     L.block_copy.argtypes = [vp, vp, vp] + [i32] * 6 + [vp]
     L.block_copy.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    L.kv_cache_write_fp8.argtypes = [vp, vp, i32, vp, vp, vp] + [i32] * 5 + [f32, f32, vp]
+    L.kv_cache_write_fp8.restype = ctypes.c_int
+    L.paged_attn_decode_fp8.argtypes = ([vp, i32, vp, vp, vp, f32, f32, vp, i32, vp] + [i32] * 7
+                                        + [f32, i32, vp, ctypes.c_size_t, vp])
+    L.paged_attn_decode_fp8.restype = ctypes.c_int
+    L.paged_attn_prefill_chunk_fp8.argtypes = ([vp, i32, vp, vp, vp, f32, f32, vp, i32, vp, vp] + [i32] * 9
+                                               + [f32, vp])
+    L.paged_attn_prefill_chunk_fp8.restype = ctypes.c_int
     L.kv_swap_out.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
     L.kv_swap_out.restype = ctypes.c_int
     L.kv_swap_in.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
@@ -103,7 +115,15 @@ def _dtype_code(t) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError("unsupported dtype %s (float32, bfloat16, or uint8 / float8_e4m3fn codes)" % t.dtype)
+
+
+def _fp8_cache(t, name: str):
+    if _dtype_code(t) != PA_FP8_E4M3:
+        raise TypeError("%s must hold E4M3 codes (uint8 or float8_e4m3fn), got %s" % (name, t.dtype))
+    return _dev(t, name)
 
 
 def _dev(t, name: str, dtype=None):
@@ -254,3 +274,61 @@ def kv_swap_out(k_cache, v_cache, block_ids, host_dst, staging, stream=None):
 def kv_swap_in(k_cache, v_cache, block_ids, host_src, staging, stream=None):
     """Write the pieces of host_src (as kv_swap_out packs them) to blocks block_ids of both caches."""
     _swap("kv_swap_in", k_cache, v_cache, block_ids, host_src, staging, stream)
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3) caches
+def kv_cache_write_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float, stream=None):
+    """Quantise key/value [T, Hkv, D] (fp32 or bf16) into the FP8 caches [NB, Hkv, bs, D] at slot_mapping."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or key.shape != value.shape or k_cache.shape != v_cache.shape:
+        raise ValueError("shape mismatch")
+    if key.dtype != value.dtype:
+        raise TypeError("key and value must share one dtype")
+    st = _L().kv_cache_write_fp8(_dev(key, "key"), _dev(value, "value"), _dtype_code(key),
+                                _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"),
+                                _dev(slot_mapping, "slot_mapping", torch.int64), T, NB, Hkv, bs, D,
+                                float(k_scale), float(v_scale), _stream(stream))
+    _check("kv_cache_write_fp8", st)
+
+
+def paged_attn_decode_fp8(out, q, k_cache, v_cache, k_scale: float, v_scale: float, block_tables, seq_lens,
+                          scale: float, max_seq_len: int, partition_size: int = 0, workspace=None, stream=None):
+    """paged_attn_decode over FP8 caches; q is bf16 [B, Hq, D]."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _L().paged_attn_decode_fp8(_dev(out, "out"), _dtype_code(out), _dev(q, "q", torch.bfloat16),
+                                   _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"),
+                                   float(k_scale), float(v_scale), _dev(block_tables, "block_tables", torch.int32),
+                                   block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D,
+                                   bs, NB, int(max_seq_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                                   _stream(stream))
+    _check("paged_attn_decode_fp8", st)
+
+
+def paged_attn_prefill_chunk_fp8(out, q, k_cache, v_cache, k_scale: float, v_scale: float, block_tables,
+                                 query_start_loc, seq_lens, scale: float, max_query_len: int, max_seq_len: int,
+                                 stream=None):
+    """paged_attn_prefill_chunk over FP8 caches; q is bf16 [Tq, Hq, D]."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    Tq, Hq, Dq = q.shape
+    B = seq_lens.shape[0]
+    if Dq != D or tuple(out.shape) != (Tq, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    st = _L().paged_attn_prefill_chunk_fp8(_dev(out, "out"), _dtype_code(out), _dev(q, "q", torch.bfloat16),
+                                          _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"),
+                                          float(k_scale), float(v_scale),
+                                          _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                                          _dev(query_start_loc, "query_start_loc", torch.int32),
+                                          _dev(seq_lens, "seq_lens", torch.int32), B, Tq, Hq, Hkv, D, bs, NB,
+                                          int(max_query_len), int(max_seq_len), float(scale), _stream(stream))
+    _check("paged_attn_prefill_chunk_fp8", st)

@@ -15,8 +15,12 @@ constexpr int kDefaultPartitionTokens = 256;
 constexpr int64_t kStreamKMaxPiecesPerRow = 16;
 constexpr int kMaxGridYZ = 65535;
 
-int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
+// dtypes attention computes in (q, out, and the KV of the plain calls)
 bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+// dtypes the byte-moving calls store
+bool storage_dtype_ok(int32_t dtype) { return dtype_ok(dtype) || dtype == PA_FP8_E4M3; }
+bool scale_ok(float s) { return s > 0.f && s <= 3.4e38f; }  // finite and positive (false for NaN)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -141,7 +145,7 @@ int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_ca
                    void *stream) {
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
     return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!storage_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
@@ -149,6 +153,21 @@ int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_ca
                                                  num_tokens, num_blocks, num_kv_heads, block_size,
                                                  head_dim, elem_bytes(dtype),
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int kv_cache_write_fp8(const void *key, const void *value, int32_t src_dtype, void *k_cache, void *v_cache,
+                       const int64_t *slot_mapping, int32_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                       int32_t block_size, int32_t head_dim, float k_scale, float v_scale, void *stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
+  if (!dtype_ok(src_dtype) || head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  return launch_status(pa::launch_kv_cache_write_fp8(key, value, src_dtype == PA_BF16, k_cache, v_cache,
+                                                     slot_mapping, num_tokens, num_blocks, num_kv_heads,
+                                                     block_size, head_dim, k_scale, v_scale,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -166,23 +185,34 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int
   return std::max(a.workspace_bytes, b.workspace_bytes);
 }
 
-int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k_cache,
-                      const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
-                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
-                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
-                      int32_t partition_size, void *workspace, size_t workspace_bytes,
-                      void *stream) {
-  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                  num_blocks, max_blocks_per_seq, max_seq_len, kv_dtype, out_dtype);
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points.  kv_dtype PA_FP8_E4M3: the caches hold E4M3
+// codes read as value * k_scale / v_scale, q is bf16, and only the MFMA
+// shapes are served.
+int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,
+                int32_t kv_dtype, float k_scale, float v_scale, const int32_t *block_tables,
+                int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t max_seq_len, float scale, int32_t partition_size, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  const bool fp8 = kv_dtype == PA_FP8_E4M3;
+  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
   if (st != PA_OK) return st;
+  if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
+  if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
+  if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size) && num_heads / num_kv_heads <= 16))
+    return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
 
   const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
-  const bool mfma_shape = kv_dtype == PA_BF16 && head_dim == 128 && pa::mfma_block_size(block_size) &&
+  const bool mfma_shape = (kv_dtype == PA_BF16 || fp8) && head_dim == 128 && pa::mfma_block_size(block_size) &&
                           num_heads / num_kv_heads <= 16;
   DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                                 cap, partition_size, mfma_shape);
@@ -197,6 +227,9 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.kv_bf16 = kv_dtype == PA_BF16;
+  p.kv_fp8 = fp8;
+  p.k_scale = fp8 ? k_scale : 1.f;
+  p.v_scale = fp8 ? v_scale : 1.f;
   p.block_tables = block_tables;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.seq_lens = seq_lens;
@@ -226,28 +259,68 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   return launch_status(pa::launch_decode(p, s));
 }
 
-int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,
-                             const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
-                             int32_t max_blocks_per_seq, const int32_t *query_start_loc,
-                             const int32_t *seq_lens, int32_t num_seqs, int32_t num_query_tokens,
-                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, int32_t num_blocks, int32_t max_query_len,
-                             int32_t max_seq_len, float scale, void *stream) {
-  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                  num_blocks, max_blocks_per_seq, max_seq_len, kv_dtype, out_dtype);
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                      const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  if (!dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, 1.f, 1.f, block_tables, max_blocks_per_seq,
+                     seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
+                     scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,
+                          float k_scale, float v_scale, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                          float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return decode_impl(out, out_dtype, q, k_cache, v_cache, PA_FP8_E4M3, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_seq_len, scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,
+                 int32_t kv_dtype, float k_scale, float v_scale, const int32_t *block_tables,
+                 int32_t max_blocks_per_seq, const int32_t *query_start_loc, const int32_t *seq_lens,
+                 int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_query_len,
+                 int32_t max_seq_len, float scale, void *stream) {
+  const bool fp8 = kv_dtype == PA_FP8_E4M3;
+  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
   if (st != PA_OK) return st;
+  if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
+  if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
+  const int g = num_heads / num_kv_heads;
+  if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size) && g <= 16 && 16 % g == 0))
+    return PA_ERR_UNSUPPORTED;
   if (max_query_len < 0 || num_query_tokens < 0) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens)
     return PA_ERR_NULL;
   const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
-  pa::PrefillParams p;
+  pa::PrefillParams p = {};
   p.out = out;
   p.out_bf16 = out_dtype == PA_BF16;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.kv_bf16 = kv_dtype == PA_BF16;
+  p.kv_fp8 = fp8;
+  p.k_scale = fp8 ? k_scale : 1.f;
+  p.v_scale = fp8 ? v_scale : 1.f;
   p.block_tables = block_tables;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.query_start_loc = query_start_loc;
@@ -265,12 +338,41 @@ int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const 
   return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 
+}  // namespace
+
+extern "C" {
+
+int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                             const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *query_start_loc,
+                             const int32_t *seq_lens, int32_t num_seqs, int32_t num_query_tokens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_query_len,
+                             int32_t max_seq_len, float scale, void *stream) {
+  if (!dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  return prefill_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, 1.f, 1.f, block_tables, max_blocks_per_seq,
+                      query_start_loc, seq_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_query_len, max_seq_len, scale, stream);
+}
+
+int paged_attn_prefill_chunk_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                                 const void *v_cache, float k_scale, float v_scale, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *query_start_loc,
+                                 const int32_t *seq_lens, int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_query_len, int32_t max_seq_len, float scale,
+                                 void *stream) {
+  return prefill_impl(out, out_dtype, q, k_cache, v_cache, PA_FP8_E4M3, k_scale, v_scale, block_tables,
+                      max_blocks_per_seq, query_start_loc, seq_lens, num_seqs, num_query_tokens, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_query_len, max_seq_len, scale, stream);
+}
+
 int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_pairs,
                int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                int32_t dtype, void *stream) {
   if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
     return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!storage_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
@@ -291,7 +393,7 @@ int swap_blocks(bool out, void *k_cache, void *v_cache, const int64_t *block_ids
                 int32_t block_size, int32_t head_dim, int32_t dtype, void *stream) {
   if (num_ids < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
     return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!storage_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
   if (block_bytes / 16 > 0x7fffffff) return PA_ERR_UNSUPPORTED;

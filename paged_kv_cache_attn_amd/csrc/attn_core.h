@@ -106,6 +106,80 @@ __device__ __forceinline__ void load_kv_tile_rows(KVTile &t, const uint16_t *kc,
   for (int v = 0; v < 4; ++v) t.v[v] = ld16(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
 }
 
+// -- FP8 (E4M3) tiles ------------------------------------------------------------
+// A tile as loaded from an FP8 cache (rows of 128 bytes): lane (r, c) holds
+// K[token c][bytes 16r .. 16r+15] and [64+16r .. 64+16r+15] (two 16-byte
+// loads; each instruction reads 64 contiguous bytes of all 16 rows), and
+// V[token 4r+v][dims 8c .. 8c+7] (8-byte loads, whole rows per instruction).
+// expand() turns it into the bf16 tile the MFMA step takes, exactly.  The K
+// dims a lane holds are a permutation of the bf16 tile's (chunk i covers
+// dims 64(i/2) + 16r + 8(i%2) .. +7); the QK product sums over all dims, so
+// the q operand is loaded with the same permutation (load_q_operand_fp8k).
+struct KVTile8 {
+  u32x4 k[2];
+  u32x2 v[4];
+};
+
+__device__ __forceinline__ void load_kv_tile_rows_fp8(KVTile8 &t, const uint8_t *kc, const uint8_t *vc,
+                                                      const TileRows &tr, int r, int c) {
+  const int64_t kr = (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128 + 16 * r;
+  t.k[0] = ld16(kc + kr);
+  t.k[1] = ld16(kc + kr + 64);
+  const int64_t vr = r < 2 ? tr.lo : tr.hi;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) t.v[v] = ld8(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+}
+
+__device__ __forceinline__ KVTile expand_fp8_tile(const KVTile8 &s) {
+  KVTile t;
+  t.k[0] = fp8x8_to_bf16x8(s.k[0][0], s.k[0][1]);
+  t.k[1] = fp8x8_to_bf16x8(s.k[0][2], s.k[0][3]);
+  t.k[2] = fp8x8_to_bf16x8(s.k[1][0], s.k[1][1]);
+  t.k[3] = fp8x8_to_bf16x8(s.k[1][2], s.k[1][3]);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) t.v[v] = fp8x8_to_bf16x8(s.v[v][0], s.v[v][1]);
+  return t;
+}
+
+// The q operand in the FP8 tile's K-dim order (nullptr -> zeros).
+__device__ __forceinline__ void load_q_operand_fp8k(bf16x8 qb[4], const uint16_t *qrow, int r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 v = qrow ? ld16(qrow + 64 * (i >> 1) + 16 * r + 8 * (i & 1)) : u32x4{0u, 0u, 0u, 0u};
+    qb[i] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// The two cache formats the decode kernels take, behind one interface:
+// Raw is the tile as loaded (and carried through the prefetch ring), expand()
+// the bf16 tile the step multiplies.
+template <bool kFp8>
+struct KVFormat;
+template <>
+struct KVFormat<false> {
+  using Elem = uint16_t;
+  using Raw = KVTile;
+  static __device__ __forceinline__ void load(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
+                                              int c) {
+    load_kv_tile_rows(t, kc, vc, tr, r, c);
+  }
+  static __device__ __forceinline__ KVTile expand(const Raw &t) { return t; }
+  static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r);
+};
+template <>
+struct KVFormat<true> {
+  using Elem = uint8_t;
+  using Raw = KVTile8;
+  static __device__ __forceinline__ void load(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
+                                              int c) {
+    load_kv_tile_rows_fp8(t, kc, vc, tr, r, c);
+  }
+  static __device__ __forceinline__ KVTile expand(const Raw &t) { return expand_fp8_tile(t); }
+  static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r) {
+    load_q_operand_fp8k(qb, qrow, r);
+  }
+};
+
 // Q^T operand for column c from a query row of 128 bf16 (nullptr -> zeros).
 __device__ __forceinline__ void load_q_operand_d128(bf16x8 qb[4], const uint16_t *qrow, int r) {
 #pragma unroll
@@ -113,6 +187,10 @@ __device__ __forceinline__ void load_q_operand_d128(bf16x8 qb[4], const uint16_t
     u32x4 v = qrow ? ld16(qrow + 32 * i + 8 * r) : u32x4{0u, 0u, 0u, 0u};
     qb[i] = __builtin_bit_cast(bf16x8, v);
   }
+}
+
+__device__ __forceinline__ void KVFormat<false>::load_q(bf16x8 qb[4], const uint16_t *qrow, int r) {
+  load_q_operand_d128(qb, qrow, r);
 }
 
 struct MfmaAttnState {

@@ -41,14 +41,18 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 }
 
 // ----------------------------------------------------------------------------
-// MFMA kernel: bf16 KV, head_dim 128, block size 8, 16, 32, 64 or 128
-// (walked in 16-token tiles), g <= 16.
+// MFMA kernel: bf16 (or FP8 E4M3, FP8) KV with bf16 q, head_dim 128, block
+// size 8, 16, 32, 64 or 128 (walked in 16-token tiles), g <= 16.
 // Lane (r, c) = (lane >> 4, lane & 15); column c is query head kh*g + c.
 // The block size BSZ is a template argument so the table walk folds to
-// constants for each supported size.
+// constants for each supported size.  FP8 tiles travel through the pipeline
+// as loaded (half the registers) and are expanded to bf16 just before their
+// step; k_scale is folded into the score scale and v_scale into the final
+// normalisation.
 // ----------------------------------------------------------------------------
-template <int NW, int BSZ>
+template <int NW, int BSZ, bool FP8>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams p) {
+  using F = KVFormat<FP8>;
   constexpr int D = 128;
   constexpr int BS = 16;
   const int part = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
@@ -66,16 +70,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
   const bool col_ok = c < g;
 
   bf16x8 qb[4];
-  load_q_operand_d128(qb,
-                      col_ok ? reinterpret_cast<const uint16_t *>(p.q) +
-                                   ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * D
-                             : nullptr,
-                      r);
+  F::load_q(qb,
+            col_ok ? reinterpret_cast<const uint16_t *>(p.q) + ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * D
+                   : nullptr,
+            r);
 
-  const float sl2 = p.scale * kLog2e;
+  const float sl2 = p.scale * p.k_scale * kLog2e;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
-  const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+  const typename F::Elem *kc = reinterpret_cast<const typename F::Elem *>(p.k_cache);
+  const typename F::Elem *vc = reinterpret_cast<const typename F::Elem *>(p.v_cache);
   const int nblk_tab = (L + BSZ - 1) / BSZ;
   const TileMap map(BSZ, p.num_kv_heads, p.num_blocks);
 
@@ -84,32 +87,32 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
 
   // 16-token tile j (any supported block size).  An out-of-range table entry
   // is never dereferenced: the tile is read from block 0 and fully masked.
-  auto load = [&](int j, KVTile &t, int &lim) {
+  auto load = [&](int j, typename F::Raw &t, int &lim) {
     int e0, e1;
     const bool ok = map.entries(table, j, nblk_tab, e0, e1);
     lim = ok ? L : 0;
-    load_kv_tile_rows(t, kc, vc, map.rows(e0, e1, kh), r, c);
+    F::load(t, kc, vc, map.rows(e0, e1, kh), r, c);
   };
 
   // Two-deep software pipeline: the next tile's loads are in flight while
   // the current one is multiplied.
   int j = j0 + w;
   if (j < j1) {
-    KVTile cur;
+    typename F::Raw cur;
     int lim;
     load(j, cur, lim);
     while (true) {
       const int jn = j + NW;
       if (jn < j1) {
-        KVTile nxt;
+        typename F::Raw nxt;
         int limn;
         load(jn, nxt, limn);
-        st.step(qb, cur, j * BS, lim, sl2, r);
+        st.step(qb, F::expand(cur), j * BS, lim, sl2, r);
         cur = nxt;
         lim = limn;
         j = jn;
       } else {
-        st.step(qb, cur, j * BS, lim, sl2, r);
+        st.step(qb, F::expand(cur), j * BS, lim, sl2, r);
         break;
       }
     }
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
   if (NW == 1) {
     if (!col_ok) return;
     if (nparts == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float inv = l > 0.f ? p.v_scale / l : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
     }
     const int64_t rr = (int64_t)b * p.num_heads + (int64_t)kh * g + cc;
     if (nparts == 1) {
-      store_out(p.out, p.out_bf16, rr * D + d, lsum > 0.f ? o / lsum : 0.f);
+      store_out(p.out, p.out_bf16, rr * D + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
     } else {
       p.ws_o[(rr * p.nparts_max + part) * D + d] = o;
       if (d == 0) {
@@ -322,7 +325,8 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int d = tid + u * 128;
-    if (d < p.head_dim) store_out(p.out, p.out_bf16, row * p.head_dim + d, lsum > 0.f ? acc[u] / lsum : 0.f);
+    if (d < p.head_dim)
+      store_out(p.out, p.out_bf16, row * p.head_dim + d, lsum > 0.f ? acc[u] * p.v_scale / lsum : 0.f);
   }
 }
 
@@ -342,17 +346,27 @@ size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int npa
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
-  const bool mfma = p.kv_bf16 && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16;
+  const bool mfma = (p.kv_bf16 || p.kv_fp8) && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16;
   if (p.num_seqs == 0) return hipSuccess;
   if (mfma) {
     const dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs), block(64 * PA_DECODE_WAVES);
     constexpr int NW = PA_DECODE_WAVES;
-    switch (p.block_size) {
-      case 8: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 8>), grid, block, 0, stream, p); break;
-      case 16: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 16>), grid, block, 0, stream, p); break;
-      case 32: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 32>), grid, block, 0, stream, p); break;
-      case 64: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 64>), grid, block, 0, stream, p); break;
-      default: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 128>), grid, block, 0, stream, p); break;
+    if (p.kv_fp8) {
+      switch (p.block_size) {
+        case 8: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 8, true>), grid, block, 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 16, true>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 32, true>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 64, true>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 128, true>), grid, block, 0, stream, p); break;
+      }
+    } else {
+      switch (p.block_size) {
+        case 8: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 8, false>), grid, block, 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 16, false>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 32, false>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 64, false>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_mfma_d128_kernel<NW, 128, false>), grid, block, 0, stream, p); break;
+      }
     }
   } else {
     dim3 grid(p.nparts_max, p.num_heads, p.num_seqs);

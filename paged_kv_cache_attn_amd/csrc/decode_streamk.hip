@@ -61,9 +61,14 @@ __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, 
 // of a wave's share are parked in LDS and combined, in wave order, once all
 // waves are done.  So no barrier interrupts the stream, and runs of short
 // rows are spread evenly over the waves.
-template <int NW>
+//
+// FP8 (E4M3) caches: the ring carries the tiles as loaded (16 instead of 32
+// registers each), expanded to bf16 just before their step; k_scale is
+// folded into the score scale, v_scale into the final normalisation.
+template <int NW, bool FP8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
     DecodeParams p) {
+  using F = KVFormat<FP8>;
   __shared__ int s_pref[kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int ls = (int)((int64_t)(e - s) * w / NW);
   const int le = (int)((int64_t)(e - s) * (w + 1) / NW);
 
-  const float sl2 = p.scale * kLog2e;
-  const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
-  const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+  const float sl2 = p.scale * p.k_scale * kLog2e;
+  const typename F::Elem *kc = reinterpret_cast<const typename F::Elem *>(p.k_cache);
+  const typename F::Elem *vc = reinterpret_cast<const typename F::Elem *>(p.v_cache);
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(p.q);
   const bool col_ok = c < g;
   const int c_ld = c < g ? c : g - 1;  // idle columns read a valid row, never stored
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // the same prefetch distance.  An out-of-range table entry is never
   // dereferenced: the tile is read from block 0 and fully masked.
   struct Slot {
-    KVTile t;
+    typename F::Raw t;
     bf16x8 q[4];
     int lim;
   };
@@ -207,8 +212,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool ok = u.x >= 0;
     sl.lim = ok ? s_len[b] : 0;
     // a masked tile reads the first rows of the cache
-    load_kv_tile_rows(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
-    load_q_operand_d128(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
+    F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
+    F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
   };
 
   if (ls < le) {
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const bool whole = seg_j0 == 0 && s_pj[li] == nb - 1;
       if (whole) {
         if (col_ok) {
-          const float inv = lw > 0.f ? 1.f / lw : 0.f;
+          const float inv = lw > 0.f ? p.v_scale / lw : 0.f;
           const int64_t orow = ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * kD;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -267,13 +272,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     load_slot(ls + 1, sb);
     for (int li = ls;;) {
       load_slot(li + 2, sc);
-      st.step(sa.q, sa.t, s_pj[li] * kBS, sa.lim, sl2, r);
+      st.step(sa.q, F::expand(sa.t), s_pj[li] * kBS, sa.lim, sl2, r);
       if (!after_step(li++)) break;
       load_slot(li + 2, sa);
-      st.step(sb.q, sb.t, s_pj[li] * kBS, sb.lim, sl2, r);
+      st.step(sb.q, F::expand(sb.t), s_pj[li] * kBS, sb.lim, sl2, r);
       if (!after_step(li++)) break;
       load_slot(li + 2, sb);
-      st.step(sc.q, sc.t, s_pj[li] * kBS, sc.lim, sl2, r);
+      st.step(sc.q, F::expand(sc.t), s_pj[li] * kBS, sc.lim, sl2, r);
       if (!after_step(li++)) break;
     }
   }
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         o += ov[i] * wgt;
       }
       if (whole) {
-        store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o / lsum : 0.f);
+        store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
       } else {
         const int64_t base = ((int64_t)gi * 2 + slot) * g + cc;
         p.sk_part[base * kD + d] = o;
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
       const float w0 = fast_exp2(m0 - Mu), w1 = fast_exp2(m1 - Mu);
       const float ls = sl[f][u] * w0 + sl[2][u] * w1;
       const float o = so[f][u] * w0 + so[2][u] * w1;
-      store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? o / ls : 0.f);
+      store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? o * p.v_scale / ls : 0.f);
     }
     return;
   }
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
       }
       M = Mb;
     }
-    store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o / lsum : 0.f);
+    store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
   }
 }
 
@@ -435,8 +440,12 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
   const size_t park = (size_t)PA_DECODE_WAVES * 2 * g * (kD + 2) * sizeof(float);
-  hipLaunchKernelGGL(decode_streamk_kernel<PA_DECODE_WAVES>, dim3(p.sk_ranges), dim3(64 * PA_DECODE_WAVES),
-                     park, stream, p);
+  if (p.kv_fp8)
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, true>), dim3(p.sk_ranges),
+                       dim3(64 * PA_DECODE_WAVES), park, stream, p);
+  else
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false>), dim3(p.sk_ranges),
+                       dim3(64 * PA_DECODE_WAVES), park, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);

@@ -52,6 +52,88 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   st16(v_cache + dst, vv);
 }
 
+// Quantising write into FP8 E4M3 caches (Lecture 7 §10: KV stored in 8 bits
+// halves its memory and bandwidth).  One thread per 16 codes (16 bytes) of
+// one (token, head) row, K and V: the 16 source values (bf16 or fp32) are
+// loaded with the slot, divided by the tensor's scale (IEEE fp32 division,
+// round to nearest) and rounded to the nearest code with ties to even,
+// saturating at +-448.  row_chunks = head_dim / 16.
+template <typename I, bool SRC_BF16>
+__global__ __launch_bounds__(256) void kv_cache_write_fp8_kernel(
+    const uint8_t *__restrict__ key, const uint8_t *__restrict__ value, uint8_t *__restrict__ k_cache,
+    uint8_t *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, I total_chunks, int num_kv_heads,
+    int block_size, int row_chunks, int64_t num_slots, float k_scale, float v_scale) {
+  constexpr int kSrcLoads = SRC_BF16 ? 2 : 4;  // 16-byte loads for 16 source values
+  const I gid = (I)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const I chunk = gid % (I)row_chunks;
+  const I row = gid / (I)row_chunks;  // t * num_kv_heads + h
+  const I h = row % (I)num_kv_heads;
+  const I t = row / (I)num_kv_heads;
+  const int64_t src = ((int64_t)row * row_chunks + chunk) * 16 * (SRC_BF16 ? 2 : 4);
+  u32x4 ks[kSrcLoads], vs[kSrcLoads];
+#pragma unroll
+  for (int i = 0; i < kSrcLoads; ++i) {
+    ks[i] = ld16(key + src + 16 * i);
+    vs[i] = ld16(value + src + 16 * i);
+  }
+  const int64_t slot = slot_mapping[t];
+  asm volatile("" ::"v"(ks[0]), "v"(vs[0]), "v"(slot));
+  if (slot < 0 || slot >= num_slots) return;
+  // source value j (0..15) of a row piece
+  auto val = [&](const u32x4 *s, int j) -> float {
+    if (SRC_BF16) {
+      const uint32_t w = s[j >> 3][(j >> 1) & 3];
+      return bf16_bits_to_float((j & 1) ? w >> 16 : w & 0xffffu);
+    }
+    return __uint_as_float(s[j >> 2][j & 3]);
+  };
+  u32x4 kq, vq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kq[i] = pack_fp8x4(__fdiv_rn(val(ks, 4 * i), k_scale), __fdiv_rn(val(ks, 4 * i + 1), k_scale),
+                       __fdiv_rn(val(ks, 4 * i + 2), k_scale), __fdiv_rn(val(ks, 4 * i + 3), k_scale));
+    vq[i] = pack_fp8x4(__fdiv_rn(val(vs, 4 * i), v_scale), __fdiv_rn(val(vs, 4 * i + 1), v_scale),
+                       __fdiv_rn(val(vs, 4 * i + 2), v_scale), __fdiv_rn(val(vs, 4 * i + 3), v_scale));
+  }
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot - blk * block_size);
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * (int64_t)row_chunks * 16 + (int64_t)chunk * 16;
+  st16(k_cache + dst, kq);
+  st16(v_cache + dst, vq);
+}
+
+hipError_t launch_kv_cache_write_fp8(const void *key, const void *value, int src_bf16, void *k_cache,
+                                     void *v_cache, const int64_t *slot_mapping, int num_tokens,
+                                     int num_blocks, int num_kv_heads, int block_size, int head_dim,
+                                     float k_scale, float v_scale, hipStream_t stream) {
+  const int row_chunks = head_dim / 16;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * row_chunks;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const uint8_t *k8 = (const uint8_t *)key, *v8 = (const uint8_t *)value;
+  uint8_t *kc = (uint8_t *)k_cache, *vc = (uint8_t *)v_cache;
+  const bool narrow = total < INT32_MAX && num_slots < INT32_MAX;
+  if (narrow && src_bf16)
+    hipLaunchKernelGGL((kv_cache_write_fp8_kernel<uint32_t, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       k8, v8, kc, vc, slot_mapping, (uint32_t)total, num_kv_heads, block_size, row_chunks,
+                       num_slots, k_scale, v_scale);
+  else if (narrow)
+    hipLaunchKernelGGL((kv_cache_write_fp8_kernel<uint32_t, false>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       k8, v8, kc, vc, slot_mapping, (uint32_t)total, num_kv_heads, block_size, row_chunks,
+                       num_slots, k_scale, v_scale);
+  else if (src_bf16)
+    hipLaunchKernelGGL((kv_cache_write_fp8_kernel<int64_t, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       k8, v8, kc, vc, slot_mapping, total, num_kv_heads, block_size, row_chunks, num_slots,
+                       k_scale, v_scale);
+  else
+    hipLaunchKernelGGL((kv_cache_write_fp8_kernel<int64_t, false>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       k8, v8, kc, vc, slot_mapping, total, num_kv_heads, block_size, row_chunks, num_slots,
+                       k_scale, v_scale);
+  return hipGetLastError();
+}
+
 // grid.x = pair, grid.y = 0 (K) / 1 (V); each workgroup copies one block of
 // one cache: block_chunks 16-byte chunks, strided over 256 threads.
 __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t *__restrict__ k_cache,

@@ -109,6 +109,28 @@ __device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
 
 // 16-byte global load/store through a plain vector type (global_load_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+
+// -- FP8 E4M3 (OCP: bias 7, no infinities, S.1111.111 = NaN, max 448) ------
+// Two codes (bytes 0-1 of w, or bytes 2-3 with kHigh) to two bf16, exactly:
+// every E4M3 value is a bf16 value (v_cvt_scalef32_pk_bf16_fp8, scale 1).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+// Eight codes (two dwords) to eight bf16 (four dwords), in order.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t a, uint32_t b) {
+  return u32x4{fp8x2_to_bf16x2<false>(a), fp8x2_to_bf16x2<true>(a), fp8x2_to_bf16x2<false>(b),
+               fp8x2_to_bf16x2<true>(b)};
+}
+// fp32 -> code, nearest with ties to even and saturation at +-448: the clamp
+// supplies the saturation (v_cvt_pk_fp8_f32 rounds to nearest-even and turns
+// magnitudes of 464 and up into NaN).  NaN inputs give an unspecified code.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  auto sat = [](float x) { return fminf(fmaxf(x, -448.f), 448.f); };
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+}
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // Select halves of two packed-bf16 dwords: lo16(a) | lo16(b) << 16 and

@@ -32,6 +32,11 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cac
                                  const int64_t *slot_mapping, int num_tokens, int num_blocks,
                                  int num_kv_heads, int block_size, int head_dim, int elem_bytes,
                                  hipStream_t stream);
+// Quantising write into FP8 E4M3 caches; src_bf16: key/value are bf16 (else fp32).
+hipError_t launch_kv_cache_write_fp8(const void *key, const void *value, int src_bf16, void *k_cache,
+                                     void *v_cache, const int64_t *slot_mapping, int num_tokens,
+                                     int num_blocks, int num_kv_heads, int block_size, int head_dim,
+                                     float k_scale, float v_scale, hipStream_t stream);
 
 // gather (true): ids[0..n) of the K and V caches -> staging [n][2][block];
 // scatter (false): the reverse.  block_chunks = 16-byte chunks per block.
@@ -48,7 +53,9 @@ struct DecodeParams {
   const void *q;           // [B][Hq][D]
   const void *k_cache;     // [NB][Hkv][bs][D]
   const void *v_cache;
-  int kv_bf16;             // 0: fp32 KV, 1: bf16 KV
+  int kv_bf16;             // 0: fp32 KV, 1: bf16 KV (q has the KV dtype)
+  int kv_fp8;              // 1: FP8 E4M3 KV codes with bf16 q (kv_bf16 is then 0)
+  float k_scale, v_scale;  // FP8: K = value(code) * k_scale, V likewise; 1 otherwise
   const int32_t *block_tables;
   int max_blocks_per_seq;
   const int32_t *seq_lens;
@@ -85,6 +92,8 @@ struct PrefillParams {
   const void *k_cache;
   const void *v_cache;
   int kv_bf16;
+  int kv_fp8;              // as in DecodeParams
+  float k_scale, v_scale;
   const int32_t *block_tables;
   int max_blocks_per_seq;
   const int32_t *query_start_loc;  // [B+1]

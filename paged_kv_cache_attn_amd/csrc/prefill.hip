@@ -68,14 +68,23 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // every barrier.  grid = ntiles * Hkv * B workgroups, ntiles =
 // ceil(max_query_len / (NW * CG * 16 / g)).  The block size BSZ is a template
 // argument so the table walk folds to constants for each supported size.
-template <int NW, int CG, int BSZ>
+//
+// FP8 (E4M3) caches: a pair is 512 16-byte chunks in HBM instead of 1024;
+// each chunk is expanded to bf16 (exactly) on its way into LDS, so the LDS
+// layout and everything after it are those of the bf16 cache.  k_scale is
+// folded into the score scale and v_scale into the final normalisation.
+template <int NW, int CG, int BSZ, bool FP8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_d128_kernel(
     PrefillParams p, int ntiles) {
+  using Elem = typename KVFormat<FP8>::Elem;
   constexpr int D = 128;
   constexpr int BS = 16;
-  constexpr int kTile = 4096;            // bytes of one K or V tile
+  constexpr int kTile = 4096;            // bytes of one K or V tile in LDS (bf16)
   constexpr int kStage = 4 * kTile;      // K_a, V_a, K_b, V_b
-  constexpr int kChunksPerThread = 4 * 256 / (64 * NW);
+  constexpr int kTileShift = FP8 ? 7 : 8;
+  constexpr int kTileChunks = 1 << kTileShift;      // 16-byte chunks of one tile in HBM
+  constexpr int kChunkElems = FP8 ? 16 : 8;         // elements per chunk
+  constexpr int kChunksPerThread = 4 * kTileChunks / (64 * NW);
   __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
 
   const unsigned item = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -123,16 +132,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                         r);
   }
 
-  const float sl2 = p.scale * kLog2e;
+  const float sl2 = p.scale * p.k_scale * kLog2e;
   const __attribute__((address_space(4))) int32_t *table =
       (const __attribute__((address_space(4))) int32_t *)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
-  const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
-  const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+  const Elem *kc = reinterpret_cast<const Elem *>(p.k_cache);
+  const Elem *vc = reinterpret_cast<const Elem *>(p.v_cache);
   const TileMap map(BSZ, p.num_kv_heads, p.num_blocks);
   const int nblk_tab = (S + BSZ - 1) / BSZ;  // table entries the sequence uses
 
-  // Cooperative pair load: the 1024 16-byte chunks of a pair of 16-token
-  // tiles, consecutive threads on consecutive chunks of a tile.  Returns
+  // Cooperative pair load: the 4 * kTileChunks 16-byte chunks of a pair of
+  // 16-token tiles, consecutive threads on consecutive chunks of a tile.  Returns
   // which of the two tiles hold real data (bit 0: A, bit 1: B); tile
   // j >= nblk (the odd tail) and a tile with an out-of-range table entry are
   // read from block 0 and masked later.  Which tile, K or V, and which half
@@ -149,23 +158,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int k = 0; k < kChunksPerThread; ++k) {
       const int uw = w * 64 + k * 64 * NW;  // first chunk of the wave (a multiple of 64)
-      const int kind = uw >> 8;             // 0 K_a, 1 V_a, 2 K_b, 3 V_b
+      const int kind = uw >> kTileShift;    // 0 K_a, 1 V_a, 2 K_b, 3 V_b
       const TileRows &tr = kind < 2 ? ra : rb;
-      // rows 8-15 start 8 rows after their own base: rebase so chunk q sits at q * 8
-      const int64_t base = (uw & 128) == 0 ? tr.lo : tr.hi - 8 * D;
-      regs[k] = ld16(((kind & 1) ? vc : kc) + base + ((uw & 255) + lane) * 8);
+      // rows 8-15 start 8 rows after their own base: rebase so chunk q sits at q * kChunkElems
+      const int64_t base = (uw & (kTileChunks / 2)) == 0 ? tr.lo : tr.hi - 8 * D;
+      regs[k] = ld16(((kind & 1) ? vc : kc) + base + ((uw & (kTileChunks - 1)) + lane) * kChunkElems);
     }
     return (int)oka | ((int)okb << 1);
+  };
+  // LDS byte offset of bf16 chunk kc (0..15) of row t in a K or a V tile
+  auto lds_off = [](bool is_v, int t, int kc) -> int {
+    return is_v ? t * 256 + ((((kc >> 1) ^ (t & 7)) << 5) | ((kc & 1) << 4)) : (t * 16 + (kc ^ t)) << 4;
   };
   auto lstore = [&](int stage, const u32x4 *regs) {
 #pragma unroll
     for (int k = 0; k < kChunksPerThread; ++k) {
       const int u = tid + k * 64 * NW;
-      const int kind = u >> 8, q = u & 255;
-      const int t = q >> 4, kc = q & 15;
-      const int off = (kind & 1) ? t * 256 + ((((kc >> 1) ^ (t & 7)) << 5) | ((kc & 1) << 4))
-                                 : (t * 16 + (kc ^ t)) << 4;
-      *reinterpret_cast<u32x4 *>(lds + stage * kStage + kind * kTile + off) = regs[k];
+      const int kind = u >> kTileShift, q = u & (kTileChunks - 1);
+      uint8_t *tb = lds + stage * kStage + kind * kTile;
+      if (FP8) {
+        // 16 codes = bf16 chunks 2 kc8 and 2 kc8 + 1 of row t
+        const int t = q >> 3, kc8 = q & 7;
+        *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, t, 2 * kc8)) = fp8x8_to_bf16x8(regs[k][0], regs[k][1]);
+        *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, t, 2 * kc8 + 1)) =
+            fp8x8_to_bf16x8(regs[k][2], regs[k][3]);
+      } else {
+        *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, q >> 4, q & 15)) = regs[k];
+      }
     }
   };
   // V^T operand address of this lane inside a V tile for dim tile dt: lane
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     const float l = row_sum4(st[cg].l);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? p.v_scale / l : 0.f;
     const int qi = tile * tpg + w * tpw + cg * tpgrp + ti;
     const int64_t row = ((int64_t)q0 + qi) * p.num_heads + (int64_t)kh * g + hh;
     if (!col_ok[cg]) continue;
@@ -319,7 +338,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_query_len == 0) return hipSuccess;
   const int g = p.num_heads / p.num_kv_heads;
-  const bool mfma = p.kv_bf16 && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16 && (16 % g) == 0;
+  const bool mfma =
+      (p.kv_bf16 || p.kv_fp8) && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16 && (16 % g) == 0;
   if (mfma) {
     constexpr int NW = PA_PREFILL_WAVES, CG = PA_PREFILL_GROUPS;
     const int tpg = NW * CG * (16 / g);
@@ -327,13 +347,26 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const int64_t items = ntiles * p.num_kv_heads * p.num_seqs;
     if (items * 64 * NW > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)items), block(64 * NW);
-    switch (p.block_size) {
-      case 8: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 8>), grid, block, 0, stream, p, (int)ntiles); break;
-      case 16: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 16>), grid, block, 0, stream, p, (int)ntiles); break;
-      case 32: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 32>), grid, block, 0, stream, p, (int)ntiles); break;
-      case 64: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 64>), grid, block, 0, stream, p, (int)ntiles); break;
-      default: hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, 128>), grid, block, 0, stream, p, (int)ntiles); break;
+#define PA_PREFILL_LAUNCH(BSZ, FP8)                                                                   \
+  hipLaunchKernelGGL((prefill_mfma_d128_kernel<NW, CG, BSZ, FP8>), grid, block, 0, stream, p, (int)ntiles)
+    if (p.kv_fp8) {
+      switch (p.block_size) {
+        case 8: PA_PREFILL_LAUNCH(8, true); break;
+        case 16: PA_PREFILL_LAUNCH(16, true); break;
+        case 32: PA_PREFILL_LAUNCH(32, true); break;
+        case 64: PA_PREFILL_LAUNCH(64, true); break;
+        default: PA_PREFILL_LAUNCH(128, true); break;
+      }
+    } else {
+      switch (p.block_size) {
+        case 8: PA_PREFILL_LAUNCH(8, false); break;
+        case 16: PA_PREFILL_LAUNCH(16, false); break;
+        case 32: PA_PREFILL_LAUNCH(32, false); break;
+        case 64: PA_PREFILL_LAUNCH(64, false); break;
+        default: PA_PREFILL_LAUNCH(128, false); break;
+      }
     }
+#undef PA_PREFILL_LAUNCH
   } else {
     dim3 grid(p.max_query_len, p.num_heads, p.num_seqs);
     if (p.head_dim == 64) {

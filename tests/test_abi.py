@@ -177,6 +177,45 @@ def test_swap_validation(pa):
         assert f(N, N, N, 0, N, N, 0, 64, 8, 16, 128, 1, N) == PA_OK
 
 
+def test_fp8_validation(pa):
+    f = pa.lib.kv_cache_write_fp8
+    # key, value, src_dtype, k, v, slots, T, NB, Hkv, bs, D, ks, vs, stream
+    args = [P, P, 1, P, P, P, 4, 64, 8, 16, 128, 0.5, 0.5, N]
+    assert f(*args[:6], -1, *args[7:]) == PA_ERR_SHAPE
+    assert f(*args[:11], 0.0, 0.5, N) == PA_ERR_SHAPE
+    assert f(*args[:11], 0.5, float("nan"), N) == PA_ERR_SHAPE
+    assert f(*args[:11], float("inf"), 0.5, N) == PA_ERR_SHAPE
+    assert f(P, P, 2, *args[3:]) == PA_ERR_UNSUPPORTED          # the source must be fp32 or bf16
+    assert f(*args[:10], 40, 0.5, 0.5, N) == PA_ERR_UNSUPPORTED  # head_dim not a multiple of 16
+    assert f(N, *args[1:]) == PA_ERR_NULL
+    assert f(N, N, 1, N, N, N, 0, 64, 8, 16, 128, 0.5, 0.5, N) == PA_OK
+    d = pa.lib.paged_attn_decode_fp8
+    # out, out_dtype, q, k, v, ks, vs, bt, maxblk, sl, B, Hq, Hkv, D, bs, NB, max_len, scale, part, ws, wsb, stream
+    base = [P, 0, P, P, P, 0.5, 0.5, P, 16, P, 4, 32, 8, 128, 16, 64, 256, 0.1, 64, N, 0, N]
+    def dec(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return d(*a)
+    assert dec(a5=-1.0) == PA_ERR_SHAPE
+    assert dec(a13=64) == PA_ERR_UNSUPPORTED                  # FP8 serves head_dim 128 only
+    assert dec(a14=4) == PA_ERR_UNSUPPORTED                   # and the MFMA block sizes
+    assert dec(a11=136, a12=8) == PA_ERR_UNSUPPORTED          # and groups of at most 16
+    assert dec(a1=2) == PA_ERR_UNSUPPORTED                    # out cannot be FP8
+    assert dec(a2=N) == PA_ERR_NULL
+    assert dec(a10=0) == PA_OK
+    pf = pa.lib.paged_attn_prefill_chunk_fp8
+    # out, out_dtype, q, k, v, ks, vs, bt, maxblk, qsl, sl, B, Tq, Hq, Hkv, D, bs, NB, maxq, maxlen, scale, stream
+    pbase = [P, 0, P, P, P, 0.5, 0.5, P, 16, P, P, 4, 8, 24, 8, 128, 16, 64, 4, 256, 0.1, N]
+    assert pf(*pbase) == PA_ERR_UNSUPPORTED                   # group 3 does not divide 16
+    pbase[13] = 32
+    assert pf(*pbase[:6], 0.0, *pbase[7:]) == PA_ERR_SHAPE
+    assert pf(*pbase[:11], 0, *pbase[12:]) == PA_OK
+    # the plain calls refuse the FP8 code for their KV
+    assert pa.lib.paged_attn_decode(P, 0, P, P, P, 2, P, 16, P, 4, 32, 8, 128, 16, 64, 256, 0.1, 64, N, 0, N) \
+        == PA_ERR_UNSUPPORTED
+
+
 def test_binding_refuses_cpu_tensors(pa):
     import torch
     k = torch.zeros(4, 2, 16, 64)
