@@ -78,10 +78,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
-                    choices=["llama8b_decode", "llama70b_long", "shared_prefix", "shared_prefix_cow",
+                    choices=["llama8b_decode", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
+                             "chunked_prefill_fp8", "shared_prefix", "shared_prefix_cow",
                              "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
                              "copy_calibration"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="cache block size of the decode and prefill workloads (the headline runs use 16)")
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -216,7 +219,7 @@ def time_layers(args, torch, layers, write, call, out):
     return ms_step, ms_call, wall, "hip-graph"
 
 
-def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s):
+def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s, kv_scales=(None, None)):
     """Time the oracle over whole passes of the batch (all sequences, one layer) on all host cores."""
     import oracle
     oracle.build(force=False)
@@ -224,7 +227,8 @@ def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s):
     B = q.shape[0]
 
     def one(b):
-        return oracle.paged_decode(q[b:b + 1], k, v, tables[b:b + 1], lens[b:b + 1], scale)
+        return oracle.paged_decode(q[b:b + 1], k, v, tables[b:b + 1], lens[b:b + 1], scale,
+                                   k_scale=kv_scales[0], v_scale=kv_scales[1])
 
     outs = None
     passes = 0
@@ -242,15 +246,31 @@ def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s):
     return outs, passes, time.perf_counter() - t0, cores
 
 
-def bench_decode(args, torch, pa, W, w, layers, partition):
+def fp8_pool(torch, W, shape, std, seed):
+    """An FP8 E4M3 layer pool: N(0, std) values quantised with the per-tensor scale
+    max|x| / 448 (torch's float8 conversion; input preparation only)."""
+    x = W.device_values(shape, std, seed, "f32")
+    s = float(x.abs().max()) / 448.0
+    codes = (x / s).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    del x
+    return codes, s
+
+
+def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
     dev = "cuda"
     B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
     lens = w.layout.seq_lens
     max_len = int(lens.max())
     shape = w.cache_shape()
     # per-layer pools, drawn on the device
-    K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
-    V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+    if fp8:
+        KS = [fp8_pool(torch, W, shape, w.std, w.seed * 1000 + 2 * l) for l in range(layers)]
+        VS = [fp8_pool(torch, W, shape, w.std, w.seed * 1000 + 2 * l + 1) for l in range(layers)]
+        K, ks = [a for a, _ in KS], [s for _, s in KS]
+        V, vs = [a for a, _ in VS], [s for _, s in VS]
+    else:
+        K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+        V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
     q = W.device_values((B, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
     newk = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
     newv = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
@@ -263,19 +283,30 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     scale = w.scale
 
-    ms_step, ms_decode, wall, mode = time_layers(
-        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
-        lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws), out)
+    if fp8:
+        write = lambda l: pa.kv_cache_write_fp8(newk, newv, K[l], V[l], slots, ks[l], vs[l])
+        call = lambda l: pa.paged_attn_decode_fp8(out, q, K[l], V[l], ks[l], vs[l], bt, sl, scale, max_len,
+                                                  partition, ws)
+    else:
+        write = lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+        call = lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws)
+    ms_step, ms_decode, wall, mode = time_layers(args, torch, layers, write, call, out)
     copy_gbs = measured_copy_gbs(torch)
-    dec_bytes = w.algorithmic_bytes(out_bytes=4)
-    write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
+    if fp8:
+        # 1-byte K/V rows, bf16 q, fp32 out, table entries, lengths
+        nblk = (lens.astype(np.int64) + w.block_size - 1) // w.block_size
+        dec_bytes = int(lens.astype(np.int64).sum()) * Hkv * D * 2 + B * Hq * D * (2 + 4) + 4 * int(nblk.sum()) + 4 * B
+        write_bytes = B * Hkv * D * (2 + 1) * 2 + 8 * B
+    else:
+        dec_bytes = w.algorithmic_bytes(out_bytes=4)
+        write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
     step_bytes = layers * (dec_bytes + write_bytes)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_bytes / (ms_decode * 1e-3) / 1e9
 
     # sampled parity + CPU baseline on layer 0 (the oracle on the host copies)
     torch.cuda.synchronize()
-    pa.paged_attn_decode(out, q, K[0], V[0], bt, sl, scale, max_len, partition, ws)
+    call(0)
     torch.cuda.synchronize()
     gpu_out = out.double().cpu().numpy()
 
@@ -287,7 +318,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     parity = None
     if not args.no_cpu_baseline:
         ref, passes, secs, cores = cpu_oracle_decode(host(q), host(K[0]), host(V[0]), w.layout.block_tables,
-                                                     lens, scale, args.cpu_seconds)
+                                                     lens, scale, args.cpu_seconds,
+                                                     (ks[0], vs[0]) if fp8 else (None, None))
         parity = float(np.max(np.abs(gpu_out - ref)))
         cpu = {"value": round(passes * dec_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
@@ -296,16 +328,19 @@ def bench_decode(args, torch, pa, W, w, layers, partition):
     res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+        "vs_baseline": None, "dtype": "fp8_e4m3 KV, bf16 q" if fp8 else w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + ("_fp8" if fp8 else ""), "batch": B, "num_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": w.block_size, "layers": layers, "total_tokens": int(lens.sum()),
                    "max_seq_len": max_len, "partition_size": partition or "auto",
                    "num_blocks_per_layer": w.layout.num_blocks},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "traffic_unit": "bytes per call", "kernel": "paged_attn_decode call",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name + ("_fp8" if fp8 else "")),
+                     "traffic_unit": "bytes per call",
+                     "kernel": "paged_attn_decode_fp8 call" if fp8 else "paged_attn_decode call",
                      "bytes_per_launch": dec_bytes,
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
@@ -321,14 +356,20 @@ def host_copy(torch, t):
     return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
 
-def bench_prefill(args, torch, pa, W, w, layers):
+def bench_prefill(args, torch, pa, W, w, layers, fp8=False):
     """Chunked prefill: per layer, write the chunk's K/V rows, then causal chunk attention."""
     dev = "cuda"
     B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
     Tq = w.num_query_tokens
     shape = (w.layout.num_blocks, Hkv, w.layout.block_size, D)
-    K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
-    V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+    if fp8:
+        KS = [fp8_pool(torch, W, shape, w.std, w.seed * 1000 + 2 * l) for l in range(layers)]
+        VS = [fp8_pool(torch, W, shape, w.std, w.seed * 1000 + 2 * l + 1) for l in range(layers)]
+        K, ks = [a for a, _ in KS], [s for _, s in KS]
+        V, vs = [a for a, _ in VS], [s for _, s in VS]
+    else:
+        K = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+        V = [W.device_values(shape, w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
     q = W.device_values((Tq, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
     newk = W.device_values((Tq, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
     newv = W.device_values((Tq, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
@@ -339,18 +380,25 @@ def bench_prefill(args, torch, pa, W, w, layers):
     out = torch.empty(Tq, Hq, D, device=dev, dtype=torch.float32)
     max_q, max_len = int(w.chunk_lens.max()), int(w.layout.seq_lens.max())
 
-    ms_step, ms_call, wall, mode = time_layers(
-        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
-        lambda l: pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len), out)
-    ms_write = time_calls(args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots))
-    write_bytes = Tq * Hkv * D * 2 * 2 * 2 + 8 * Tq  # K and V rows read and written, bf16, + slots
+    if fp8:
+        write = lambda l: pa.kv_cache_write_fp8(newk, newv, K[l], V[l], slots, ks[l], vs[l])
+        call = lambda l: pa.paged_attn_prefill_chunk_fp8(out, q, K[l], V[l], ks[l], vs[l], bt, qsl, sl, w.scale,
+                                                         max_q, max_len)
+        write_bytes = Tq * Hkv * D * (2 + 1) * 2 + 8 * Tq  # bf16 rows read, codes written, + slots
+    else:
+        write = lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+        call = lambda l: pa.paged_attn_prefill_chunk(out, q, K[l], V[l], bt, qsl, sl, w.scale, max_q, max_len)
+        write_bytes = Tq * Hkv * D * 2 * 2 * 2 + 8 * Tq  # K and V rows read and written, bf16, + slots
+    ms_step, ms_call, wall, mode = time_layers(args, torch, layers, write, call, out)
+    ms_write = time_calls(args, torch, layers, write)
     flops = w.flops()
     tflops = flops / (ms_call * 1e-3) / 1e12
     # sampled parity: the last 8 rows of sequence 0 and the first 8 rows of the last sequence,
     # each checked as a chunk of its own (a chunk's rows depend only on their positions)
-    pa.paged_attn_prefill_chunk(out, q, K[0], V[0], bt, qsl, sl, w.scale, max_q, max_len)
+    call(0)
     torch.cuda.synchronize()
     import oracle
+    kvs = dict(k_scale=ks[0], v_scale=vs[0]) if fp8 else {}
     oracle.build(force=False)
     hq, hk, hv = host_copy(torch, q), host_copy(torch, K[0]), host_copy(torch, V[0])
     qsl_h = w.query_start_loc
@@ -359,7 +407,7 @@ def bench_prefill(args, torch, pa, W, w, layers):
         S, n = int(w.layout.seq_lens[b]), int(w.chunk_lens[b])
         rows = slice(qsl_h[b] + i0, qsl_h[b] + i1)
         ref = oracle.paged_prefill(hq[rows], hk, hv, w.layout.block_tables[b:b + 1], np.array([0, i1 - i0], np.int32),
-                                   np.array([S - n + i1], np.int32), w.scale)
+                                   np.array([S - n + i1], np.int32), w.scale, **kvs)
         errs.append(float(np.max(np.abs(out[rows].double().cpu().numpy() - ref))))
     cpu = None
     if not args.no_cpu_baseline:
@@ -372,7 +420,7 @@ def bench_prefill(args, torch, pa, W, w, layers):
         def one(i):
             r_ = slice(qsl_h[b] + i, qsl_h[b] + i + 1)
             return oracle.paged_prefill(hq[r_], hk, hv, w.layout.block_tables[b:b + 1], np.array([0, 1], np.int32),
-                                        np.array([S - n + i + 1], np.int32), w.scale)
+                                        np.array([S - n + i + 1], np.int32), w.scale, **kvs)
 
         with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as ex:
             i = 0
@@ -390,15 +438,16 @@ def bench_prefill(args, torch, pa, W, w, layers):
         "metric": "chunked prefill attention TFLOP/s and query tokens/s per layer", "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "prefix": int(w.layout.seq_lens[0] - w.chunk_lens[0]),
+        "dtype": "fp8_e4m3 KV, bf16 q" if fp8 else w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + ("_fp8" if fp8 else ""), "batch": B,
+                   "prefix": int(w.layout.seq_lens[0] - w.chunk_lens[0]),
                    "chunk": int(w.chunk_lens[0]), "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": w.layout.block_size, "layers": layers},
         "query_tokens_per_s_per_layer": round(Tq / (ms_call * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes per call",
-                     "kernel": "paged_attn_prefill_chunk call", "flops_per_launch": flops,
+                     "traffic": measured_traffic(w.name + ("_fp8" if fp8 else "")), "traffic_unit": "bytes per call",
+                     "kernel": "paged_attn_prefill_chunk%s call" % ("_fp8" if fp8 else ""), "flops_per_launch": flops,
                      "avg_launch_ms": round(ms_call, 5)},
         "kv_cache_write": {"rows": Tq * Hkv, "us_per_call": round(ms_write * 1e3, 3),
                            "GBs": round(write_bytes / (ms_write * 1e-3) / 1e9, 1)},
@@ -749,19 +798,20 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.workload == "llama8b_decode":
-        w = W.llama8b_decode()
+    fp8 = args.workload.endswith("_fp8")
+    if args.workload in ("llama8b_decode", "llama8b_decode_fp8"):
+        w = W.llama8b_decode(block_size=args.block_size)
         layers = args.layers or 32
         part = 0 if args.partition < 0 else args.partition
-        res = bench_decode(args, torch, pa, W, w, layers, part)
-    elif args.workload == "llama70b_long":
-        w = W.llama70b_long()
+        res = bench_decode(args, torch, pa, W, w, layers, part, fp8=fp8)
+    elif args.workload in ("llama70b_long", "llama70b_long_fp8"):
+        w = W.llama70b_long(block_size=args.block_size)
         layers = args.layers or 4
         part = 0 if args.partition < 0 else args.partition
-        res = bench_decode(args, torch, pa, W, w, layers, part)
-    elif args.workload == "chunked_prefill":
-        w = W.chunked_prefill()
-        res = bench_prefill(args, torch, pa, W, w, args.layers or 32)
+        res = bench_decode(args, torch, pa, W, w, layers, part, fp8=fp8)
+    elif args.workload in ("chunked_prefill", "chunked_prefill_fp8"):
+        w = W.chunked_prefill(block_size=args.block_size)
+        res = bench_prefill(args, torch, pa, W, w, args.layers or 32, fp8=fp8)
     elif args.workload in ("shared_prefix", "shared_prefix_cow"):
         w = W.shared_prefix(prompt_len=512 if args.workload == "shared_prefix" else 500)
         res = bench_shared_prefix(args, torch, pa, W, w, args.layers or 32)

@@ -144,7 +144,8 @@ PA_EXPORT size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_
  *                 Must be <= max_seq_len and <= max_blocks_per_seq*block_size;
  *                 larger values are clamped to those bounds.  0 gives a zero row.
  *   max_seq_len   host-side upper bound of seq_lens (sizes the launch grid).
- *   scale         multiplies q.k (normally 1/sqrt(head_dim)).
+ *   scale         multiplies q.k (normally 1/sqrt(head_dim)); finite and > 0,
+ *                 else PA_ERR_SHAPE.
  *   partition_size  split-K granularity in tokens, a multiple of block_size,
  *                 or 0 for the library's choice.  The KV blocks of all
  *                 (sequence, KV head) rows are split into contiguous pieces of
@@ -186,7 +187,8 @@ PA_EXPORT int paged_attn_decode(void *out, int32_t out_dtype, const void *q, con
  *                 or written, whatever query_start_loc says.
  *   seq_lens      [num_seqs] int32: tokens in the cache after the chunk.
  *   max_query_len host-side upper bound of n_b (rows beyond it are not
- *                 computed); max_seq_len bounds seq_lens.
+ *                 computed); max_seq_len bounds seq_lens.  scale as in
+ *                 paged_attn_decode.
  * Row i of sequence b sits at position seq_lens[b] - n_b + i and attends to
  * tokens 0 .. that position (inclusive).  The prefix need not end on a block
  * boundary.

@@ -202,6 +202,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                   max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
   if (st != PA_OK) return st;
+  if (!scale_ok(scale)) return PA_ERR_SHAPE;  // the kernels scale after taking the max
   if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
   if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
   if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size) && num_heads / num_kv_heads <= 16))
@@ -301,6 +302,7 @@ int prefill_impl(void *out, int32_t out_dtype, const void *q, const void *k_cach
   int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                   max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
   if (st != PA_OK) return st;
+  if (!scale_ok(scale)) return PA_ERR_SHAPE;  // the kernels scale after taking the max
   if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
   if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
   const int g = num_heads / num_kv_heads;

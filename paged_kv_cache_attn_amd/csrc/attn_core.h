@@ -193,6 +193,11 @@ __device__ __forceinline__ void KVFormat<false>::load_q(bf16x8 qb[4], const uint
   load_q_operand_d128(qb, qrow, r);
 }
 
+// Slack of the lazy output rescale (log2 units): weights may reach 2^8
+// before the running max is moved up, which fp32 sums and the bf16 hi + lo
+// split carry without loss.
+constexpr float kLazyRescale = 8.f;
+
 struct MfmaAttnState {
   float m;          // running max of the column, log2 domain
   float l;          // running sum of this lane's share of the weights
@@ -207,7 +212,10 @@ struct MfmaAttnState {
 
   // One 16-token block whose first token has logical index tok0; keys with
   // logical index >= lim are masked for this lane's column.  sl2 =
-  // scale * log2(e).
+  // scale * log2(e) > 0.  As in the prefill step, the max is taken on the
+  // raw scores and scaled once, and the output is rescaled only when some
+  // column's max grows by more than 2^kLazyRescale (wave-uniform), so most
+  // tiles of a long row skip the 32-register rescale.
   __device__ __forceinline__ void step(const bf16x8 qb[4], const KVTile &t, int tok0, int lim,
                                        float sl2, int r) {
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
@@ -216,14 +224,21 @@ struct MfmaAttnState {
     const int tok = tok0 + 4 * r;
     float x[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = (tok + v < lim) ? s[v] * sl2 : kNegInf;
-    const float mx = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float corr = fast_exp2(m - m_use);
+    for (int v = 0; v < 4; ++v) x[v] = (tok + v < lim) ? s[v] : kNegInf;
+    const float mx = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float corr = fast_exp2(m - m_use);
+      l *= corr;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
+      m = m_new;
+    }
+    const float neg_m = m == kNegInf ? 0.f : -m;
     float e[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) e[v] = fast_exp2(x[v] - m_use);
+    for (int v = 0; v < 4; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, neg_m));
     // The weights enter the bf16 PV product as hi + lo bf16 parts: hi is e
     // rounded to bf16, lo is the (exactly representable) remainder rounded to
     // bf16, so hi + lo carries e to about 2^-17 relative.
@@ -231,12 +246,9 @@ struct MfmaAttnState {
     const uint32_t hi1 = pack_bf16x2(e[2], e[3]);
     const uint32_t lo0 = pack_bf16x2(e[0] - bf16_bits_to_float(hi0 & 0xffffu), e[1] - bf16_bits_to_float(hi0 >> 16));
     const uint32_t lo1 = pack_bf16x2(e[2] - bf16_bits_to_float(hi1 & 0xffffu), e[3] - bf16_bits_to_float(hi1 >> 16));
-    l = l * corr + ((e[0] + e[1]) + (e[2] + e[3]));
-    m = m_new;
+    l += (e[0] + e[1]) + (e[2] + e[3]);
     const u32x2 pb_hi = {hi0, hi1};
     const u32x2 pb_lo = {lo0, lo1};
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       const u32x2 a_lo = {pack_lo_halves(t.v[0][w2], t.v[1][w2]), pack_lo_halves(t.v[2][w2], t.v[3][w2])};
@@ -263,7 +275,6 @@ struct MfmaAttnState {
 // hi + lo split carry without loss.  Scores stay unscaled until the exponent:
 // m is kept in log2 units and each weight is exp2(s * sl2 - m) with one fma
 // (scaling by sl2 > 0 commutes with the max).
-constexpr float kLazyRescale = 8.f;
 
 struct MfmaAttnPairState {
   float m;

@@ -23,6 +23,12 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
+// Prefetch ring depth of the FP8 kernel (3 to 6).
+#ifndef PA_FP8_SLOTS
+#define PA_FP8_SLOTS 3
+#endif
+constexpr int kFp8Slots = PA_FP8_SLOTS;
+static_assert(kFp8Slots >= 3 && kFp8Slots <= 6, "FP8 ring depth out of range");
 constexpr int kBS = 16;  // tokens per tile: the unit of the flat space, whatever the block size
 
 
@@ -265,21 +271,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st.init();
       return true;
     };
-    // Three fixed slots: position li lives in slot li mod 3 (counting from
-    // ls), so no tile register is copied while its load is in flight.
-    Slot sa, sb, sc;
-    load_slot(ls, sa);
-    load_slot(ls + 1, sb);
-    for (int li = ls;;) {
-      load_slot(li + 2, sc);
-      st.step(sa.q, F::expand(sa.t), s_pj[li] * kBS, sa.lim, sl2, r);
-      if (!after_step(li++)) break;
-      load_slot(li + 2, sa);
-      st.step(sb.q, F::expand(sb.t), s_pj[li] * kBS, sb.lim, sl2, r);
-      if (!after_step(li++)) break;
-      load_slot(li + 2, sb);
-      st.step(sc.q, F::expand(sc.t), s_pj[li] * kBS, sc.lim, sl2, r);
-      if (!after_step(li++)) break;
+    if constexpr (!FP8) {
+      // Three fixed slots: position li lives in slot li mod 3 (counting from
+      // ls), so no tile register is copied while its load is in flight.
+      Slot sa, sb, sc;
+      load_slot(ls, sa);
+      load_slot(ls + 1, sb);
+      for (int li = ls;;) {
+        load_slot(li + 2, sc);
+        st.step(sa.q, F::expand(sa.t), s_pj[li] * kBS, sa.lim, sl2, r);
+        if (!after_step(li++)) break;
+        load_slot(li + 2, sa);
+        st.step(sb.q, F::expand(sb.t), s_pj[li] * kBS, sb.lim, sl2, r);
+        if (!after_step(li++)) break;
+        load_slot(li + 2, sb);
+        st.step(sc.q, F::expand(sc.t), s_pj[li] * kBS, sc.lim, sl2, r);
+        if (!after_step(li++)) break;
+      }
+    } else {
+      // FP8 tiles take half the registers, so the ring is deeper (kFp8Slots
+      // fixed slots, position li in slot (li - ls) mod kFp8Slots) and keeps
+      // about as many bytes in flight as the bf16 ring.
+      constexpr int NS = kFp8Slots;
+      Slot s[NS];
+#pragma unroll
+      for (int i = 0; i < NS - 1; ++i) load_slot(ls + i, s[i]);
+      auto one = [&](int li, auto kc) __attribute__((always_inline)) -> bool {
+        constexpr int k = decltype(kc)::value;
+        load_slot(li + NS - 1, s[(k + NS - 1) % NS]);
+        st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
+        return after_step(li);
+      };
+      for (int li = ls;; li += NS) {
+        if (!one(li, std::integral_constant<int, 0>())) break;
+        if (!one(li + 1, std::integral_constant<int, 1>())) break;
+        if (!one(li + 2, std::integral_constant<int, 2>())) break;
+        if constexpr (NS > 3) {
+          if (!one(li + 3, std::integral_constant<int, 3>())) break;
+        }
+        if constexpr (NS > 4) {
+          if (!one(li + 4, std::integral_constant<int, 4>())) break;
+        }
+        if constexpr (NS > 5) {
+          if (!one(li + 5, std::integral_constant<int, 5>())) break;
+        }
+      }
     }
   }
   __syncthreads();

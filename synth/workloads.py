@@ -139,10 +139,10 @@ def llama8b_decode(batch: int = 64, seed: int = 2, block_size: int = 16) -> Deco
     return DecodeWorkload(name, lay, 32, 8, 128, "bf16", 0.5, seed=seed)
 
 
-def llama70b_long(batch: int = 8, seq_len: int = 32768, seed: int = 4) -> DecodeWorkload:
-    lay = build_paged_layout([seq_len] * batch, 16, seed=seed + 1000, pool_factor=1.0)
-    return DecodeWorkload("llama70b_long_bf16", lay, 64, 8, 128, "bf16", 1.0, seed=seed,
-                          partition_size=512)
+def llama70b_long(batch: int = 8, seq_len: int = 32768, seed: int = 4, block_size: int = 16) -> DecodeWorkload:
+    lay = build_paged_layout([seq_len] * batch, block_size, seed=seed + 1000, pool_factor=1.0)
+    name = "llama70b_long_bf16" + ("" if block_size == 16 else "_bs%d" % block_size)
+    return DecodeWorkload(name, lay, 64, 8, 128, "bf16", 1.0, seed=seed, partition_size=512)
 
 
 def shared_prefix(prompts: int = 16, prompt_len: int = 512, samples: int = 8, max_private: int = 256,

@@ -88,6 +88,8 @@ def test_decode_validation(pa):
     assert _dec(pa, out_dtype=2) == PA_ERR_UNSUPPORTED
     assert _dec(pa, NB=0) == PA_ERR_SHAPE
     assert _dec(pa, part=24) == PA_ERR_SHAPE                                  # not a block multiple
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        assert _dec(pa, scale=bad) == PA_ERR_SHAPE                            # scale finite and > 0
     assert _dec(pa, q=N) == PA_ERR_NULL
     assert _dec(pa, bt=N) == PA_ERR_NULL
     # 4096 tokens in 256-token partitions need a workspace
