@@ -349,28 +349,48 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int g_first = range_of(rs, T, G, R);
       p.sk_desc[gi] = int4{row, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
     }
+    // the run's members: the entries from h on with this row start (a bit
+    // mask, uniform; empty entries may sit between members).  Most runs have
+    // one member: a row that only touches one wave's share.
+    unsigned mem = 0;
+#pragma unroll
+    for (int i = h; i < NE; ++i) mem |= (ers[i] == rs ? 1u : 0u) << i;
+    const bool single = (mem & (mem - 1)) == 0;
     for (int idx = tid; idx < g * kD; idx += 64 * NW) {
       const int cc = idx / kD, d = idx - cc * kD;
-      float mv[NE], lv[NE], ov[NE];
+      float M, lsum, o;
+      if (single) {
+        // weight exp2(0) = 1 (an all-masked entry carries zero sum and output)
+        const float *pc = s_park + ((size_t)h * g + cc) * (kD + 2);
+        M = pc[kD];
+        lsum = pc[kD + 1];
+        o = pc[d];
+      } else {
+        float mv[NE], lv[NE], ov[NE];
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const float *pc = s_park + ((size_t)i * g + cc) * (kD + 2);
-        const bool in = i >= h && ers[i] == rs;
-        mv[i] = in ? pc[kD] : kNegInf;
-        lv[i] = in ? pc[kD + 1] : 0.f;
-        ov[i] = in ? pc[d] : 0.f;
-      }
-      float M = kNegInf;
+        for (int i = h; i < NE; ++i) {
+          if ((mem >> i) & 1u) {
+            const float *pc = s_park + ((size_t)i * g + cc) * (kD + 2);
+            mv[i] = pc[kD];
+            lv[i] = pc[kD + 1];
+            ov[i] = pc[d];
+          }
+        }
+        M = kNegInf;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) M = fmaxf(M, mv[i]);
-      const float M_use = M == kNegInf ? 0.f : M;
-      float lsum = 0.f, o = 0.f;
+        for (int i = h; i < NE; ++i)
+          if ((mem >> i) & 1u) M = fmaxf(M, mv[i]);
+        const float M_use = M == kNegInf ? 0.f : M;
+        lsum = 0.f;
+        o = 0.f;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        if (i < h) continue;
-        const float wgt = fast_exp2(mv[i] - M_use);  // 0 for entries outside the run
-        lsum += lv[i] * wgt;
-        o += ov[i] * wgt;
+        for (int i = h; i < NE; ++i) {
+          if ((mem >> i) & 1u) {
+            const float wgt = fast_exp2(mv[i] - M_use);
+            lsum += lv[i] * wgt;
+            o += ov[i] * wgt;
+          }
+        }
       }
       if (whole) {
         store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
