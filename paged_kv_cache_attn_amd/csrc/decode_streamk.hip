@@ -203,14 +203,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int c_ld = c < g ? c : g - 1;  // idle columns read a valid row, never stored
 
   // A slot holds one tile and the q operand of its row, loaded together at
-  // the same prefetch distance.  An out-of-range table entry is never
-  // dereferenced: the tile is read from block 0 and fully masked.
+  // the same prefetch distance.  The q operand is loaded only when the slot's
+  // previous occupant (position li - dist, dist = ring depth) belonged to
+  // another row; otherwise the registers still hold this row's q.  An
+  // out-of-range table entry is never dereferenced: the tile is read from
+  // block 0 and fully masked.
   struct Slot {
     typename F::Raw t;
     bf16x8 q[4];
     int lim;
   };
-  auto load_slot = [&](int li, Slot &sl) {
+  auto load_slot = [&](int li, Slot &sl, int dist) {
+    const int lp = li - dist;
     li = li < le ? li : le - 1;  // past the share: reload the last tile (unused)
     const int2 u = s_rows[li];
     const int row = s_prow[li];
@@ -219,7 +223,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     sl.lim = ok ? s_len[b] : 0;
     // a masked tile reads the first rows of the cache
     F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
-    F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
+    const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
+    if (__builtin_amdgcn_readfirstlane((int)need_q))
+      F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
   };
 
   if (ls < le) {
@@ -275,16 +281,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // Three fixed slots: position li lives in slot li mod 3 (counting from
       // ls), so no tile register is copied while its load is in flight.
       Slot sa, sb, sc;
-      load_slot(ls, sa);
-      load_slot(ls + 1, sb);
+      load_slot(ls, sa, 3);
+      load_slot(ls + 1, sb, 3);
       for (int li = ls;;) {
-        load_slot(li + 2, sc);
+        load_slot(li + 2, sc, 3);
         st.step(sa.q, F::expand(sa.t), s_pj[li] * kBS, sa.lim, sl2, r);
         if (!after_step(li++)) break;
-        load_slot(li + 2, sa);
+        load_slot(li + 2, sa, 3);
         st.step(sb.q, F::expand(sb.t), s_pj[li] * kBS, sb.lim, sl2, r);
         if (!after_step(li++)) break;
-        load_slot(li + 2, sb);
+        load_slot(li + 2, sb, 3);
         st.step(sc.q, F::expand(sc.t), s_pj[li] * kBS, sc.lim, sl2, r);
         if (!after_step(li++)) break;
       }
@@ -295,10 +301,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       constexpr int NS = kFp8Slots;
       Slot s[NS];
 #pragma unroll
-      for (int i = 0; i < NS - 1; ++i) load_slot(ls + i, s[i]);
+      for (int i = 0; i < NS - 1; ++i) load_slot(ls + i, s[i], NS);
       auto one = [&](int li, auto kc) __attribute__((always_inline)) -> bool {
         constexpr int k = decltype(kc)::value;
-        load_slot(li + NS - 1, s[(k + NS - 1) % NS]);
+        load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS);
         st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
         return after_step(li);
       };
