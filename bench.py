@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=-1, help="decode partition size (-1 = workload default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="decode without a per-step plan (each call stages its own split)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every call from Python instead of replaying captured HIP graphs")
     return ap.parse_args()
@@ -144,7 +146,7 @@ def measured_copy_gbs(torch):
     return round(gbs, 1)
 
 
-def time_layers(args, torch, layers, write, call, out):
+def time_layers(args, torch, layers, write, call, out, pre=None):
     """Time one step (every layer: write(l) then call(l)) and the attention call alone.
 
     Default: each is captured once in a HIP graph (a decode step is a fixed
@@ -154,9 +156,13 @@ def time_layers(args, torch, layers, write, call, out):
     `layers`.  Before timing, a replay of the step graph must reproduce the
     eager result of the last layer bit for bit.  With --no-graph every call is
     launched from Python and bracketed by pre-created event pairs.
+    `pre` (optional) runs once at the start of a step and of the call-only
+    graph (a decode plan shared by the step's layers); its time is included.
     Returns (ms per step, ms per call, wall seconds of the timed steps, mode).
     """
     def step():
+        if pre is not None:
+            pre()
         for l in range(layers):
             write(l)
             call(l)
@@ -172,6 +178,8 @@ def time_layers(args, torch, layers, write, call, out):
         t0.record()
         i = 0
         for _ in range(args.steps):
+            if pre is not None:
+                pre()
             for l in range(layers):
                 write(l)
                 ev[i][0].record()
@@ -187,6 +195,8 @@ def time_layers(args, torch, layers, write, call, out):
     with torch.cuda.graph(g_step):
         step()
     with torch.cuda.graph(g_call):
+        if pre is not None:
+            pre()
         for l in range(layers):
             call(l)
     g_step.replay()
@@ -283,14 +293,27 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     scale = w.scale
 
+    # one plan per step serves all layers (same block tables and lengths)
+    kvd = pa.PA_FP8_E4M3 if fp8 else pa._dtype_code(K[0])
+    psize = pa.paged_attn_decode_plan_size(B, Hq, Hkv, D, w.block_size, w.layout.block_tables.shape[1], max_len,
+                                           partition, kvd)
+    use_plan = not args.no_plan and psize > 0
+    plan = torch.empty(max(psize, 1), dtype=torch.uint8, device=dev) if use_plan else None
+    pre = (lambda: pa.paged_attn_decode_plan(plan, K[0], bt, sl, Hq, max_len, partition)) if use_plan else None
     if fp8:
         write = lambda l: pa.kv_cache_write_fp8(newk, newv, K[l], V[l], slots, ks[l], vs[l])
+    else:
+        write = lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots)
+    if use_plan:
+        call = lambda l: pa.paged_attn_decode_planned(out, q, K[l], V[l], plan, bt, sl, scale, max_len, partition,
+                                                      ws, k_scale=ks[l] if fp8 else 1.0,
+                                                      v_scale=vs[l] if fp8 else 1.0)
+    elif fp8:
         call = lambda l: pa.paged_attn_decode_fp8(out, q, K[l], V[l], ks[l], vs[l], bt, sl, scale, max_len,
                                                   partition, ws)
     else:
-        write = lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots)
         call = lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, scale, max_len, partition, ws)
-    ms_step, ms_decode, wall, mode = time_layers(args, torch, layers, write, call, out)
+    ms_step, ms_decode, wall, mode = time_layers(args, torch, layers, write, call, out, pre)
     copy_gbs = measured_copy_gbs(torch)
     if fp8:
         # 1-byte K/V rows, bf16 q, fp32 out, table entries, lengths
@@ -306,6 +329,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
 
     # sampled parity + CPU baseline on layer 0 (the oracle on the host copies)
     torch.cuda.synchronize()
+    if pre is not None:
+        pre()
     call(0)
     torch.cuda.synchronize()
     gpu_out = out.double().cpu().numpy()
@@ -347,6 +372,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         "parity_max_abs_err_layer0": parity,
         "timing": mode, "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")],
         "copy_GBs_read_plus_write": copy_gbs, "wall_s": round(wall, 3),
+        "decode_plan": "one plan per step, shared by the layers" if use_plan else None,
     }
     return res
 

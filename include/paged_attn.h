@@ -232,6 +232,55 @@ PA_EXPORT int kv_cache_write_fp8(const void *key, const void *value, int32_t src
                                  int32_t head_dim, float k_scale, float v_scale, void *stream);
 
 /*
+ * Decode plans.  Which blocks each part of the balanced split reads depends
+ * only on seq_lens, the block tables and the sizes, not on the layer, so a
+ * plan computed once per decode step serves the attention of every layer
+ * (all layers of a step share the block tables; [L7] §4.5).  A planned
+ * decode starts streaming K/V after one memory round trip instead of
+ * computing its part of the split from seq_lens and the tables first.
+ *
+ * paged_attn_decode_plan_size -- bytes of the plan buffer for these sizes
+ * (host, pure function).  0: this shape is not split by the balanced path
+ * and needs no plan (the planned call then behaves as the plain one).
+ */
+PA_EXPORT size_t paged_attn_decode_plan_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                             int32_t max_seq_len, int32_t partition_size, int32_t kv_dtype);
+
+/*
+ * paged_attn_decode_plan -- enqueue the computation of a plan into `plan`
+ * (DEVICE, plan_bytes >= paged_attn_decode_plan_size(...), else
+ * PA_ERR_WORKSPACE) from block_tables and seq_lens, as paged_attn_decode
+ * would read them.  Nothing else is read or written.  A no-op when the size
+ * is 0.
+ */
+PA_EXPORT int paged_attn_decode_plan(void *plan, size_t plan_bytes, int32_t kv_dtype,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, int32_t max_seq_len, int32_t partition_size,
+                                     void *stream);
+
+/*
+ * paged_attn_decode_planned -- paged_attn_decode (kv_dtype PA_F32 / PA_BF16)
+ * or paged_attn_decode_fp8 (kv_dtype PA_FP8_E4M3; k_scale and v_scale are
+ * ignored otherwise) reading its split from `plan`.  The plan must have been
+ * made by paged_attn_decode_plan with the same kv_dtype, sizes,
+ * max_blocks_per_seq, max_seq_len and partition_size, from block_tables and
+ * seq_lens whose contents have not changed since (the call still reads
+ * seq_lens, for sequences with no tokens); otherwise the result is
+ * unspecified.  Results are bit-identical to the unplanned call.
+ */
+PA_EXPORT int paged_attn_decode_planned(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                                        const void *v_cache, int32_t kv_dtype, float k_scale, float v_scale,
+                                        const void *plan, size_t plan_bytes, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                        int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/*
  * paged_attn_decode_fp8 -- paged_attn_decode over FP8 caches (q bf16
  * [num_seqs][num_heads][head_dim], out PA_F32 or PA_BF16).  All other
  * arguments, the workspace (paged_attn_decode_workspace_size covers it) and

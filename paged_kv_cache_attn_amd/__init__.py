@@ -20,6 +20,7 @@ __all__ = [
     "pa_abi_version", "kv_cache_write", "paged_attn_decode_workspace_size", "paged_attn_decode",
     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in", "swap_host_bytes",
     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
+    "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -32,7 +33,8 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpage
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
                     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
-                    "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8")
+                    "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8",
+                    "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned")
 
 
 class PagedAttnError(RuntimeError):
@@ -72,6 +74,13 @@ def _load():
     L.paged_attn_prefill_chunk_fp8.argtypes = ([vp, i32, vp, vp, vp, f32, f32, vp, i32, vp, vp] + [i32] * 9
                                                + [f32, vp])
     L.paged_attn_prefill_chunk_fp8.restype = ctypes.c_int
+    L.paged_attn_decode_plan_size.argtypes = [i32] * 9
+    L.paged_attn_decode_plan_size.restype = ctypes.c_size_t
+    L.paged_attn_decode_plan.argtypes = [vp, ctypes.c_size_t, i32, vp, i32, vp] + [i32] * 8 + [vp]
+    L.paged_attn_decode_plan.restype = ctypes.c_int
+    L.paged_attn_decode_planned.argtypes = ([vp, i32, vp, vp, vp, i32, f32, f32, vp, ctypes.c_size_t, vp, i32, vp]
+                                            + [i32] * 7 + [f32, i32, vp, ctypes.c_size_t, vp])
+    L.paged_attn_decode_planned.restype = ctypes.c_int
     L.kv_swap_out.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
     L.kv_swap_out.restype = ctypes.c_int
     L.kv_swap_in.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
@@ -332,3 +341,53 @@ def paged_attn_prefill_chunk_fp8(out, q, k_cache, v_cache, k_scale: float, v_sca
                                           _dev(seq_lens, "seq_lens", torch.int32), B, Tq, Hq, Hkv, D, bs, NB,
                                           int(max_query_len), int(max_seq_len), float(scale), _stream(stream))
     _check("paged_attn_prefill_chunk_fp8", st)
+
+
+# ----------------------------------------------------------------------------- decode plans
+def paged_attn_decode_plan_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                                max_blocks_per_seq: int, max_seq_len: int, partition_size: int = 0,
+                                kv_dtype: int = PA_BF16) -> int:
+    return int(_L().paged_attn_decode_plan_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                               max_blocks_per_seq, max_seq_len, partition_size, kv_dtype))
+
+
+def paged_attn_decode_plan(plan, k_cache, block_tables, seq_lens, num_heads: int, max_seq_len: int,
+                           partition_size: int = 0, stream=None):
+    """Fill `plan` (uint8 GPU tensor, may be None when the plan size is 0) for decodes over caches shaped
+    like k_cache (its dtype picks the kernel family) with these block tables and lengths."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B = seq_lens.shape[0]
+    pptr, pbytes = ctypes.c_void_p(0), 0
+    if plan is not None:
+        pptr, pbytes = _dev(plan, "plan"), plan.numel() * plan.element_size()
+    st = _L().paged_attn_decode_plan(pptr, pbytes, _dtype_code(k_cache),
+                                    _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                                    _dev(seq_lens, "seq_lens", torch.int32), B, num_heads, Hkv, D, bs, NB,
+                                    int(max_seq_len), int(partition_size), _stream(stream))
+    _check("paged_attn_decode_plan", st)
+
+
+def paged_attn_decode_planned(out, q, k_cache, v_cache, plan, block_tables, seq_lens, scale: float,
+                              max_seq_len: int, partition_size: int = 0, workspace=None, k_scale: float = 1.0,
+                              v_scale: float = 1.0, stream=None):
+    """paged_attn_decode (or its FP8 form, by the caches' dtype) reading its split from `plan`."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    pptr, pbytes = ctypes.c_void_p(0), 0
+    if plan is not None:
+        pptr, pbytes = _dev(plan, "plan"), plan.numel() * plan.element_size()
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _L().paged_attn_decode_planned(_dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                       _dev(v_cache, "v_cache"), _dtype_code(k_cache), float(k_scale),
+                                       float(v_scale), pptr, pbytes, _dev(block_tables, "block_tables", torch.int32),
+                                       block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D,
+                                       bs, NB, int(max_seq_len), float(scale), int(partition_size), ws_ptr,
+                                       ws_bytes, _stream(stream))
+    _check("paged_attn_decode_planned", st)

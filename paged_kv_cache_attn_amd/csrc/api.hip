@@ -61,6 +61,9 @@ struct DecodePlan {
   int ranges = 0, range_blocks = 0;      // balanced path
   int part_blocks = 0, nparts = 1;       // partition-grid path
   size_t off_part = 0, off_ml = 0, off_desc = 0, workspace_bytes = 0;
+  // the balanced path's plan buffer: header, records, records2
+  int plan_stride = 0;
+  size_t plan_off_rec = 0, plan_off_rec2 = 0, plan_bytes = 0;
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -101,6 +104,14 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     pl.off_ml = align256(part);
     pl.off_desc = pl.off_ml + align256(ml);
     pl.workspace_bytes = pl.off_desc + align256((size_t)pl.ranges * 4 * sizeof(int));
+    // a range holds at most ceil(T / G) <= ceil(t_upper / ranges) positions
+    // (or range_blocks), and never more than the staging cache
+    pl.plan_stride = pl.range_blocks > 0
+                         ? pl.range_blocks
+                         : (int)std::min<int64_t>(ceil_div(t_upper, pl.ranges) + 1, pa::kStreamKTabCache);
+    pl.plan_off_rec = align256((size_t)pl.ranges * 4 * sizeof(int));
+    pl.plan_off_rec2 = pl.plan_off_rec + align256((size_t)pl.ranges * pl.plan_stride * 4 * sizeof(int));
+    pl.plan_bytes = pl.plan_off_rec2 + align256((size_t)pl.ranges * pl.plan_stride * 2 * sizeof(int));
     return pl;
   }
   const int64_t P = effective_partition(partition_size, block_size);
@@ -189,15 +200,23 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int
 
 namespace {
 
-// Both decode entry points.  kv_dtype PA_FP8_E4M3: the caches hold E4M3
+bool mfma_decode_shape(int32_t kv_dtype, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size) {
+  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && head_dim == 128 && pa::mfma_block_size(block_size) &&
+         num_heads / num_kv_heads <= 16;
+}
+
+// Every decode entry point.  kv_dtype PA_FP8_E4M3: the caches hold E4M3
 // codes read as value * k_scale / v_scale, q is bf16, and only the MFMA
-// shapes are served.
+// shapes are served.  plan (may be NULL): a plan from
+// paged_attn_decode_plan for the same sizes, block tables and seq_lens.
 int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,
                 int32_t kv_dtype, float k_scale, float v_scale, const int32_t *block_tables,
                 int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_seq_len, float scale, int32_t partition_size, void *workspace,
-                size_t workspace_bytes, void *stream) {
+                size_t workspace_bytes, void *stream, bool planned = false, const void *plan_buf = nullptr,
+                size_t plan_bytes = 0) {
   const bool fp8 = kv_dtype == PA_FP8_E4M3;
   int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                   max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
@@ -213,13 +232,13 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
 
   const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
-  const bool mfma_shape = (kv_dtype == PA_BF16 || fp8) && head_dim == 128 && pa::mfma_block_size(block_size) &&
-                          num_heads / num_kv_heads <= 16;
+  const bool mfma_shape = mfma_decode_shape(kv_dtype, num_heads, num_kv_heads, head_dim, block_size);
   DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                                 cap, partition_size, mfma_shape);
   if (plan.too_large) return PA_ERR_UNSUPPORTED;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return PA_ERR_WORKSPACE;
+  if (planned && plan.streamk && (!plan_buf || plan_bytes < plan.plan_bytes)) return PA_ERR_WORKSPACE;
 
   pa::DecodeParams p = {};
   p.out = out;
@@ -250,6 +269,13 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
     p.sk_part = reinterpret_cast<float *>(ws + plan.off_part);
     p.sk_ml = reinterpret_cast<float *>(ws + plan.off_ml);
     p.sk_desc = reinterpret_cast<int4 *>(ws + plan.off_desc);
+    if (planned) {
+      char *pb = static_cast<char *>(const_cast<void *>(plan_buf));
+      p.plan_hdr = reinterpret_cast<int4 *>(pb);
+      p.plan_rec = reinterpret_cast<int4 *>(pb + plan.plan_off_rec);
+      p.plan_rec2 = reinterpret_cast<int2 *>(pb + plan.plan_off_rec2);
+      p.plan_stride = plan.plan_stride;
+    }
     return launch_status(pa::launch_decode_streamk(p, s));
   }
   p.tile_tokens = mfma_shape ? 16 : block_size;
@@ -275,6 +301,73 @@ int paged_attn_decode(void *out, int32_t out_dtype, const void *q, const void *k
   return decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, 1.f, 1.f, block_tables, max_blocks_per_seq,
                      seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
                      scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+size_t paged_attn_decode_plan_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                   int32_t partition_size, int32_t kv_dtype) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
+    return 0;
+  if (partition_size > 0 && partition_size % block_size != 0) return 0;
+  const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
+  DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len, cap,
+                                partition_size, mfma_decode_shape(kv_dtype, num_heads, num_kv_heads, head_dim,
+                                                                  block_size));
+  return plan.streamk ? plan.plan_bytes : 0;
+}
+
+int paged_attn_decode_plan(void *plan_buf, size_t plan_bytes, int32_t kv_dtype, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_seq_len, int32_t partition_size, void *stream) {
+  const bool fp8 = kv_dtype == PA_FP8_E4M3;
+  if (!fp8 && !dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, PA_F32);
+  if (st != PA_OK) return st;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
+  DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len, cap,
+                                partition_size,
+                                mfma_decode_shape(kv_dtype, num_heads, num_kv_heads, head_dim, block_size));
+  if (!plan.streamk) return PA_OK;  // this shape is not split by ranges: nothing to plan
+  if (!plan_buf || plan_bytes < plan.plan_bytes) return PA_ERR_WORKSPACE;
+  if (!block_tables || !seq_lens) return PA_ERR_NULL;
+  pa::DecodeParams p = {};
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_len_cap = (int)cap;
+  p.sk_ranges = plan.ranges;
+  p.sk_range_blocks = plan.range_blocks;
+  char *pb = static_cast<char *>(plan_buf);
+  p.plan_hdr = reinterpret_cast<int4 *>(pb);
+  p.plan_rec = reinterpret_cast<int4 *>(pb + plan.plan_off_rec);
+  p.plan_rec2 = reinterpret_cast<int2 *>(pb + plan.plan_off_rec2);
+  p.plan_stride = plan.plan_stride;
+  return launch_status(pa::launch_decode_streamk_plan(p, static_cast<hipStream_t>(stream)));
+}
+
+int paged_attn_decode_planned(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,
+                              int32_t kv_dtype, float k_scale, float v_scale, const void *plan_buf,
+                              size_t plan_bytes, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (kv_dtype != PA_FP8_E4M3 && !dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_seq_len, scale, partition_size, workspace, workspace_bytes, stream, true,
+                     plan_buf, plan_bytes);
 }
 
 int paged_attn_decode_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,

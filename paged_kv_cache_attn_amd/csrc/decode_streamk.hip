@@ -71,19 +71,29 @@ __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, 
 // FP8 (E4M3) caches: the ring carries the tiles as loaded (16 instead of 32
 // registers each), expanded to bf16 just before their step; k_scale is
 // folded into the score scale, v_scale into the final normalisation.
-template <int NW, bool FP8>
+//
+// MODE kFused computes its range's staging (the prologue below) itself;
+// kPlanOnly runs only that prologue and writes the staging to a plan buffer;
+// kPlanned loads the staging from such a plan in one memory round trip.  A
+// plan depends only on seq_lens and the block tables, so one plan serves every
+// layer of a decode step.
+enum : int { kFused = 0, kPlanOnly = 1, kPlanned = 2 };
+
+template <int NW, bool FP8, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
     DecodeParams p) {
   using F = KVFormat<FP8>;
-  __shared__ int s_pref[kStreamKMaxSeqs + 1];  // first flat block of each sequence
-  __shared__ int s_len[kStreamKMaxSeqs];       // clamped sequence lengths
+  __shared__ int s_pref[MODE == kPlanned ? 1 : kStreamKMaxSeqs + 1];  // first flat block of each sequence
+  __shared__ int s_len[MODE == kPlanned ? 1 : kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
   __shared__ int2 s_rows[kStreamKTabCache];    // each position's tile rows 0 and 8, in 8-row
                                                //   units (x = -1: a table entry out of range)
   __shared__ int s_prow[kStreamKTabCache + 1]; // row (b * Hkv + kh) of each position, -1 past the end
   __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
+  __shared__ int2 s_ln[kStreamKTabCache];      // {sequence length, blocks of the row} of each position
   __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
   __shared__ int s_brid[NW][2];                // its row, b * Hkv + kh
+  __shared__ int s_bnb[NW][2];                 // its blocks
   extern __shared__ float s_park[];            // [NW][2][g][kD + 2]: acc, then max and sum
 
   const int tid = threadIdx.x;
@@ -95,101 +105,162 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);  // this workgroup's range
   const int R = p.sk_range_blocks;
 
-  // -- flat index space: exclusive prefix over sequences of blocks * Hkv ----
-  if (B <= 64) {
-    // one wave scans with cross-lane adds; a single barrier publishes it
-    if (w == 0) {
-      int L = lane < B ? p.seq_lens[lane] : 0;
-      L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
-      const int v = ((L + kBS - 1) / kBS) * Hkv;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        incl += lane >= off ? t : 0;
+  int T, G, s, e;
+  if constexpr (MODE != kPlanned) {
+    // -- flat index space: exclusive prefix over sequences of blocks * Hkv ----
+    if (B <= 64) {
+      // one wave scans with cross-lane adds; a single barrier publishes it
+      if (w == 0) {
+        int L = lane < B ? p.seq_lens[lane] : 0;
+        L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
+        const int v = ((L + kBS - 1) / kBS) * Hkv;
+        int incl = v;
+  #pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int t = __shfl_up(incl, off, 64);
+          incl += lane >= off ? t : 0;
+        }
+        if (lane < B) {
+          s_len[lane] = L;
+          s_pref[lane] = incl - v;
+        }
+        if (lane == (B > 0 ? B - 1 : 0)) s_pref[B] = B > 0 ? incl : 0;
       }
-      if (lane < B) {
-        s_len[lane] = L;
-        s_pref[lane] = incl - v;
+      if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
+      __syncthreads();
+    } else {
+      const int nt = 64 * NW;
+      const int per = (B + nt - 1) / nt;
+      const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
+      int local = 0;
+      for (int b = b0; b < b1; ++b) {
+        int L = p.seq_lens[b];
+        L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
+        s_len[b] = L;
+        local += ((L + kBS - 1) / kBS) * Hkv;
       }
-      if (lane == (B > 0 ? B - 1 : 0)) s_pref[B] = B > 0 ? incl : 0;
+      s_scan[tid] = local;
+      if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
+      __syncthreads();
+      for (int off = 1; off < nt; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+      }
+      int run = s_scan[tid] - local;
+      for (int b = b0; b < b1; ++b) {
+        s_pref[b] = run;
+        run += ((s_len[b] + kBS - 1) / kBS) * Hkv;
+      }
+      if (tid == nt - 1) s_pref[B] = s_scan[tid];
+      __syncthreads();
     }
-    if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
+    T = s_pref[B];
+    G = ranges_used((int)gridDim.x, T, R);
+
+    if constexpr (MODE == kFused) {
+      // no split row ends in this range unless the combine below says so
+      if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
+      // -- rows with no tokens get zeros (spread over the workgroups) ---------
+      for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
+        const int b = row / Hkv, kh = row - b * Hkv;
+        if (s_len[b] != 0) continue;
+        for (int idx = tid; idx < g * kD; idx += 64 * NW)
+          store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
+      }
+    }
+
+    s = range_begin(gi, T, G, R);
+    e = range_begin(gi + 1, T, G, R);
+    if constexpr (MODE == kPlanOnly) {
+      if (tid == 0) p.plan_hdr[gi] = int4{gi < G ? s : 0, gi < G ? e : 0, T, G};
+    }
+    if (gi >= G) return;
+    if (s >= e || e - s > kStreamKTabCache) return;  // the planner keeps ranges within the cache
+
+    const TileMap map(p.block_size, Hkv, p.num_blocks);
+    // Stage, for every position of this range, where its tile's rows 0 and 8
+    // start (element offsets / 1024, exact: both are multiples of 8 rows of
+    // 128), its (sequence, KV head) row and its tile index inside the row (the
+    // table loads of all positions issued together), so the streaming loop does
+    // no searching and no tile load waits on a dependent table read.  The
+    // planner keeps ranges within kStreamKTabCache positions; the host keeps a
+    // cache below 2^41 elements, so the offsets / 1024 fit in 31 bits.
+    for (int pos = s + tid; pos < e; pos += 64 * NW) {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= pos) lo = mid; else hi = mid;
+      }
+      const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
+      const int off = pos - s_pref[lo];
+      const int kh = off / nb, j = off - kh * nb;
+      int e0, e1;
+      const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
+                                  (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
+      const TileRows tr = map.rows(e0, e1, kh);
+      s_rows[pos - s] = ok ? int2{(int)(tr.lo >> 10), (int)(tr.hi >> 10)} : int2{-1, 0};
+      s_prow[pos - s] = lo * Hkv + kh;
+      s_pj[pos - s] = j;
+      s_ln[pos - s] = int2{s_len[lo], nb};
+      if constexpr (MODE == kPlanOnly) {
+        const int64_t at = (int64_t)gi * p.plan_stride + (pos - s);
+        p.plan_rec[at] = int4{s_rows[pos - s].x, s_rows[pos - s].y, lo * Hkv + kh, j};
+        p.plan_rec2[at] = int2{s_len[lo], nb};
+      }
+    }
+    if constexpr (MODE == kPlanOnly) return;
+    if (tid == 0) s_prow[e - s] = -1;
     __syncthreads();
   } else {
-    const int nt = 64 * NW;
-    const int per = (B + nt - 1) / nt;
-    const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
-    int local = 0;
-    for (int b = b0; b < b1; ++b) {
-      int L = p.seq_lens[b];
-      L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
-      s_len[b] = L;
-      local += ((L + kBS - 1) / kBS) * Hkv;
-    }
-    s_scan[tid] = local;
+    // -- the staging from the plan: header and records in one round trip ----
+    if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
     if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
+    constexpr int kMaxPer = (kStreamKTabCache + 64 * NW - 1) / (64 * NW);
+    const int4 h = p.plan_hdr[gi];
+    int4 ra[kMaxPer];
+    int2 rb[kMaxPer];
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      const int li = tid + k * 64 * NW;
+      if (li < p.plan_stride) {
+        ra[k] = p.plan_rec[(int64_t)gi * p.plan_stride + li];
+        rb[k] = p.plan_rec2[(int64_t)gi * p.plan_stride + li];
+      }
+    }
+    s = h.x;
+    e = h.y;
+    T = h.z;
+    G = h.w;
+    // rows with no tokens get zeros (spread over the workgroups)
+    for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
+      const int b = row / Hkv, kh = row - b * Hkv;
+      if (clamp_len(p.seq_lens[b], p.max_len_cap) != 0) continue;
+      for (int idx = tid; idx < g * kD; idx += 64 * NW)
+        store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
+    }
+    if (gi >= G || G > (int)gridDim.x || s < 0 || s >= e || e > T || e - s > p.plan_stride) return;
+    // The plan is trusted for its values but not for its bounds: a record
+    // whose tile lies outside the cache or whose row is not a (sequence, KV
+    // head) row of this call is masked and charged to row 0, so a stale or
+    // foreign plan gives wrong results, never an access out of bounds.
+    const int64_t units = ((int64_t)p.num_blocks * Hkv * p.block_size * kD) >> 10;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      const int li = tid + k * 64 * NW;
+      if (li < e - s) {
+        const bool ok = ra[k].x >= -1 && ra[k].x < units && ra[k].y >= 0 && ra[k].y < units && ra[k].z >= 0 &&
+                        ra[k].z < B * Hkv && ra[k].w >= 0;
+        s_rows[li] = ok ? int2{ra[k].x, ra[k].y} : int2{-1, 0};
+        s_prow[li] = ok ? ra[k].z : 0;
+        s_pj[li] = ok ? ra[k].w : 0;
+        s_ln[li] = rb[k];
+      }
+    }
+    if (tid == 0) s_prow[e - s] = -1;
     __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    int run = s_scan[tid] - local;
-    for (int b = b0; b < b1; ++b) {
-      s_pref[b] = run;
-      run += ((s_len[b] + kBS - 1) / kBS) * Hkv;
-    }
-    if (tid == nt - 1) s_pref[B] = s_scan[tid];
-    __syncthreads();
   }
-  const int T = s_pref[B];
-  const int G = ranges_used((int)gridDim.x, T, R);
-
-  // no split row ends in this range unless the combine below says so
-  if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
-
-  // -- rows with no tokens get zeros (spread over the workgroups) -----------
-  for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
-    const int b = row / Hkv, kh = row - b * Hkv;
-    if (s_len[b] != 0) continue;
-    for (int idx = tid; idx < g * kD; idx += 64 * NW)
-      store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
-  }
-
-  if (gi >= G) return;
-  const int s = range_begin(gi, T, G, R);
-  const int e = range_begin(gi + 1, T, G, R);
-  if (s >= e || e - s > kStreamKTabCache) return;  // the planner keeps ranges within the cache
-
-  const TileMap map(p.block_size, Hkv, p.num_blocks);
-  // Stage, for every position of this range, where its tile's rows 0 and 8
-  // start (element offsets / 1024, exact: both are multiples of 8 rows of
-  // 128), its (sequence, KV head) row and its tile index inside the row (the
-  // table loads of all positions issued together), so the streaming loop does
-  // no searching and no tile load waits on a dependent table read.  The
-  // planner keeps ranges within kStreamKTabCache positions; the host keeps a
-  // cache below 2^41 elements, so the offsets / 1024 fit in 31 bits.
-  for (int pos = s + tid; pos < e; pos += 64 * NW) {
-    int lo = 0, hi = B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= pos) lo = mid; else hi = mid;
-    }
-    const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
-    const int off = pos - s_pref[lo];
-    const int kh = off / nb, j = off - kh * nb;
-    int e0, e1;
-    const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
-                                (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
-    const TileRows tr = map.rows(e0, e1, kh);
-    s_rows[pos - s] = ok ? int2{(int)(tr.lo >> 10), (int)(tr.hi >> 10)} : int2{-1, 0};
-    s_prow[pos - s] = lo * Hkv + kh;
-    s_pj[pos - s] = j;
-  }
-  if (tid == 0) s_prow[e - s] = -1;
-  __syncthreads();
 
   // this wave's share of the range, in local positions [ls, le)
   const int ls = (int)((int64_t)(e - s) * w / NW);
@@ -220,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int row = s_prow[li];
     const int b = row / Hkv, kh = row - b * Hkv;
     const bool ok = u.x >= 0;
-    sl.lim = ok ? s_len[b] : 0;
+    sl.lim = ok ? s_ln[li].x : 0;
     // a masked tile reads the first rows of the cache
     F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
     const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
@@ -240,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const bool row_end = li + 1 == le || s_prow[li + 1] != row;
       if (!row_end) return true;
       const int b = row / Hkv, kh = row - b * Hkv;
-      const int nb = (s_pref[b + 1] - s_pref[b]) / Hkv;
+      const int nb = s_ln[li].y;
       const float lw = row_sum4(st.l);
       const bool whole = seg_j0 == 0 && s_pj[li] == nb - 1;
       if (whole) {
@@ -255,7 +326,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
       } else {
         // a wave has at most two boundary rows: its first and its last
-        const int k = slot_used++;
+        // (the bound only matters for a plan that is not this call's)
+        const int k = slot_used < 2 ? slot_used++ : 1;
         float *pc = s_park + (((size_t)w * 2 + k) * g + (col_ok ? c : 0)) * (kD + 2);
         if (col_ok) {
 #pragma unroll
@@ -268,8 +340,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           }
         }
         if (lane == 0) {
-          s_brow[w][k] = s_pref[b] + kh * nb;
+          s_brow[w][k] = s + li - s_pj[li];  // flat index of the row's first block
           s_brid[w][k] = row;
+          s_bnb[w][k] = nb;
         }
       }
       if (li + 1 == le) return false;
@@ -332,11 +405,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // in the same order; for each of its output elements it loads the members'
   // max, sum and partial value together and combines them in entry order.
   constexpr int NE = 2 * NW;
-  int ers[NE], erow[NE];
+  int ers[NE], erow[NE], enb[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     ers[i] = s_brow[i >> 1][i & 1];
     erow[i] = s_brid[i >> 1][i & 1];
+    enb[i] = s_bnb[i >> 1][i & 1];
   }
   int prev_rs = -1;
 #pragma unroll
@@ -346,13 +420,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     prev_rs = rs;
     const int row = erow[h];
     const int b = row / Hkv, kh = row - b * Hkv;
-    const int nb = (s_pref[b + 1] - s_pref[b]) / Hkv;
+    const int nb = enb[h];
     const bool whole = rs >= s && rs + nb <= e;
     const int slot = rs <= s ? 0 : 1;
     const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
     if (!whole && slot == 0 && rs + nb <= e && tid == 0) {
       // this range holds the last piece of a row that began in an earlier one
-      const int g_first = range_of(rs, T, G, R);
+      const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
       p.sk_desc[gi] = int4{row, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
     }
     // the run's members: the entries from h on with this row start (a bit
@@ -499,15 +573,25 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
 
 }  // namespace
 
+hipError_t launch_decode_streamk_plan(const DecodeParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kPlanOnly>), dim3(p.sk_ranges),
+                     dim3(64 * PA_DECODE_WAVES), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
   const size_t park = (size_t)PA_DECODE_WAVES * 2 * g * (kD + 2) * sizeof(float);
-  if (p.kv_fp8)
-    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, true>), dim3(p.sk_ranges),
-                       dim3(64 * PA_DECODE_WAVES), park, stream, p);
+  const dim3 grid(p.sk_ranges), block(64 * PA_DECODE_WAVES);
+  const bool planned = p.plan_hdr != nullptr;
+  if (p.kv_fp8 && planned)
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, true, kPlanned>), grid, block, park, stream, p);
+  else if (p.kv_fp8)
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, true, kFused>), grid, block, park, stream, p);
+  else if (planned)
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kPlanned>), grid, block, park, stream, p);
   else
-    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false>), dim3(p.sk_ranges),
-                       dim3(64 * PA_DECODE_WAVES), park, stream, p);
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kFused>), grid, block, park, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);

@@ -39,6 +39,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A sequence length clamped to [0, cap] (cap: the tokens the table and the
+// host bound admit).
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
 __device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
                                                       const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -75,6 +75,11 @@ struct DecodeParams {
   float *sk_ml;            // [ranges][2][g][2] partial (max, sum)
   int4 *sk_desc;           // [ranges] split row whose last piece the range holds:
                            // {row or -1, first range, slot of the first piece, pieces}
+  // a decode plan (balanced path; nullptr: each launch stages its own range)
+  int4 *plan_hdr;          // [ranges] {range start, range end, total blocks T, ranges used G}
+  int4 *plan_rec;          // [ranges][plan_stride] {tile row 0 / 1024, tile row 8 / 1024, row, j}
+  int2 *plan_rec2;         // [ranges][plan_stride] {sequence length, blocks of the row}
+  int plan_stride;         // positions per range in the plan (>= every range's size)
 };
 
 // Library choice of split-K partition size (tokens) for these sizes.
@@ -84,6 +89,8 @@ size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int npa
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream);
+// Writes the plan of p's balanced split (p.plan_* set, the attention fields unused).
+hipError_t launch_decode_streamk_plan(const DecodeParams &p, hipStream_t stream);
 
 struct PrefillParams {
   void *out;

@@ -28,8 +28,6 @@ namespace pa {
 
 namespace {
 
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
-
 __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, float v) {
   if (out_bf16) {
     reinterpret_cast<__bf16 *>(out)[idx] = (__bf16)v;

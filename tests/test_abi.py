@@ -218,6 +218,37 @@ def test_fp8_validation(pa):
         == PA_ERR_UNSUPPORTED
 
 
+def test_plan_validation(pa):
+    size = pa.lib.paged_attn_decode_plan_size
+    # B, Hq, Hkv, D, bs, maxblk, max_len, part, kv_dtype
+    n = size(64, 32, 8, 128, 16, 128, 2048, 0, 1)
+    assert n > 0 and n % 256 == 0
+    assert size(64, 32, 8, 128, 16, 128, 2048, 0, 2) == n     # FP8 plans the same split
+    assert size(64, 32, 8, 64, 16, 128, 2048, 0, 1) == 0      # head_dim 64: vector path, no plan
+    assert size(64, 32, 8, 128, 16, 128, 2048, 0, 0) == 0     # fp32: vector path
+    assert size(0, 32, 8, 128, 16, 128, 2048, 0, 1) == 0
+    assert size(64, 30, 8, 128, 16, 128, 2048, 0, 1) == 0     # Hq not a multiple of Hkv
+    assert size(64, 32, 8, 128, 16, 128, 2048, 24, 1) == 0    # partition not a block multiple
+    plan = pa.lib.paged_attn_decode_plan
+    # plan, bytes, kv_dtype, bt, maxblk, sl, B, Hq, Hkv, D, bs, NB, max_len, part, stream
+    args = [P, n, 1, P, 128, P, 64, 32, 8, 128, 16, 4096, 2048, 0, N]
+    assert plan(*args[:2], 7, *args[3:]) == PA_ERR_UNSUPPORTED
+    assert plan(N, *args[1:]) == PA_ERR_WORKSPACE
+    assert plan(P, n - 1, *args[2:]) == PA_ERR_WORKSPACE
+    assert plan(*args[:3], N, *args[4:]) == PA_ERR_NULL
+    assert plan(*args[:6], 0, *args[7:]) == PA_OK
+    assert plan(N, 0, 1, N, 128, N, 64, 32, 8, 64, 16, 4096, 2048, 0, N) == PA_OK   # nothing to plan
+    run = pa.lib.paged_attn_decode_planned
+    # out, odt, q, k, v, kvdt, ks, vs, plan, bytes, bt, maxblk, sl, B, Hq, Hkv, D, bs, NB, max_len, scale, part,
+    # ws, wsb, stream
+    need = pa.paged_attn_decode_workspace_size(64, 32, 8, 128, 16, 2048, 0)
+    r = [P, 0, P, P, P, 1, 1.0, 1.0, P, n, P, 128, P, 64, 32, 8, 128, 16, 4096, 2048, 0.1, 0, P, need, N]
+    assert run(*r[:8], N, *r[9:]) == PA_ERR_WORKSPACE
+    assert run(*r[:9], n - 1, *r[10:]) == PA_ERR_WORKSPACE
+    assert run(*r[:5], 3, *r[6:]) == PA_ERR_UNSUPPORTED
+    assert run(*r[:13], 0, *r[14:]) == PA_OK
+
+
 def test_binding_refuses_cpu_tensors(pa):
     import torch
     k = torch.zeros(4, 2, 16, 64)
