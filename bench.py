@@ -354,7 +354,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3 KV, bf16 q" if fp8 else w.dtype, "data": "synthetic",
-        "config": {"workload": w.name + ("_fp8" if fp8 else ""), "batch": B, "num_heads": Hq,
+        "config": {"workload": (w.name.replace("_bf16", "_fp8") if fp8 else w.name), "batch": B, "num_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": w.block_size, "layers": layers, "total_tokens": int(lens.sum()),
                    "max_seq_len": max_len, "partition_size": partition or "auto",
@@ -363,7 +363,7 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name + ("_fp8" if fp8 else "")),
+                     "traffic": measured_traffic((w.name.replace("_bf16", "_fp8") if fp8 else w.name)),
                      "traffic_unit": "bytes per call",
                      "kernel": "paged_attn_decode_fp8 call" if fp8 else "paged_attn_decode call",
                      "bytes_per_launch": dec_bytes,
@@ -465,14 +465,14 @@ def bench_prefill(args, torch, pa, W, w, layers, fp8=False):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 KV, bf16 q" if fp8 else w.dtype, "data": "synthetic",
-        "config": {"workload": w.name + ("_fp8" if fp8 else ""), "batch": B,
+        "config": {"workload": (w.name.replace("_bf16", "_fp8") if fp8 else w.name), "batch": B,
                    "prefix": int(w.layout.seq_lens[0] - w.chunk_lens[0]),
                    "chunk": int(w.chunk_lens[0]), "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": w.layout.block_size, "layers": layers},
         "query_tokens_per_s_per_layer": round(Tq / (ms_call * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name + ("_fp8" if fp8 else "")), "traffic_unit": "bytes per call",
+                     "traffic": measured_traffic((w.name.replace("_bf16", "_fp8") if fp8 else w.name)), "traffic_unit": "bytes per call",
                      "kernel": "paged_attn_prefill_chunk%s call" % ("_fp8" if fp8 else ""), "flops_per_launch": flops,
                      "avg_launch_ms": round(ms_call, 5)},
         "kv_cache_write": {"rows": Tq * Hkv, "us_per_call": round(ms_write * 1e3, 3),
@@ -504,9 +504,17 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
     copies = w.copies
     pairs = torch.from_numpy(np.asarray(copies, np.int64).reshape(-1, 2)).to(dev)
 
+    psize = pa.paged_attn_decode_plan_size(B, Hq, Hkv, D, w.block_size, w.layout.block_tables.shape[1], max_len, 0,
+                                           pa.PA_BF16)
+    use_plan = not args.no_plan and psize > 0
+    plan = torch.empty(max(psize, 1), dtype=torch.uint8, device=dev) if use_plan else None
+    pre = (lambda: pa.paged_attn_decode_plan(plan, K[0], bt, sl, Hq, max_len, 0)) if use_plan else None
+    if use_plan:
+        call = lambda l: pa.paged_attn_decode_planned(out, q, K[l], V[l], plan, bt, sl, w.scale, max_len, 0, ws)
+    else:
+        call = lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, w.scale, max_len, 0, ws)
     ms_step, ms_call, wall, mode = time_layers(
-        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots),
-        lambda l: pa.paged_attn_decode(out, q, K[l], V[l], bt, sl, w.scale, max_len, 0, ws), out)
+        args, torch, layers, lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots), call, out, pre)
     logical = w.algorithmic_bytes(out_bytes=4)
     unique = w.extra["unique_blocks"] * w.block_size * Hkv * D * w.elem_bytes * 2
     copy = None
@@ -523,7 +531,9 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
         us = e0.elapsed_time(e1) * 1e3 / layers
         cbytes = len(copies) * 2 * 2 * Hkv * w.block_size * D * w.elem_bytes  # K and V, read + write
         copy = {"pairs": len(copies), "us_per_call": round(us, 3), "GBs": round(cbytes / us / 1e3, 1)}
-    pa.paged_attn_decode(out, q, K[0], V[0], bt, sl, w.scale, max_len, 0, ws)
+    if pre is not None:
+        pre()
+    call(0)
     torch.cuda.synchronize()
     import oracle
     oracle.build(force=False)
@@ -548,6 +558,7 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
                      "unique_kv_bytes": unique, "unique_GBs": round(unique / (ms_call * 1e-3) / 1e9, 2),
                      "avg_launch_ms": round(ms_call, 5)},
         "block_copy": copy, "cpu_baseline": None, "parity_max_abs_err_sampled": err, "timing": mode,
+        "decode_plan": "one plan per step, shared by the layers" if use_plan else None,
         "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")], "wall_s": round(wall, 3),
     }
 
@@ -630,11 +641,22 @@ def bench_mixed_decode(args, torch, pa, W):
     wsb = pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, bs, max_len, 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
+    # a plan per decode step (the tables change every step), shared by its layers
+    psize = max(pa.paged_attn_decode_plan_size(B, Hq, Hkv, D, bs, t.shape[1], max_len, 0, pa.PA_BF16)
+                for t in tr.tables)
+    use_plan = not args.no_plan and psize > 0
+    plan = torch.empty(max(psize, 1), dtype=torch.uint8, device=dev)
+
     def step(s, l):
+        if l == 0 and use_plan:
+            pa.paged_attn_decode_plan(plan, K[0], bt[s], sl[s], Hq, max_len, 0)
         if len(tr.copies[s]):
             pa.block_copy(K[l], V[l], pairs[s])
         pa.kv_cache_write(newk, newv, K[l], V[l], slots[s])
-        pa.paged_attn_decode(out, q, K[l], V[l], bt[s], sl[s], tr.scale, max_len, 0, ws)
+        if use_plan:
+            pa.paged_attn_decode_planned(out, q, K[l], V[l], plan, bt[s], sl[s], tr.scale, max_len, 0, ws)
+        else:
+            pa.paged_attn_decode(out, q, K[l], V[l], bt[s], sl[s], tr.scale, max_len, 0, ws)
 
     # eager pass of the whole trace; layer 0's last decode against the oracle's replay
     for s in range(S):
@@ -704,6 +726,7 @@ def bench_mixed_decode(args, torch, pa, W):
                 "copy_us_per_step_all_layers": round(ms_copy * 1e3, 3)},
         "query_tokens_per_s_per_layer": round(B / (ms_step * 1e-3 / layers), 1),
         "parity_max_abs_err_sampled_rows": err, "cpu_baseline": None, "timing": "hip-graph",
+        "decode_plan": "one plan per step, shared by the layers" if use_plan else None,
     }
 
 
