@@ -23,12 +23,12 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-// Prefetch ring depth of the FP8 kernel (3 to 6).
-#ifndef PA_FP8_SLOTS
-#define PA_FP8_SLOTS 3
+// Prefetch ring depth of the balanced decode kernel (2 to 6 tiles per wave).
+#ifndef PA_DECODE_SLOTS
+#define PA_DECODE_SLOTS 2
 #endif
-constexpr int kFp8Slots = PA_FP8_SLOTS;
-static_assert(kFp8Slots >= 3 && kFp8Slots <= 6, "FP8 ring depth out of range");
+constexpr int kSlots = PA_DECODE_SLOTS;
+static_assert(kSlots >= 2 && kSlots <= 6, "decode ring depth out of range");
 constexpr int kBS = 16;  // tokens per tile: the unit of the flat space, whatever the block size
 
 
@@ -58,8 +58,8 @@ __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, 
     reinterpret_cast<float *>(out)[i] = v;
 }
 
-// Two waves per SIMD: with the three-slot ring that is 16 tiles (128 KB) in
-// flight per CU.
+// Two waves per SIMD: with the two-slot ring that is 16 tiles (128 KB of bf16
+// K/V) in flight per CU.
 //
 // Inside a workgroup every wave owns a contiguous quarter of the range and
 // streams it alone.  A row that lies wholly inside a wave's share is
@@ -350,28 +350,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st.init();
       return true;
     };
-    if constexpr (!FP8) {
-      // Three fixed slots: position li lives in slot li mod 3 (counting from
-      // ls), so no tile register is copied while its load is in flight.
-      Slot sa, sb, sc;
-      load_slot(ls, sa, 3);
-      load_slot(ls + 1, sb, 3);
-      for (int li = ls;;) {
-        load_slot(li + 2, sc, 3);
-        st.step(sa.q, F::expand(sa.t), s_pj[li] * kBS, sa.lim, sl2, r);
-        if (!after_step(li++)) break;
-        load_slot(li + 2, sa, 3);
-        st.step(sb.q, F::expand(sb.t), s_pj[li] * kBS, sb.lim, sl2, r);
-        if (!after_step(li++)) break;
-        load_slot(li + 2, sb, 3);
-        st.step(sc.q, F::expand(sc.t), s_pj[li] * kBS, sc.lim, sl2, r);
-        if (!after_step(li++)) break;
-      }
-    } else {
-      // FP8 tiles take half the registers, so the ring is deeper (kFp8Slots
-      // fixed slots, position li in slot (li - ls) mod kFp8Slots) and keeps
-      // about as many bytes in flight as the bf16 ring.
-      constexpr int NS = kFp8Slots;
+    {
+      // kSlots fixed register slots: position li lives in slot (li - ls) mod
+      // kSlots, so no tile register is copied while its load is in flight.
+      // Two slots (one tile computed while the next one loads) keep about
+      // 128 KB in flight per CU, which streams as fast as three (bf16) and
+      // leaves the registers to the scheduler.
+      constexpr int NS = kSlots;
       Slot s[NS];
 #pragma unroll
       for (int i = 0; i < NS - 1; ++i) load_slot(ls + i, s[i], NS);
@@ -384,7 +369,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int li = ls;; li += NS) {
         if (!one(li, std::integral_constant<int, 0>())) break;
         if (!one(li + 1, std::integral_constant<int, 1>())) break;
-        if (!one(li + 2, std::integral_constant<int, 2>())) break;
+        if constexpr (NS > 2) {
+          if (!one(li + 2, std::integral_constant<int, 2>())) break;
+        }
         if constexpr (NS > 3) {
           if (!one(li + 3, std::integral_constant<int, 3>())) break;
         }
