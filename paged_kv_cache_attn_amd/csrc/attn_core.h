@@ -288,37 +288,28 @@ struct MfmaAttnPairState {
     for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Blocks A (keys tok0 .. tok0+15) and B (keys tok0+16 ..): ka / kb are the
-  // K operands (token c, dims 32i + 8r ..), vt the V^T operands.  When `mask`
-  // is set (wave-uniform; false when every key of both blocks is visible to
-  // every column of the wave), keys of A at or past lim_a and keys of B at or
-  // past lim_b are masked for this lane's column.
-  __device__ __forceinline__ void step(const bf16x8 qb[4], const u32x4 ka[4], const u32x4 kb[4],
-                                       const bf16x8 vt[8], int tok0, int lim_a, int lim_b, bool mask,
-                                       float sl2, int r) {
+  // The raw scores of blocks A (keys tok0 .. tok0+15) and B (keys tok0+16 ..)
+  // for this lane's column: ka / kb are the K operands (token c, dims 32i + 8r ..).
+  static __device__ __forceinline__ void scores(const bf16x8 qb[4], const u32x4 ka[4], const u32x4 kb[4],
+                                                float x[8]) {
     floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sa = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[i]), qb[i], sa);
       sb = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[i]), qb[i], sb);
     }
-    float x[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       x[v] = sa[v];
       x[4 + v] = sb[v];
     }
-    if (mask) {
-      const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        x[v] = ta + v < lim_a ? x[v] : kNegInf;
-        x[4 + v] = tb + v < lim_b ? x[4 + v] : kNegInf;
-      }
-    }
+  }
+
+  // Raises the running max to cover scores x (scaled by sl2 into log2 units),
+  // rescaling the output only when some column's max grew past the slack.
+  __device__ __forceinline__ void raise_max(const float x[8], float sl2) {
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = row_max4(mx) * sl2;
-    // rescale only when some column's max grew by more than the slack
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
       const float m_new = fmaxf(m, mx);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
@@ -328,6 +319,10 @@ struct MfmaAttnPairState {
       for (int t = 0; t < 8; ++t) acc[t] *= corr;
       m = m_new;
     }
+  }
+
+  // The weights exp2(x * sl2 - m) as bf16 hi + lo operand parts; adds them to l.
+  __device__ __forceinline__ void weights(const float x[8], float sl2, bf16x8 &pb_hi, bf16x8 &pb_lo) {
     const float neg_m = m == kNegInf ? 0.f : -m;
     float e[8];
 #pragma unroll
@@ -340,14 +335,79 @@ struct MfmaAttnPairState {
                           e[2 * u + 1] - bf16_bits_to_float(hi[u] >> 16));
     }
     l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    pb_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    pb_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+  }
+
+  // O^T += V^T P^T for the eight 16-dim tiles, hi part then lo part.
+  __device__ __forceinline__ void pv(const bf16x8 vt[8], const bf16x8 &pb_hi, const bf16x8 &pb_lo) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       acc[t] = mfma_16x16x32_bf16(vt[t], pb_hi, acc[t]);
       acc[t] = mfma_16x16x32_bf16(vt[t], pb_lo, acc[t]);
     }
   }
+
+  // One pair of blocks for this lane's column: vt are the V^T operands.  When
+  // `mask` is set (wave-uniform; false when every key of both blocks is
+  // visible to every column of the wave), keys of A at or past lim_a and keys
+  // of B at or past lim_b are masked for this lane's column.
+  __device__ __forceinline__ void step(const bf16x8 qb[4], const u32x4 ka[4], const u32x4 kb[4],
+                                       const bf16x8 vt[8], int tok0, int lim_a, int lim_b, bool mask,
+                                       float sl2, int r) {
+    float x[8];
+    scores(qb, ka, kb, x);
+    if (mask) {
+      const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = ta + v < lim_a ? x[v] : kNegInf;
+        x[4 + v] = tb + v < lim_b ? x[4 + v] : kNegInf;
+      }
+    }
+    raise_max(x, sl2);
+    bf16x8 pb_hi, pb_lo;
+    weights(x, sl2, pb_hi, pb_lo);
+    pv(vt, pb_hi, pb_lo);
+  }
 };
+
+// Two column groups over the same pair of blocks: the same arithmetic per
+// group as MfmaAttnPairState::step (`mask0` / `mask1` as its `mask`, with the
+// groups' own key limits), ordered so that one group's matrix products can
+// run while the other group's softmax is computed: both score products
+// first, then the max updates, then group 0's weights and PV products, then
+// group 1's.  A group whose keys are all masked leaves its state unchanged
+// (its weights are exp2(-inf) = 0).
+__device__ __forceinline__ void pair_step_x2(MfmaAttnPairState &s0, MfmaAttnPairState &s1, const bf16x8 q0[4],
+                                             const bf16x8 q1[4], const u32x4 ka[4], const u32x4 kb[4],
+                                             const bf16x8 vt[8], int tok0, int lim_a0, int lim_b0, bool mask0,
+                                             int lim_a1, int lim_b1, bool mask1, float sl2, int r) {
+  float x0[8], x1[8];
+  MfmaAttnPairState::scores(q0, ka, kb, x0);
+  MfmaAttnPairState::scores(q1, ka, kb, x1);
+  const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
+  if (mask0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x0[v] = ta + v < lim_a0 ? x0[v] : kNegInf;
+      x0[4 + v] = tb + v < lim_b0 ? x0[4 + v] : kNegInf;
+    }
+  }
+  if (mask1) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x1[v] = ta + v < lim_a1 ? x1[v] : kNegInf;
+      x1[4 + v] = tb + v < lim_b1 ? x1[4 + v] : kNegInf;
+    }
+  }
+  s0.raise_max(x0, sl2);
+  s1.raise_max(x1, sl2);
+  bf16x8 h0, l0, h1, l1;
+  s0.weights(x0, sl2, h0, l0);
+  s0.pv(vt, h0, l0);
+  s1.weights(x1, sl2, h1, l1);
+  s1.pv(vt, h1, l1);
+}
 
 }  // namespace pa

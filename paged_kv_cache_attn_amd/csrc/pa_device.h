@@ -43,6 +43,29 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // host bound admit).
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// One 16-byte load per lane from global memory straight into LDS: lane i's
+// bytes land at lds_base + 16 i (lds_base is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Waits until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order).  Loads straight into LDS count here.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// All waves of the workgroup meet; the compiler moves no memory access across
+// it.  Unlike __syncthreads it waits for none of this wave's loads, so loads
+// into LDS stages that are not read yet stay in flight.
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
                                                       const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

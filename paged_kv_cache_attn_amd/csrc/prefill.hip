@@ -83,7 +83,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int kTileChunks = 1 << kTileShift;      // 16-byte chunks of one tile in HBM
   constexpr int kChunkElems = FP8 ? 16 : 8;         // elements per chunk
   constexpr int kChunksPerThread = 4 * kTileChunks / (64 * NW);
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+  // bf16 pairs go from global memory straight into LDS (four stages); FP8
+  // pairs are widened on the way, through registers (three stages).  Each
+  // stage is an array of its own, so the compiler can tell a load into one
+  // stage from reads of another and waits only for what a read needs.
+  constexpr bool kDma = !FP8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[kDma ? kStage : 16];
+  auto stage_mem = [&](auto st) __attribute__((always_inline)) -> uint8_t * {
+    constexpr int k = decltype(st)::value;
+    return k == 0 ? lds0 : k == 1 ? lds1 : k == 2 ? lds2 : lds3;
+  };
 
   const unsigned item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int tile = ntiles - 1 - (int)(item % (unsigned)ntiles);
@@ -164,16 +176,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     return (int)oka | ((int)okb << 1);
   };
+  // Direct pair load (bf16): the k-th load of wave w fills the 64 consecutive
+  // 16-byte slots of the stage from slot (k * NW + w) * 64 on, one per lane
+  // (64 slots = 4 rows of one tile), so each lane fetches the global chunk
+  // that the swizzled layout below puts in its slot: in a K tile slot col of
+  // row t holds chunk col ^ t, in a V tile chunk 2 ((col / 2) ^ (t & 7)) +
+  // (col & 1).  Same tiles, masking bits and clamping as gload.
+  auto dma = [&](int pr, auto st) __attribute__((always_inline)) -> int {
+    pr = min(pr, max(npair - 1, 0));
+    const int ja = 2 * pr, jb = 2 * pr + 1;
+    int a0, a1, b0, b1;
+    const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
+    const bool okb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1) && jb < nblk;
+    const TileRows ra = map.rows(a0, a1, kh);
+    const TileRows rb = map.rows(b0, b1, kh);
+    const int col = lane & 15;
+#pragma unroll
+    for (int k = 0; k < kChunksPerThread; ++k) {
+      const int slot0 = (k * NW + w) * 64;  // wave-uniform
+      const int kind = slot0 >> 8;          // 0 K_a, 1 V_a, 2 K_b, 3 V_b
+      const int t = ((slot0 & 255) >> 4) + (lane >> 4);
+      const int ch = (kind & 1) ? ((((col >> 1) ^ (t & 7)) << 1) | (col & 1)) : (col ^ t);
+      const TileRows &tr = kind < 2 ? ra : rb;
+      const int64_t base = (slot0 & 128) == 0 ? tr.lo : tr.hi - 8 * D;  // rows 0-7 or 8-15 of the tile
+      const Elem *src = ((kind & 1) ? vc : kc) + base + t * D + ch * 8;
+      load_lds16(src, stage_mem(st) + slot0 * 16);
+    }
+    return (int)oka | ((int)okb << 1);
+  };
   // LDS byte offset of bf16 chunk kc (0..15) of row t in a K or a V tile
   auto lds_off = [](bool is_v, int t, int kc) -> int {
     return is_v ? t * 256 + ((((kc >> 1) ^ (t & 7)) << 5) | ((kc & 1) << 4)) : (t * 16 + (kc ^ t)) << 4;
   };
-  auto lstore = [&](int stage, const u32x4 *regs) {
+  auto lstore = [&](auto stage, const u32x4 *regs) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kChunksPerThread; ++k) {
       const int u = tid + k * 64 * NW;
       const int kind = u >> kTileShift, q = u & (kTileChunks - 1);
-      uint8_t *tb = lds + stage * kStage + kind * kTile;
+      uint8_t *tb = stage_mem(stage) + kind * kTile;
       if (FP8) {
         // 16 codes = bf16 chunks 2 kc8 and 2 kc8 + 1 of row t
         const int t = q >> 3, kc8 = q & 7;
@@ -191,8 +231,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int vq8 = (c & 3) * 8;
   auto vt_addr = [&](int dt) -> int { return vtok * 256 + (((dt ^ (vtok & 7)) << 5) | vq8); };
   // The operands of one pair for this wave, from LDS stage `stage`.
-  auto lread = [&](int stage, u32x4 *ka, u32x4 *kb, bf16x8 *vt) {
-    const uint8_t *base = lds + stage * kStage;
+  auto lread = [&](auto stage, u32x4 *ka, u32x4 *kb, bf16x8 *vt) __attribute__((always_inline)) {
+    const uint8_t *base = stage_mem(stage);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ck = (c * 16 + ((4 * i + r) ^ c)) << 4;
@@ -209,17 +249,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       vt[dt] = __builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], b2[0], b2[1]});
     }
   };
-  auto compute = [&](int stage, int pr, int okbits, MfmaAttnPairState *st) {
+  auto compute = [&](auto stage, int pr, int okbits, MfmaAttnPairState *st) __attribute__((always_inline)) {
     u32x4 ka[4], kb[4];
     bf16x8 vt[8];
     lread(stage, ka, kb, vt);
     const int tok0 = 32 * pr;
     const bool oka = okbits & 1, okb = okbits & 2;
+    if constexpr (CG == 2) {
+      // both groups in one step (a group past its causal bound is fully masked)
+      const bool full0 = tok0 + 32 <= lim_min[0] && oka && okb;
+      const bool full1 = tok0 + 32 <= lim_min[1] && oka && okb;
+      pair_step_x2(st[0], st[1], qb[0], qb[1], ka, kb, vt, tok0, oka ? lim[0] : 0, okb ? lim[0] : 0, !full0,
+                   oka ? lim[1] : 0, okb ? lim[1] : 0, !full1, sl2, r);
+    } else {
 #pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
-      if (tok0 < kend[cg]) {
-        const bool full = tok0 + 32 <= lim_min[cg] && oka && okb;
-        st[cg].step(qb[cg], ka, kb, vt, tok0, oka ? lim[cg] : 0, okb ? lim[cg] : 0, !full, sl2, r);
+      for (int cg = 0; cg < CG; ++cg) {
+        if (tok0 < kend[cg]) {
+          const bool full = tok0 + 32 <= lim_min[cg] && oka && okb;
+          st[cg].step(qb[cg], ka, kb, vt, tok0, oka ? lim[cg] : 0, okb ? lim[cg] : 0, !full, sl2, r);
+        }
       }
     }
   };
@@ -228,24 +276,54 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) st[cg].init();
 
-  if (npair > 0) {
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if (kDma && npair > 0) {
+    // Pair X lands in stage X % 4; its loads are issued three pairs ahead,
+    // right after the barrier that ends every read of that stage's previous
+    // pair.  Before pair X is read each thread waits for its own loads of it
+    // (the two later pairs may still be in flight: 2 * kChunksPerThread
+    // loads), and the barrier then covers every thread's.  A pair index past
+    // the end re-loads the last pair, so the count of loads in flight is the
+    // same in every iteration.
+    int ok[4];
+    ok[0] = dma(0, S0());
+    ok[1] = dma(1, S1());
+    ok[2] = dma(2, S2());
+    ok[3] = 0;
+    auto iter = [&](int X, auto cur, auto nxt) __attribute__((always_inline)) -> bool {
+      vm_wait<2 * kChunksPerThread>();
+      workgroup_barrier();
+      ok[decltype(nxt)::value] = dma(X + 3, nxt);
+      compute(cur, X, ok[decltype(cur)::value], st);
+      return X + 1 < npair;
+    };
+    for (int X = 0;; X += 4) {
+      if (!iter(X, S0(), S3())) break;
+      if (!iter(X + 1, S1(), S0())) break;
+      if (!iter(X + 2, S2(), S1())) break;
+      if (!iter(X + 3, S3(), S2())) break;
+    }
+  } else if (npair > 0) {
     // Pair X sits in register set X % 3 and LDS stage X % 3.  Its loads are
     // issued while pair X - 3 is computed and reach LDS while pair X - 1 is,
     // so each load has two pairs of work to arrive.
     u32x4 rs[3][kChunksPerThread];
     int ok_r[3], ok_s[3];
     ok_r[0] = gload(0, rs[0]);
-    lstore(0, rs[0]);
+    lstore(S0(), rs[0]);
     ok_s[0] = ok_r[0];
     ok_r[1] = gload(1, rs[1]);
     ok_r[2] = gload(2, rs[2]);
     auto iter = [&](int X, auto phase) -> bool {
       constexpr int j = decltype(phase)::value, j1 = (j + 1) % 3;
       __syncthreads();
-      if (X + 1 < npair) lstore(j1, rs[j1]);
+      if (X + 1 < npair) lstore(std::integral_constant<int, j1>(), rs[j1]);
       ok_s[j1] = ok_r[j1];
       ok_r[j] = gload(X + 3, rs[j]);
-      compute(j, X, ok_s[j], st);
+      compute(phase, X, ok_s[j], st);
       return X + 1 < npair;
     };
     for (int X = 0;; X += 3) {
