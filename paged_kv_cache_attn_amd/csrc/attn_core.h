@@ -198,13 +198,48 @@ __device__ __forceinline__ void KVFormat<false>::load_q(bf16x8 qb[4], const uint
 // split carry without loss.
 constexpr float kLazyRescale = 8.f;
 
+// The lazy max update shared by the decode and prefill steps.  `local` is this
+// lane's max of the new scores (log2 units).  Only when some lane's max
+// exceeds its column's running max m by more than kLazyRescale (a
+// wave-uniform test) is the column max taken across the four lanes that hold
+// a column, m raised to it and the output (acc, l) rescaled; otherwise m stays
+// and the new weights may exceed 1 by up to 2^kLazyRescale.  Taking the
+// column max only on that path changes nothing: the test fires exactly when
+// the column max would pass it.  nm is -m, or 0 while m is -inf.
+template <int N>
+__device__ __forceinline__ void raise_lazy_max(float local, float &m, float &nm, float &l, floatx4 (&acc)[N]) {
+  if (__builtin_amdgcn_ballot_w64(local > m + kLazyRescale) != 0) {
+    const float m_new = fmaxf(m, row_max4(local));
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float corr = fast_exp2(m - m_use);
+    l *= corr;
+#pragma unroll
+    for (int t = 0; t < N; ++t) acc[t] *= corr;
+    m = m_new;
+    nm = m_new == kNegInf ? 0.f : -m_new;
+  }
+}
+
+// Splits two weights into bf16 hi parts (each rounded to nearest even) and
+// bf16 lo parts (the exactly representable remainders, rounded), packed in
+// pairs as the MFMA operands take them.  The hi parts are widened back with
+// one permute / one mask instead of a second conversion.
+__device__ __forceinline__ void split_bf16x2(float e0, float e1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(e0, e1);
+  const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));  // hi << 16
+  const float h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = pack_bf16x2(e0 - h0, e1 - h1);
+}
+
 struct MfmaAttnState {
   float m;          // running max of the column, log2 domain
+  float nm;         // -m, or 0 while m is -inf (the exponent offset)
   float l;          // running sum of this lane's share of the weights
   floatx4 acc[8];   // unnormalised output, see the header comment
 
   __device__ __forceinline__ void init() {
     m = kNegInf;
+    nm = 0.f;
     l = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -225,27 +260,16 @@ struct MfmaAttnState {
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) x[v] = (tok + v < lim) ? s[v] : kNegInf;
-    const float mx = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * sl2;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float corr = fast_exp2(m - m_use);
-      l *= corr;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[jj] *= corr;
-      m = m_new;
-    }
-    const float neg_m = m == kNegInf ? 0.f : -m;
+    raise_lazy_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * sl2, m, nm, l, acc);
     float e[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, neg_m));
+    for (int v = 0; v < 4; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, nm));
     // The weights enter the bf16 PV product as hi + lo bf16 parts: hi is e
     // rounded to bf16, lo is the (exactly representable) remainder rounded to
     // bf16, so hi + lo carries e to about 2^-17 relative.
-    const uint32_t hi0 = pack_bf16x2(e[0], e[1]);
-    const uint32_t hi1 = pack_bf16x2(e[2], e[3]);
-    const uint32_t lo0 = pack_bf16x2(e[0] - bf16_bits_to_float(hi0 & 0xffffu), e[1] - bf16_bits_to_float(hi0 >> 16));
-    const uint32_t lo1 = pack_bf16x2(e[2] - bf16_bits_to_float(hi1 & 0xffffu), e[3] - bf16_bits_to_float(hi1 >> 16));
+    uint32_t hi0, hi1, lo0, lo1;
+    split_bf16x2(e[0], e[1], hi0, lo0);
+    split_bf16x2(e[2], e[3], hi1, lo1);
     l += (e[0] + e[1]) + (e[2] + e[3]);
     const u32x2 pb_hi = {hi0, hi1};
     const u32x2 pb_lo = {lo0, lo1};
@@ -278,11 +302,13 @@ struct MfmaAttnState {
 
 struct MfmaAttnPairState {
   float m;
+  float nm;  // -m, or 0 while m is -inf
   float l;
   floatx4 acc[8];
 
   __device__ __forceinline__ void init() {
     m = kNegInf;
+    nm = 0.f;
     l = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -308,32 +334,18 @@ struct MfmaAttnPairState {
   // Raises the running max to cover scores x (scaled by sl2 into log2 units),
   // rescaling the output only when some column's max grew past the slack.
   __device__ __forceinline__ void raise_max(const float x[8], float sl2) {
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = row_max4(mx) * sl2;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float corr = fast_exp2(m - m_use);
-      l *= corr;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= corr;
-      m = m_new;
-    }
+    const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    raise_lazy_max(mx * sl2, m, nm, l, acc);
   }
 
   // The weights exp2(x * sl2 - m) as bf16 hi + lo operand parts; adds them to l.
   __device__ __forceinline__ void weights(const float x[8], float sl2, bf16x8 &pb_hi, bf16x8 &pb_lo) {
-    const float neg_m = m == kNegInf ? 0.f : -m;
     float e[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, neg_m));
+    for (int v = 0; v < 8; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, nm));
     uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      hi[u] = pack_bf16x2(e[2 * u], e[2 * u + 1]);
-      lo[u] = pack_bf16x2(e[2 * u] - bf16_bits_to_float(hi[u] & 0xffffu),
-                          e[2 * u + 1] - bf16_bits_to_float(hi[u] >> 16));
-    }
+    for (int u = 0; u < 4; ++u) split_bf16x2(e[2 * u], e[2 * u + 1], hi[u], lo[u]);
     l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     pb_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
     pb_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
