@@ -384,20 +384,23 @@ struct MfmaAttnPairState {
   }
 };
 
-// Two column groups over the same pair of blocks: the same arithmetic per
+// Two column groups over the same pair of blocks (load_v() fills the V^T
+// operands vt): the same arithmetic per
 // group as MfmaAttnPairState::step (`mask0` / `mask1` as its `mask`, with the
 // groups' own key limits), ordered so that one group's matrix products can
 // run while the other group's softmax is computed: both score products
 // first, then the max updates, then group 0's weights and PV products, then
 // group 1's.  A group whose keys are all masked leaves its state unchanged
 // (its weights are exp2(-inf) = 0).
+template <class LoadV>
 __device__ __forceinline__ void pair_step_x2(MfmaAttnPairState &s0, MfmaAttnPairState &s1, const bf16x8 q0[4],
                                              const bf16x8 q1[4], const u32x4 ka[4], const u32x4 kb[4],
-                                             const bf16x8 vt[8], int tok0, int lim_a0, int lim_b0, bool mask0,
-                                             int lim_a1, int lim_b1, bool mask1, float sl2, int r) {
+                                             LoadV &&load_v, const bf16x8 vt[8], int tok0, int lim_a0, int lim_b0,
+                                             bool mask0, int lim_a1, int lim_b1, bool mask1, float sl2, int r) {
   float x0[8], x1[8];
   MfmaAttnPairState::scores(q0, ka, kb, x0);
   MfmaAttnPairState::scores(q1, ka, kb, x1);
+  load_v();  // fills vt; issued after the score products have read ka / kb
   const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
   if (mask0) {
 #pragma unroll

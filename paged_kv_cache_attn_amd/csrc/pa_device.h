@@ -45,8 +45,29 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 
 // One 16-byte load per lane from global memory straight into LDS: lane i's
 // bytes land at lds_base + 16 i (lds_base is the same for the whole wave).
+// Written as inline assembly so that the compiler does not track it: its
+// wait-count pass cannot tell loads into one LDS stage from reads of another
+// across a loop header and would wait there for every load in flight.  The
+// caller therefore owns the waits: vm_wait for this wave's loads (they count
+// in vmcnt like any vector load), then a workgroup barrier before any wave
+// reads the stage.  M0 holds the LDS base; the compiler sets it afresh before
+// each of its own uses.
 __device__ __forceinline__ void load_lds16(const void *src, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// The same load with the address split into a wave-uniform base (scalar
+// registers) and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16_sv(const void *sbase, uint32_t voff, void *lds_base) {
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // Waits until at most N of this wave's vector-memory operations are still in

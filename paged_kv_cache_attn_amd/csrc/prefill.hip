@@ -24,6 +24,7 @@
 #define PA_PREFILL_GROUPS 2
 #endif
 
+
 namespace pa {
 
 namespace {
@@ -182,6 +183,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // that the swizzled layout below puts in its slot: in a K tile slot col of
   // row t holds chunk col ^ t, in a V tile chunk 2 ((col / 2) ^ (t & 7)) +
   // (col & 1).  Same tiles, masking bits and clamping as gload.
+  // With four waves and blocks of 16 tokens or more, load k of wave w is tile
+  // k, rows 4w .. 4w + 3 (one row per 16 lanes), and a tile's 16 rows are
+  // contiguous: each load is a wave-uniform tile base in scalar registers
+  // plus a per-lane byte offset that never changes.
+  constexpr bool kRowsContig = NW == 4 && BSZ >= 16;
+  const int trow = 4 * w + (lane >> 4), tcol = lane & 15;
+  const uint32_t off_k = (uint32_t)(trow * D + (tcol ^ trow) * 8) * 2u;
+  const uint32_t off_v = (uint32_t)(trow * D + ((((tcol >> 1) ^ (trow & 7)) << 1) | (tcol & 1)) * 8) * 2u;
   auto dma = [&](int pr, auto st) __attribute__((always_inline)) -> int {
     pr = min(pr, max(npair - 1, 0));
     const int ja = 2 * pr, jb = 2 * pr + 1;
@@ -190,17 +199,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool okb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1) && jb < nblk;
     const TileRows ra = map.rows(a0, a1, kh);
     const TileRows rb = map.rows(b0, b1, kh);
-    const int col = lane & 15;
+    if constexpr (kRowsContig) {
+      uint8_t *sm = stage_mem(st) + w * 1024;
+      const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kc), *vb8 = reinterpret_cast<const uint8_t *>(vc);
+      load_lds16_sv(kb8 + ra.lo * 2, off_k, sm + 0 * 4096);
+      load_lds16_sv(vb8 + ra.lo * 2, off_v, sm + 1 * 4096);
+      load_lds16_sv(kb8 + rb.lo * 2, off_k, sm + 2 * 4096);
+      load_lds16_sv(vb8 + rb.lo * 2, off_v, sm + 3 * 4096);
+    } else {
+      const int col = lane & 15;
 #pragma unroll
-    for (int k = 0; k < kChunksPerThread; ++k) {
-      const int slot0 = (k * NW + w) * 64;  // wave-uniform
-      const int kind = slot0 >> 8;          // 0 K_a, 1 V_a, 2 K_b, 3 V_b
-      const int t = ((slot0 & 255) >> 4) + (lane >> 4);
-      const int ch = (kind & 1) ? ((((col >> 1) ^ (t & 7)) << 1) | (col & 1)) : (col ^ t);
-      const TileRows &tr = kind < 2 ? ra : rb;
-      const int64_t base = (slot0 & 128) == 0 ? tr.lo : tr.hi - 8 * D;  // rows 0-7 or 8-15 of the tile
-      const Elem *src = ((kind & 1) ? vc : kc) + base + t * D + ch * 8;
-      load_lds16(src, stage_mem(st) + slot0 * 16);
+      for (int k = 0; k < kChunksPerThread; ++k) {
+        const int slot0 = (k * NW + w) * 64;  // wave-uniform
+        const int kind = slot0 >> 8;          // 0 K_a, 1 V_a, 2 K_b, 3 V_b
+        const int t = ((slot0 & 255) >> 4) + (lane >> 4);
+        const int ch = (kind & 1) ? ((((col >> 1) ^ (t & 7)) << 1) | (col & 1)) : (col ^ t);
+        const TileRows &tr = kind < 2 ? ra : rb;
+        const int64_t base = (slot0 & 128) == 0 ? tr.lo : tr.hi - 8 * D;  // rows 0-7 or 8-15 of the tile
+        const Elem *src = ((kind & 1) ? vc : kc) + base + t * D + ch * 8;
+        load_lds16(src, stage_mem(st) + slot0 * 16);
+      }
     }
     return (int)oka | ((int)okb << 1);
   };
@@ -230,8 +248,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int vtok = 4 * r + (c >> 2);
   const int vq8 = (c & 3) * 8;
   auto vt_addr = [&](int dt) -> int { return vtok * 256 + (((dt ^ (vtok & 7)) << 5) | vq8); };
-  // The operands of one pair for this wave, from LDS stage `stage`.
-  auto lread = [&](auto stage, u32x4 *ka, u32x4 *kb, bf16x8 *vt) __attribute__((always_inline)) {
+  // The operands of one pair for this wave, from LDS stage `stage`: K first,
+  // the V^T operands on their own so that they can be read after the score
+  // products have taken the K registers.
+  auto lread_k = [&](auto stage, u32x4 *ka, u32x4 *kb) __attribute__((always_inline)) {
     const uint8_t *base = stage_mem(stage);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -239,6 +259,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       ka[i] = *reinterpret_cast<const u32x4 *>(base + 0 * kTile + ck);
       kb[i] = *reinterpret_cast<const u32x4 *>(base + 2 * kTile + ck);
     }
+  };
+  auto lread_v = [&](auto stage, bf16x8 *vt) __attribute__((always_inline)) {
+    const uint8_t *base = stage_mem(stage);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -252,16 +275,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto compute = [&](auto stage, int pr, int okbits, MfmaAttnPairState *st) __attribute__((always_inline)) {
     u32x4 ka[4], kb[4];
     bf16x8 vt[8];
-    lread(stage, ka, kb, vt);
+    lread_k(stage, ka, kb);
     const int tok0 = 32 * pr;
     const bool oka = okbits & 1, okb = okbits & 2;
     if constexpr (CG == 2) {
       // both groups in one step (a group past its causal bound is fully masked)
       const bool full0 = tok0 + 32 <= lim_min[0] && oka && okb;
       const bool full1 = tok0 + 32 <= lim_min[1] && oka && okb;
-      pair_step_x2(st[0], st[1], qb[0], qb[1], ka, kb, vt, tok0, oka ? lim[0] : 0, okb ? lim[0] : 0, !full0,
-                   oka ? lim[1] : 0, okb ? lim[1] : 0, !full1, sl2, r);
+      pair_step_x2(st[0], st[1], qb[0], qb[1], ka, kb, [&]() __attribute__((always_inline)) { lread_v(stage, vt); },
+                   vt, tok0, oka ? lim[0] : 0, okb ? lim[0] : 0, !full0, oka ? lim[1] : 0, okb ? lim[1] : 0, !full1,
+                   sl2, r);
     } else {
+      lread_v(stage, vt);
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
         if (tok0 < kend[cg]) {
@@ -280,7 +305,85 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
-  if (kDma && npair > 0) {
+  if (kDma && CG == 2 && npair > 0) {
+    // Software-pipelined: iteration X takes the softmax and PV products of
+    // pair X while the score products of pair X + 1 run, so the two column
+    // groups' softmax chains overlap matrix work.  Pair X lands in stage
+    // X % 4.  At the top of iteration X each thread waits for its own loads
+    // of pair X + 1 (those of X + 2 may stay in flight: kChunksPerThread
+    // loads) and the barrier covers every thread's; the loads of pair X + 3
+    // then go into stage (X + 3) % 4, whose last reads (V of X - 1, K of
+    // X - 1) came before that barrier.  Pair indices past the end re-load
+    // the last pair (valid data whose scores are never used), so every
+    // iteration has the same shape.
+    int ok[4];
+    ok[0] = dma(0, S0());
+    ok[1] = dma(1, S1());
+    ok[2] = dma(2, S2());
+    ok[3] = 0;
+    float x0[8], x1[8];  // scores of the pair the next iteration finishes
+    vm_wait<2 * kChunksPerThread>();
+    workgroup_barrier();
+    {
+      u32x4 ka[4], kb[4];
+      lread_k(S0(), ka, kb);
+      MfmaAttnPairState::scores(qb[0], ka, kb, x0);
+      MfmaAttnPairState::scores(qb[CG - 1], ka, kb, x1);
+    }
+    auto piter = [&](int X, auto cur, auto nxt, auto ld) __attribute__((always_inline)) -> bool {
+      vm_wait<kChunksPerThread>();
+      workgroup_barrier();
+      ok[decltype(ld)::value] = dma(X + 3, ld);
+      bf16x8 vt[8];
+      u32x4 ka[4], kb[4];
+      lread_v(cur, vt);
+      lread_k(nxt, ka, kb);
+      const int okbits = ok[decltype(cur)::value];
+      const int tok0 = 32 * X;
+      const bool oka = okbits & 1, okb = okbits & 2;
+      const bool full0 = tok0 + 32 <= lim_min[0] && oka && okb;
+      const bool full1 = tok0 + 32 <= lim_min[CG - 1] && oka && okb;
+      const int ta = tok0 + 4 * r, tb = tok0 + 16 + 4 * r;
+      if (!full0) {
+        const int la = oka ? lim[0] : 0, lb = okb ? lim[0] : 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x0[v] = ta + v < la ? x0[v] : kNegInf;
+          x0[4 + v] = tb + v < lb ? x0[4 + v] : kNegInf;
+        }
+      }
+      if (!full1) {
+        const int la = oka ? lim[CG - 1] : 0, lb = okb ? lim[CG - 1] : 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x1[v] = ta + v < la ? x1[v] : kNegInf;
+          x1[4 + v] = tb + v < lb ? x1[4 + v] : kNegInf;
+        }
+      }
+      st[0].raise_max(x0, sl2);
+      st[CG - 1].raise_max(x1, sl2);
+      float y0[8], y1[8];
+      MfmaAttnPairState::scores(qb[0], ka, kb, y0);
+      MfmaAttnPairState::scores(qb[CG - 1], ka, kb, y1);
+      bf16x8 h0, l0, h1, l1;
+      st[0].weights(x0, sl2, h0, l0);
+      st[0].pv(vt, h0, l0);
+      st[CG - 1].weights(x1, sl2, h1, l1);
+      st[CG - 1].pv(vt, h1, l1);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        x0[v] = y0[v];
+        x1[v] = y1[v];
+      }
+      return X + 1 < npair;
+    };
+    for (int X = 0;; X += 4) {
+      if (!piter(X, S0(), S1(), S3())) break;
+      if (!piter(X + 1, S1(), S2(), S0())) break;
+      if (!piter(X + 2, S2(), S3(), S1())) break;
+      if (!piter(X + 3, S3(), S0(), S2())) break;
+    }
+  } else if (kDma && npair > 0) {
     // Pair X lands in stage X % 4; its loads are issued three pairs ahead,
     // right after the barrier that ends every read of that stage's previous
     // pair.  Before pair X is read each thread waits for its own loads of it
