@@ -183,11 +183,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // that the swizzled layout below puts in its slot: in a K tile slot col of
   // row t holds chunk col ^ t, in a V tile chunk 2 ((col / 2) ^ (t & 7)) +
   // (col & 1).  Same tiles, masking bits and clamping as gload.
-  // With four waves and blocks of 16 tokens or more, load k of wave w is tile
-  // k, rows 4w .. 4w + 3 (one row per 16 lanes), and a tile's 16 rows are
-  // contiguous: each load is a wave-uniform tile base in scalar registers
-  // plus a per-lane byte offset that never changes.
-  constexpr bool kRowsContig = NW == 4 && BSZ >= 16;
+  // With four waves, load k of wave w is tile k, rows 4w .. 4w + 3 (one row
+  // per 16 lanes), all in one half of the tile (rows 0-7 or 8-15, contiguous
+  // at every block size): each load is a wave-uniform tile base in scalar
+  // registers plus a per-lane byte offset that never changes.
+  constexpr bool kRowsContig = NW == 4;
   const int trow = 4 * w + (lane >> 4), tcol = lane & 15;
   const uint32_t off_k = (uint32_t)(trow * D + (tcol ^ trow) * 8) * 2u;
   const uint32_t off_v = (uint32_t)(trow * D + ((((tcol >> 1) ^ (trow & 7)) << 1) | (tcol & 1)) * 8) * 2u;
@@ -202,10 +202,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if constexpr (kRowsContig) {
       uint8_t *sm = stage_mem(st) + w * 1024;
       const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kc), *vb8 = reinterpret_cast<const uint8_t *>(vc);
-      load_lds16_sv(kb8 + ra.lo * 2, off_k, sm + 0 * 4096);
-      load_lds16_sv(vb8 + ra.lo * 2, off_v, sm + 1 * 4096);
-      load_lds16_sv(kb8 + rb.lo * 2, off_k, sm + 2 * 4096);
-      load_lds16_sv(vb8 + rb.lo * 2, off_v, sm + 3 * 4096);
+      // rows 8-15 start 8 rows after their own base (the same address as
+      // tr.lo when the block holds the whole tile)
+      const int64_t ba = w < 2 ? ra.lo : ra.hi - 8 * D, bb = w < 2 ? rb.lo : rb.hi - 8 * D;
+      load_lds16_sv(kb8 + ba * 2, off_k, sm + 0 * 4096);
+      load_lds16_sv(vb8 + ba * 2, off_v, sm + 1 * 4096);
+      load_lds16_sv(kb8 + bb * 2, off_k, sm + 2 * 4096);
+      load_lds16_sv(vb8 + bb * 2, off_v, sm + 3 * 4096);
     } else {
       const int col = lane & 15;
 #pragma unroll
