@@ -8,10 +8,11 @@
 // sits at position pos = seq_lens[b] - n_b + i and attends to tokens
 // 0 .. pos through the block table.
 //
-// MFMA kernel: a wave serves 16 columns = (16 / g) consecutive chunk tokens x
-// the g query heads of one KV head, so every K/V tile it reads is shared by
-// the whole GQA group; eight waves of a workgroup cover consecutive tokens and
-// walk the same key blocks, in ascending order with per-column causal bounds.
+// MFMA kernel: a group of 16 columns = (16 / g) consecutive chunk tokens x the
+// g query heads of one KV head, so every K/V tile read is shared by the whole
+// GQA group; each wave owns two such groups, and the four waves of a
+// workgroup cover consecutive tokens and walk the same key blocks, in
+// ascending order with per-column causal bounds.
 #include <type_traits>
 
 #include "attn_core.h"
@@ -43,11 +44,12 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // A workgroup of NW waves serves NW * CG * 16 / g consecutive chunk tokens of
 // one KV head.  Wave w owns CG groups of 16 columns (16 / g tokens x the g
 // query heads each).  Keys are taken two blocks (32 keys) at a time: the
-// workgroup loads each pair of K/V tiles from global memory ONCE into LDS,
-// three pairs ahead through registers, and every wave reads its MFMA operands
-// from there, so global/L2 traffic falls by the workgroup's column count.
+// workgroup loads each pair of K/V tiles from global memory ONCE into LDS
+// (bf16: straight into a four-stage ring; FP8: through registers into a
+// three-stage ring), and every wave reads its MFMA operands from there, so
+// global/L2 traffic falls by the workgroup's column count.
 //
-// LDS holds three pair stages of four 4 KB tiles (K_a, V_a, K_b, V_b).  In a
+// An LDS stage holds four 4 KB tiles (K_a, V_a, K_b, V_b).  In a
 // K tile the 16-byte chunk k of token t sits at chunk t*16 + (k ^ t), so the
 // K operand reads (token c, chunk 4i + r) touch 16 distinct bank groups per
 // 16 lanes.  A V tile is read with ds_read_b64_tr_b16, which hands lane
@@ -63,8 +65,8 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // operations of the loop and a wait for one pair never waits on table reads.
 //
 // Within a head the query tiles go heaviest (last in the chunk) first; a
-// column group skips the pairs past its causal bound, but every wave joins
-// every barrier.  grid = ntiles * Hkv * B workgroups, ntiles =
+// column group past its causal bound is fully masked (every wave joins every
+// barrier).  grid = ntiles * Hkv * B workgroups, ntiles =
 // ceil(max_query_len / (NW * CG * 16 / g)).  The block size BSZ is a template
 // argument so the table walk folds to constants for each supported size.
 //
