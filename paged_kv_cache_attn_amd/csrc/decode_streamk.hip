@@ -483,7 +483,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
   constexpr int kPer = 2;  // the launch uses g * kD / 2 threads: two elements each
-  const int gi = blockIdx.x;
+  // the same range numbering as the main kernel, so this workgroup runs on
+  // the XCD that wrote range gi's pieces (and, but at XCD edges, gi - 1's)
+  const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const int g = p.num_heads / p.num_kv_heads;
   const int gp = gi > 0 ? gi - 1 : 0;
   const int4 dsc = p.sk_desc[gi];
