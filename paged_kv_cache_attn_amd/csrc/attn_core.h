@@ -71,6 +71,8 @@ struct TileMap {
   // Branch-free: both table reads are issued for every block size (for
   // bs >= 16 the second one repeats the first address), so a loop that calls
   // this stays one basic block.
+  // Table index of the (first) entry that tile j lives in.
+  __device__ __forceinline__ int first_index(int j) const { return sh < 0 ? 2 * j : j >> (sh & 31); }
   template <typename TablePtr>
   __device__ __forceinline__ bool entries(TablePtr table, int j, int nblk_tab, int &e0, int &e1) const {
     const bool halves = sh < 0;
@@ -96,14 +98,28 @@ struct TileMap {
 };
 
 // The operands of one tile (see load_kv_tile_d128) from its two row bases.
+// `stream` (wave-uniform) picks non-temporal loads, for a tile no other row
+// of the call reads, over ordinary ones, which leave it in the L2 for the
+// rows that share its block.
 __device__ __forceinline__ void load_kv_tile_rows(KVTile &t, const uint16_t *kc, const uint16_t *vc,
-                                                  const TileRows &tr, int r, int c) {
+                                                  const TileRows &tr, int r, int c, bool stream) {
   const int64_t kr = (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t.k[i] = ld16(kc + kr + 32 * i + 8 * r);
   const int64_t vr = r < 2 ? tr.lo : tr.hi;  // tokens 4r .. 4r+3 share a half
+  if (stream) {
+    // (the empty statements keep the compiler from merging the two load
+    // sequences into one, which would drop the non-temporal hint)
+    asm volatile("");
 #pragma unroll
-  for (int v = 0; v < 4; ++v) t.v[v] = ld16(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+    for (int i = 0; i < 4; ++i) t.k[i] = ld16_stream(kc + kr + 32 * i + 8 * r);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t.v[v] = ld16_stream(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+    asm volatile("");
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.k[i] = ld16(kc + kr + 32 * i + 8 * r);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t.v[v] = ld16(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+  }
 }
 
 // -- FP8 (E4M3) tiles ------------------------------------------------------------
@@ -121,13 +137,22 @@ struct KVTile8 {
 };
 
 __device__ __forceinline__ void load_kv_tile_rows_fp8(KVTile8 &t, const uint8_t *kc, const uint8_t *vc,
-                                                      const TileRows &tr, int r, int c) {
+                                                      const TileRows &tr, int r, int c, bool stream) {
   const int64_t kr = (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128 + 16 * r;
-  t.k[0] = ld16(kc + kr);
-  t.k[1] = ld16(kc + kr + 64);
   const int64_t vr = r < 2 ? tr.lo : tr.hi;
+  if (stream) {
+    asm volatile("");  // see load_kv_tile_rows
+    t.k[0] = ld16_stream(kc + kr);
+    t.k[1] = ld16_stream(kc + kr + 64);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) t.v[v] = ld8(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+    for (int v = 0; v < 4; ++v) t.v[v] = ld8_stream(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+    asm volatile("");
+  } else {
+    t.k[0] = ld16(kc + kr);
+    t.k[1] = ld16(kc + kr + 64);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t.v[v] = ld8(vc + vr + ((4 * r + v) & 7) * 128 + 8 * c);
+  }
 }
 
 __device__ __forceinline__ KVTile expand_fp8_tile(const KVTile8 &s) {
@@ -160,8 +185,8 @@ struct KVFormat<false> {
   using Elem = uint16_t;
   using Raw = KVTile;
   static __device__ __forceinline__ void load(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
-                                              int c) {
-    load_kv_tile_rows(t, kc, vc, tr, r, c);
+                                              int c, bool stream) {
+    load_kv_tile_rows(t, kc, vc, tr, r, c, stream);
   }
   static __device__ __forceinline__ KVTile expand(const Raw &t) { return t; }
   static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r);
@@ -171,8 +196,8 @@ struct KVFormat<true> {
   using Elem = uint8_t;
   using Raw = KVTile8;
   static __device__ __forceinline__ void load(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
-                                              int c) {
-    load_kv_tile_rows_fp8(t, kc, vc, tr, r, c);
+                                              int c, bool stream) {
+    load_kv_tile_rows_fp8(t, kc, vc, tr, r, c, stream);
   }
   static __device__ __forceinline__ KVTile expand(const Raw &t) { return expand_fp8_tile(t); }
   static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r) {

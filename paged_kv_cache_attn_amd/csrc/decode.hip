@@ -83,13 +83,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
   MfmaAttnState st;
   st.init();
 
+  // The row's tiles stream through the caches (non-temporal loads) unless
+  // the previous or the next sequence starts with the same block (forked or
+  // prefix-sharing sequences sit next to each other in a batch): then they
+  // are loaded so that they stay in the L2 for those rows.
+  bool keep = false;
+  if (nblk_tab > 0) {
+    const int t0 = table[0];
+    if (b > 0 && clamp_len(p.seq_lens[b - 1], p.max_len_cap) > 0) keep |= table[-p.max_blocks_per_seq] == t0;
+    if (b + 1 < p.num_seqs && clamp_len(p.seq_lens[b + 1], p.max_len_cap) > 0)
+      keep |= table[p.max_blocks_per_seq] == t0;
+  }
+  const bool stream = !__builtin_amdgcn_readfirstlane((int)keep);
+
   // 16-token tile j (any supported block size).  An out-of-range table entry
   // is never dereferenced: the tile is read from block 0 and fully masked.
   auto load = [&](int j, typename F::Raw &t, int &lim) {
     int e0, e1;
     const bool ok = map.entries(table, j, nblk_tab, e0, e1);
     lim = ok ? L : 0;
-    F::load(t, kc, vc, map.rows(e0, e1, kh), r, c);
+    F::load(t, kc, vc, map.rows(e0, e1, kh), r, c, stream);
   };
 
   // Two-deep software pipeline: the next tile's loads are in flight while

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int s_prow[kStreamKTabCache + 1]; // row (b * Hkv + kh) of each position, -1 past the end
   __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
   __shared__ int2 s_ln[kStreamKTabCache];      // {sequence length, blocks of the row} of each position
+  __shared__ int s_keep[kStreamKTabCache];     // 1: a neighbouring row uses the position's block
   __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
   __shared__ int s_brid[NW][2];                // its row, b * Hkv + kh
   __shared__ int s_bnb[NW][2];                 // its blocks
@@ -200,14 +201,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
                                   (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
       const TileRows tr = map.rows(e0, e1, kh);
+      // A tile read by this row only streams through the caches (non-temporal
+      // loads); one whose block the previous or the next sequence also uses at
+      // the same place (forked or prefix-sharing sequences, which sit next to
+      // each other in a batch) is loaded so that it stays in the L2 for them.
+      int keep = 0;
+      if (ok) {
+        const int i0 = map.first_index(j), bsz = p.block_size;
+        const int32_t *tb = p.block_tables + (int64_t)lo * p.max_blocks_per_seq;
+        if (lo > 0 && i0 < (s_len[lo - 1] + bsz - 1) / bsz) keep |= tb[i0 - p.max_blocks_per_seq] == e0;
+        if (lo + 1 < B && i0 < (s_len[lo + 1] + bsz - 1) / bsz) keep |= tb[i0 + p.max_blocks_per_seq] == e0;
+      }
       s_rows[pos - s] = ok ? int2{(int)(tr.lo >> 10), (int)(tr.hi >> 10)} : int2{-1, 0};
       s_prow[pos - s] = lo * Hkv + kh;
       s_pj[pos - s] = j;
       s_ln[pos - s] = int2{s_len[lo], nb};
+      s_keep[pos - s] = keep;
       if constexpr (MODE == kPlanOnly) {
         const int64_t at = (int64_t)gi * p.plan_stride + (pos - s);
         p.plan_rec[at] = int4{s_rows[pos - s].x, s_rows[pos - s].y, lo * Hkv + kh, j};
-        p.plan_rec2[at] = int2{s_len[lo], nb};
+        p.plan_rec2[at] = int2{s_len[lo], nb | (keep ? kKeepTile : 0)};
       }
     }
     if constexpr (MODE == kPlanOnly) return;
@@ -255,7 +268,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         s_rows[li] = ok ? int2{ra[k].x, ra[k].y} : int2{-1, 0};
         s_prow[li] = ok ? ra[k].z : 0;
         s_pj[li] = ok ? ra[k].w : 0;
-        s_ln[li] = rb[k];
+        s_ln[li] = int2{rb[k].x, rb[k].y & ~kKeepTile};
+        s_keep[li] = (rb[k].y & kKeepTile) != 0;
       }
     }
     if (tid == 0) s_prow[e - s] = -1;
@@ -293,7 +307,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool ok = u.x >= 0;
     sl.lim = ok ? s_ln[li].x : 0;
     // a masked tile reads the first rows of the cache
-    F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c);
+    const bool stream = __builtin_amdgcn_readfirstlane(s_keep[li]) == 0;
+    F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c, stream);
     const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
     if (__builtin_amdgcn_readfirstlane((int)need_q))
       F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);

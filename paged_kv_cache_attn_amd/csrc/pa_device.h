@@ -158,6 +158,15 @@ __device__ __forceinline__ unsigned xcd_contiguous(unsigned L, unsigned N) {
 // 16-byte global load/store through a plain vector type (global_load_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+// The same loads with the non-temporal hint, for data read once per call (the
+// K/V stream): they leave the L2 to what is reused across calls and kernels
+// (plans, partial results, queries).
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 ld8_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
 
 // -- FP8 E4M3 (OCP: bias 7, no infinities, S.1111.111 = NaN, max 448) ------
 // Two codes (bytes 0-1 of w, or bytes 2-3 with kHigh) to two bf16, exactly:

@@ -47,6 +47,10 @@ hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs,
                              int elem_bytes, hipStream_t stream);
 
 // Everything one decode launch needs.  Sizes are validated; pointers are device.
+// Bit of a plan record's block count marking a tile whose block a neighbouring
+// row also uses (its loads keep the tile in the L2).
+constexpr int kKeepTile = 1 << 30;
+
 struct DecodeParams {
   void *out;
   int out_bf16;            // 0: fp32 output, 1: bf16 output
@@ -78,7 +82,8 @@ struct DecodeParams {
   // a decode plan (balanced path; nullptr: each launch stages its own range)
   int4 *plan_hdr;          // [ranges] {range start, range end, total blocks T, ranges used G}
   int4 *plan_rec;          // [ranges][plan_stride] {tile row 0 / 1024, tile row 8 / 1024, row, j}
-  int2 *plan_rec2;         // [ranges][plan_stride] {sequence length, blocks of the row}
+  int2 *plan_rec2;         // [ranges][plan_stride] {sequence length, blocks of the row
+                           //   | kKeepTile if a neighbouring row uses the tile's block}
   int plan_stride;         // positions per range in the plan (>= every range's size)
 };
 
