@@ -300,7 +300,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   auto load_slot = [&](int li, Slot &sl, int dist) {
     const int lp = li - dist;
-    li = li < le ? li : le - 1;  // past the share: reload the last tile (unused)
+    // past the share: nothing to load (a dummy load there would be a memory
+    // round trip the combine below waits for, since its registers are reused)
+    if (li >= le) {
+      sl.lim = 0;
+      return;
+    }
     const int2 u = s_rows[li];
     const int row = s_prow[li];
     const int b = row / Hkv, kh = row - b * Hkv;
