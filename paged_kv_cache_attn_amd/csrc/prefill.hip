@@ -318,16 +318,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // of pair X + 1 (those of X + 2 may stay in flight: kChunksPerThread
     // loads) and the barrier covers every thread's; the loads of pair X + 3
     // then go into stage (X + 3) % 4, whose last reads (V of X - 1, K of
-    // X - 1) came before that barrier.  Pair indices past the end re-load
-    // the last pair (valid data whose scores are never used), so every
-    // iteration has the same shape.
-    int ok[4];
+    // X - 1) came before that barrier.  Pairs past the end are not loaded
+    // (a load there would hold the workgroup's end back by a memory round
+    // trip); the last iteration then reads stale K tiles for a next pair
+    // whose scores are never used, and near the end every load in flight is
+    // waited for, since fewer follow the pair needed.
+    int ok[4] = {0, 0, 0, 0};
     ok[0] = dma(0, S0());
-    ok[1] = dma(1, S1());
-    ok[2] = dma(2, S2());
-    ok[3] = 0;
+    if (npair > 1) ok[1] = dma(1, S1());
+    if (npair > 2) ok[2] = dma(2, S2());
     float x0[8], x1[8];  // scores of the pair the next iteration finishes
-    vm_wait<2 * kChunksPerThread>();
+    if (npair > 2)
+      vm_wait<2 * kChunksPerThread>();
+    else
+      vm_wait<0>();
     workgroup_barrier();
     {
       u32x4 ka[4], kb[4];
@@ -336,9 +340,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       MfmaAttnPairState::scores(qb[CG - 1], ka, kb, x1);
     }
     auto piter = [&](int X, auto cur, auto nxt, auto ld) __attribute__((always_inline)) -> bool {
-      vm_wait<kChunksPerThread>();
+      if (X + 2 < npair)
+        vm_wait<kChunksPerThread>();
+      else
+        vm_wait<0>();
       workgroup_barrier();
-      ok[decltype(ld)::value] = dma(X + 3, ld);
+      if (X + 3 < npair) ok[decltype(ld)::value] = dma(X + 3, ld);
       bf16x8 vt[8];
       u32x4 ka[4], kb[4];
       lread_v(cur, vt);
