@@ -387,6 +387,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         x0[v] = y0[v];
         x1[v] = y1[v];
       }
+      // Scheduling of the block above (from the last rescale test on): its 48
+      // MFMAs (16 score products of pair X + 1, 32 PV products of pair X) each
+      // followed by up to three VALU instructions (weights, exponentials,
+      // hi/lo split), so the vector work issues while the matrix unit is busy
+      // instead of in runs between MFMA runs.  Only placement changes.
+#pragma unroll
+      for (int i = 0; i < 48; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // three VALU (incl. transcendental)
+      }
       return X + 1 < npair;
     };
     for (int X = 0;; X += 4) {
