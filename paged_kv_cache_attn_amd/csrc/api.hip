@@ -63,7 +63,7 @@ struct DecodePlan {
   size_t off_part = 0, off_ml = 0, off_desc = 0, workspace_bytes = 0;
   // the balanced path's plan buffer: header, records, records2
   int plan_stride = 0;
-  size_t plan_off_rec = 0, plan_off_rec2 = 0, plan_bytes = 0;
+  size_t plan_off_rec = 0, plan_off_rec2 = 0, plan_off_desc = 0, plan_bytes = 0;
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -111,7 +111,8 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
                          : (int)std::min<int64_t>(ceil_div(t_upper, pl.ranges) + 1, pa::kStreamKTabCache);
     pl.plan_off_rec = align256((size_t)pl.ranges * 4 * sizeof(int));
     pl.plan_off_rec2 = pl.plan_off_rec + align256((size_t)pl.ranges * pl.plan_stride * 4 * sizeof(int));
-    pl.plan_bytes = pl.plan_off_rec2 + align256((size_t)pl.ranges * pl.plan_stride * 2 * sizeof(int));
+    pl.plan_off_desc = pl.plan_off_rec2 + align256((size_t)pl.ranges * pl.plan_stride * 2 * sizeof(int));
+    pl.plan_bytes = pl.plan_off_desc + align256((size_t)pl.ranges * 4 * sizeof(int));
     return pl;
   }
   const int64_t P = effective_partition(partition_size, block_size);
@@ -274,6 +275,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
       p.plan_hdr = reinterpret_cast<int4 *>(pb);
       p.plan_rec = reinterpret_cast<int4 *>(pb + plan.plan_off_rec);
       p.plan_rec2 = reinterpret_cast<int2 *>(pb + plan.plan_off_rec2);
+      p.sk_desc = reinterpret_cast<int4 *>(pb + plan.plan_off_desc);  // the plan's merge descriptors
       p.plan_stride = plan.plan_stride;
     }
     return launch_status(pa::launch_decode_streamk(p, s));
@@ -352,6 +354,7 @@ int paged_attn_decode_plan(void *plan_buf, size_t plan_bytes, int32_t kv_dtype, 
   p.plan_hdr = reinterpret_cast<int4 *>(pb);
   p.plan_rec = reinterpret_cast<int4 *>(pb + plan.plan_off_rec);
   p.plan_rec2 = reinterpret_cast<int2 *>(pb + plan.plan_off_rec2);
+  p.sk_desc = reinterpret_cast<int4 *>(pb + plan.plan_off_desc);
   p.plan_stride = plan.plan_stride;
   return launch_status(pa::launch_decode_streamk_plan(p, static_cast<hipStream_t>(stream)));
 }

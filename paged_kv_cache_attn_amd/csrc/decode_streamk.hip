@@ -160,17 +160,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     T = s_pref[B];
     G = ranges_used((int)gridDim.x, T, R);
 
-    if constexpr (MODE == kFused) {
-      // no split row ends in this range unless the combine below says so
-      if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
-      // -- rows with no tokens get zeros (spread over the workgroups) ---------
-      for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
-        const int b = row / Hkv, kh = row - b * Hkv;
-        if (s_len[b] != 0) continue;
-        for (int idx = tid; idx < g * kD; idx += 64 * NW)
-          store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
-      }
-    }
+    // no split row ends in this range unless the combine below (or, for a
+    // plan, the staging loop) says so
+    if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
 
     s = range_begin(gi, T, G, R);
     e = range_begin(gi + 1, T, G, R);
@@ -218,6 +210,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       s_ln[pos - s] = int2{s_len[lo], nb};
       s_keep[pos - s] = keep;
       if constexpr (MODE == kPlanOnly) {
+        // the split row whose last piece this range holds is the one under
+        // its first position, if that row began in an earlier range and ends
+        // in this one; the plan keeps its merge descriptor, so planned calls
+        // do no range arithmetic after the stream (same thread as the -1
+        // written above: pos == s only for tid 0)
+        if (pos == s && j > 0 && s - j + nb <= e) {
+          const int rs = s - j;
+          const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
+          p.sk_desc[gi] = int4{lo * Hkv + kh, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
+        }
         const int64_t at = (int64_t)gi * p.plan_stride + (pos - s);
         p.plan_rec[at] = int4{s_rows[pos - s].x, s_rows[pos - s].y, lo * Hkv + kh, j};
         p.plan_rec2[at] = int2{s_len[lo], nb | (keep ? kKeepTile : 0)};
@@ -228,31 +230,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __syncthreads();
   } else {
     // -- the staging from the plan: header and records in one round trip ----
-    if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
+    // (the merge descriptors are the plan's own: nothing to reset here)
     if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
     constexpr int kMaxPer = (kStreamKTabCache + 64 * NW - 1) / (64 * NW);
     const int4 h = p.plan_hdr[gi];
     int4 ra[kMaxPer];
     int2 rb[kMaxPer];
+    // every load issued unconditionally (positions past the plan's stride
+    // re-read its last record, unused), so none waits on another
 #pragma unroll
     for (int k = 0; k < kMaxPer; ++k) {
-      const int li = tid + k * 64 * NW;
-      if (li < p.plan_stride) {
-        ra[k] = p.plan_rec[(int64_t)gi * p.plan_stride + li];
-        rb[k] = p.plan_rec2[(int64_t)gi * p.plan_stride + li];
-      }
+      const int li = min(tid + k * 64 * NW, p.plan_stride - 1);
+      ra[k] = p.plan_rec[(int64_t)gi * p.plan_stride + li];
+      rb[k] = p.plan_rec2[(int64_t)gi * p.plan_stride + li];
     }
+    asm volatile("" ::: "memory");  // issue those loads before the header is tested
     s = h.x;
     e = h.y;
     T = h.z;
     G = h.w;
-    // rows with no tokens get zeros (spread over the workgroups)
-    for (int row = gi; row < B * Hkv; row += (int)gridDim.x) {
-      const int b = row / Hkv, kh = row - b * Hkv;
-      if (clamp_len(p.seq_lens[b], p.max_len_cap) != 0) continue;
-      for (int idx = tid; idx < g * kD; idx += 64 * NW)
-        store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
-    }
+    // (rows with no tokens get their zeros from the merge kernel, so this
+    // prologue has one memory round trip: header and records)
     if (gi >= G || G > (int)gridDim.x || s < 0 || s >= e || e > T || e - s > p.plan_stride) return;
     // The plan is trusted for its values but not for its bounds: a record
     // whose tile lies outside the cache or whose row is not a (sequence, KV
@@ -431,7 +429,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool whole = rs >= s && rs + nb <= e;
     const int slot = rs <= s ? 0 : 1;
     const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
-    if (!whole && slot == 0 && rs + nb <= e && tid == 0) {
+    if (MODE != kPlanned && !whole && slot == 0 && rs + nb <= e && tid == 0) {
       // this range holds the last piece of a row that began in an earlier one
       const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
       p.sk_desc[gi] = int4{row, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
@@ -509,6 +507,8 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   const int g = p.num_heads / p.num_kv_heads;
   const int gp = gi > 0 ? gi - 1 : 0;
   const int4 dsc = p.sk_desc[gi];
+  const int nrows = p.num_seqs * p.num_kv_heads;
+  const int len0 = gi < nrows ? p.seq_lens[gi / p.num_kv_heads] : 1;  // with the descriptor: one round trip
   // speculative: (gp, slot 0), (gp, slot 1), (gi, slot 0) for both elements
   float sm[3][kPer], sl[3][kPer], so[3][kPer];
 #pragma unroll
@@ -524,9 +524,20 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
     }
   }
   asm volatile("" ::: "memory");  // keep those loads ahead of the branch below
+  // rows with no tokens (no piece, no range) get zeros, spread over the
+  // workgroups: row gi, gi + grid, ...
+  for (int zr = gi; zr < nrows; zr += (int)gridDim.x) {
+    if (clamp_len(zr == gi ? len0 : p.seq_lens[zr / p.num_kv_heads], p.max_len_cap) != 0) continue;
+    const int b = zr / p.num_kv_heads, kh = zr - b * p.num_kv_heads;
+    for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x)
+      store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
+  }
+  // a planned call's descriptors come from the plan: trusted for their
+  // values, not for their bounds (a stale or foreign plan gives wrong
+  // results, never an access out of bounds)
   const int row = dsc.x;
-  if (row < 0) return;
-  const int g_first = dsc.y, s_first = dsc.z, nc = dsc.w;
+  if (row < 0 || row >= nrows) return;
+  const int g_first = min(max(dsc.y, 0), gi), s_first = dsc.z & 1, nc = gi - g_first + 1;
   const int b = row / p.num_kv_heads, kh = row - b * p.num_kv_heads;
   const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
   if (nc == 2) {
