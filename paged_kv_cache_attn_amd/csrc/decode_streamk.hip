@@ -7,12 +7,13 @@
 // streams the same number of 8 KB K+V tiles whatever the length mix.  A
 // range covers whole rows, whose output it writes directly, and at most two
 // partial rows at its ends, for which it leaves (max, sum, unnormalised
-// output) in the workspace with plain stores, and a range that holds the
-// last piece of such a row writes a descriptor of it.  A second, small
+// output) in the workspace with plain stores; a descriptor per range names
+// the split row whose last piece the range holds (written by the range
+// itself, or, for a planned call, taken from the plan).  A second, small
 // kernel (one workgroup per range) merges the pieces of those rows, in
 // ascending range order, with the online-softmax merge rule (Lecture 16 "LLM
-// Serving (1)" §3.3); the kernel boundary makes the pieces visible across
-// XCDs.  The split depends
+// Serving (1)" §3.3), and writes the zeros of rows with no tokens; the
+// kernel boundary makes the pieces visible across XCDs.  The split depends
 // only on logical block positions, so results are bit-identical under any
 // physical block permutation.
 #include "attn_core.h"
