@@ -419,83 +419,106 @@ int oracle_contiguous_attention(double *out, const double *q, const double *K,
 }
 
 /*
- * The pages' own algorithm for one decode row, kept to pin the definition
- * above against it: the kernel loop of Month 2 §5.4 (visit logical blocks,
- * look up the physical block, score the block, update a running max, a
- * running sum and a running output with the rescale factor
- * exp(old_max - new_max)), run independently over partitions of
- * `partition_blocks` logical blocks, then the partitions' (max, sum, output)
- * triples merged by the same rule (Lecture 16 §3.3: attention is associative
- * and commutative under the online-softmax merge).  `visit_order` lists the
- * logical blocks of each partition in the order to visit them (any order
- * gives the same real number); NULL means ascending.  Only valid offsets of
- * the last block are scored (the ceil reading of the loop bound).
+ * A softmax summary of a set of keys for one query row (Lecture 16 §3.3:
+ * attention over blocks is combined by the online-softmax rule, which is
+ * associative and commutative): top = the largest score in the set, mass =
+ * sum of exp(score - top), vec[d] = sum of exp(score - top) * value[d].  An
+ * empty set has top = -inf, mass = 0, vec = 0.  The attention output over the
+ * set is vec / mass.
+ */
+typedef struct {
+  double top, mass;
+  double *vec; /* D entries, owned by the caller */
+} summary;
+
+static void summary_clear(summary *s, int D) {
+  s->top = -INFINITY;
+  s->mass = 0.0;
+  for (int d = 0; d < D; ++d) s->vec[d] = 0.0;
+}
+
+/* dst := summary of (dst's keys together with src's keys).  Each side is
+ * re-expressed relative to the larger top, exp(top_side - top_both), and
+ * the two are added. */
+static void summary_absorb(summary *dst, const summary *src, int D) {
+  if (src->top == -INFINITY) return; /* nothing to add */
+  if (dst->top == -INFINITY) {
+    dst->top = src->top;
+    dst->mass = src->mass;
+    for (int d = 0; d < D; ++d) dst->vec[d] = src->vec[d];
+    return;
+  }
+  double both = dst->top > src->top ? dst->top : src->top;
+  double wd = exp(dst->top - both), ws = exp(src->top - both);
+  dst->mass = dst->mass * wd + src->mass * ws;
+  for (int d = 0; d < D; ++d) dst->vec[d] = dst->vec[d] * wd + src->vec[d] * ws;
+  dst->top = both;
+}
+
+/* The summary of the `valid` keys of one physical block for query q. */
+static void summary_of_block(summary *s, double *scores, const void *q, int64_t q_off,
+                             const void *k_cache, const void *v_cache, int dtype, int32_t phys,
+                             int valid, int kh, int Hkv, int D, int bs, double scale) {
+  summary_clear(s, D);
+  for (int o = 0; o < valid; ++o) {
+    int64_t at = cache_index(phys, kh, o, 0, Hkv, bs, D);
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, dtype) * elem(k_cache, at + d, dtype);
+    scores[o] = scale * dot;
+    if (scores[o] > s->top) s->top = scores[o];
+  }
+  for (int o = 0; o < valid; ++o) {
+    double w = exp(scores[o] - s->top);
+    int64_t at = cache_index(phys, kh, o, 0, Hkv, bs, D);
+    s->mass += w;
+    for (int d = 0; d < D; ++d) s->vec[d] += w * elem(v_cache, at + d, dtype);
+  }
+}
+
+/*
+ * The blockwise form of one decode row, kept to pin the plain definition
+ * above against the pages' claim that blockwise attention reaches the same
+ * result (Lecture 7 §4.2; Month 2 §5.4 walks the logical blocks through the
+ * block table; Lecture 16 §3.3 gives the merge rule).  The row's logical
+ * blocks are grouped into partitions of `partition_blocks` consecutive
+ * blocks.  Every block is reduced to its own summary, the summaries of a
+ * partition are absorbed into the partition's summary in the order
+ * `visit_order` lists them (NULL: ascending; any order reaches the same real
+ * number), and the partitions' summaries are then absorbed in ascending
+ * order.  Only the valid offsets of the last block are scored (the ceil
+ * reading of the loop bound).
  */
 int oracle_blockwise_decode_row(double *out, const void *q, int64_t q_off,
                                 const void *k_cache, const void *v_cache, int dtype,
                                 const int32_t *table, int n_keys, int kh, int Hkv,
                                 int D, int bs, int num_blocks, double scale,
                                 int partition_blocks, const int32_t *visit_order) {
-  if (!out || !q || !k_cache || !v_cache || !table || partition_blocks <= 0) return ORC_ERR_ARG;
+  if (!out || !q || !k_cache || !v_cache || !table || partition_blocks <= 0 || D <= 0) return ORC_ERR_ARG;
   for (int d = 0; d < D; ++d) out[d] = 0.0;
   if (n_keys <= 0) return ORC_OK;
   int n_blocks = (n_keys + bs - 1) / bs;
-  int n_parts = (n_blocks + partition_blocks - 1) / partition_blocks;
-  double *pm = (double *)malloc(sizeof(double) * n_parts);
-  double *pl = (double *)malloc(sizeof(double) * n_parts);
-  double *po = (double *)calloc((size_t)n_parts * D, sizeof(double));
-  double sc[1024];
-  if (!pm || !pl || !po || bs > 1024) {
-    free(pm); free(pl); free(po);
-    return bs > 1024 ? ORC_ERR_ARG : ORC_ERR_NOMEM;
-  }
+  double *mem = (double *)calloc((size_t)3 * D + (size_t)bs, sizeof(double));
+  if (!mem) return ORC_ERR_NOMEM;
+  summary whole = {0, 0, mem}, part = {0, 0, mem + D}, blk = {0, 0, mem + 2 * D};
+  double *scores = mem + 3 * D;
+  summary_clear(&whole, D);
   int rc = ORC_OK;
-  for (int p = 0; p < n_parts && rc == ORC_OK; ++p) {
-    double run_max = -INFINITY, run_sum = 0.0;
-    double *acc = po + (int64_t)p * D;
-    int first = p * partition_blocks;
+  for (int first = 0; first < n_blocks && rc == ORC_OK; first += partition_blocks) {
     int count = n_blocks - first < partition_blocks ? n_blocks - first : partition_blocks;
+    summary_clear(&part, D);
     for (int k = 0; k < count; ++k) {
       int j = visit_order ? visit_order[first + k] : first + k;
       if (j < first || j >= first + count) { rc = ORC_ERR_ARG; break; }
       int32_t phys = table[j];
       if (phys < 0 || phys >= num_blocks) { rc = ORC_ERR_RANGE; break; }
       int valid = n_keys - j * bs < bs ? n_keys - j * bs : bs;
-      double block_max = -INFINITY;
-      for (int o = 0; o < valid; ++o) {
-        int64_t base = cache_index(phys, kh, o, 0, Hkv, bs, D);
-        double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += elem(q, q_off + d, dtype) * elem(k_cache, base + d, dtype);
-        sc[o] = scale * dot;
-        if (sc[o] > block_max) block_max = sc[o];
-      }
-      double new_max = run_max > block_max ? run_max : block_max;
-      double correction = exp(run_max - new_max); /* exp(-inf) = 0 on the first block */
-      double block_sum = 0.0;
-      for (int d = 0; d < D; ++d) acc[d] *= correction;
-      for (int o = 0; o < valid; ++o) {
-        double e = exp(sc[o] - new_max);
-        block_sum += e;
-        int64_t base = cache_index(phys, kh, o, 0, Hkv, bs, D);
-        for (int d = 0; d < D; ++d) acc[d] += e * elem(v_cache, base + d, dtype);
-      }
-      run_sum = run_sum * correction + block_sum;
-      run_max = new_max;
+      summary_of_block(&blk, scores, q, q_off, k_cache, v_cache, dtype, phys, valid, kh, Hkv, D, bs, scale);
+      summary_absorb(&part, &blk, D);
     }
-    pm[p] = run_max;
-    pl[p] = run_sum;
+    summary_absorb(&whole, &part, D);
   }
-  if (rc == ORC_OK) {
-    double m = -INFINITY, l = 0.0;
-    for (int p = 0; p < n_parts; ++p)
-      if (pm[p] > m) m = pm[p];
-    for (int p = 0; p < n_parts; ++p) {
-      double w = exp(pm[p] - m);
-      l += pl[p] * w;
-      for (int d = 0; d < D; ++d) out[d] += po[(int64_t)p * D + d] * w;
-    }
-    for (int d = 0; d < D; ++d) out[d] /= l;
-  }
-  free(pm); free(pl); free(po);
+  if (rc == ORC_OK)
+    for (int d = 0; d < D; ++d) out[d] = whole.vec[d] / whole.mass;
+  free(mem);
   return rc;
 }

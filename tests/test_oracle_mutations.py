@@ -41,6 +41,10 @@ MUTATIONS = {
     "fp8_search_misses_largest_code": ("for (int c = 0; c < 127; ++c) {\n    double dd", "for (int c = 0; c < 126; ++c) {\n    double dd"),
     "fp8_k_scaled_by_v_scale": ("(elem(k_cache, base + d, dtype) * k_scale)", "(elem(k_cache, base + d, dtype) * v_scale)"),
     "fp8_write_multiplies_scale": ("fp8_code(kx / k_scale)", "fp8_code(kx * k_scale)"),
+    "merge_weights_crossed": ("double wd = exp(dst->top - both), ws = exp(src->top - both);",
+                              "double wd = exp(src->top - both), ws = exp(dst->top - both);"),
+    "block_summary_not_relative_to_top": ("    double w = exp(scores[o] - s->top);", "    double w = exp(scores[o]);"),
+    "merge_keeps_old_top": ("  dst->top = both;\n}", "}"),
 }
 
 
