@@ -343,18 +343,6 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
 
 }  // namespace
 
-int decode_default_partition(int num_seqs, int num_kv_heads, int max_seq_len, int block_size) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_seq_len;
-  return 16 * block_size;  // 256 tokens at block size 16
-}
-
-size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int nparts_max) {
-  if (nparts_max <= 1) return 0;
-  return (size_t)num_seqs * num_heads * nparts_max * ((size_t)head_dim + 2) * sizeof(float);
-}
-
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;
   const bool mfma = (p.kv_bf16 || p.kv_fp8) && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16;

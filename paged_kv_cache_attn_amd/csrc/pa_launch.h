@@ -88,11 +88,6 @@ struct DecodeParams {
   int plan_stride;         // positions per range in the plan (>= every range's size)
 };
 
-// Library choice of split-K partition size (tokens) for these sizes.
-int decode_default_partition(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
-
-size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int nparts_max);
-
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream);
 // Writes the plan of p's balanced split (p.plan_* set, the attention fields unused).

@@ -1,13 +1,20 @@
 """GPU: parity at the full benchmark configurations, in the launch
 configuration bench.py times (decode: one plan per step, the planned call,
-library-chosen partitioning; prefill: the MFMA grid), on sampled rows that
-the oracle computes one at a time.
+library-chosen partitioning; prefill: the MFMA grid).  Decode is checked on
+every row of every batch; the chunked prefill on two rows of every 32-row
+query tile of every sequence (one tile is one workgroup's work), at offsets
+that vary from tile to tile so every wave and column group is covered.  The
+oracle computes the rows one at a time, spread over host threads (its
+ctypes calls release the interpreter lock).
 
 Inputs come from the same seeded generators as the benchmark (device draws,
 copied to the host for the oracle).  Shapes: Llama-3.1-8B-shaped decode (64
 lognormal rows, Hq 32 / Hkv 8), the 70B-shaped 8 x 32K decode (Hq 64 / Hkv 8),
 parallel sampling over shared prompts, and the 16 x (1024 + 512) chunked
 prefill, in bf16 and with FP8 caches."""
+import concurrent.futures
+import os
+
 import numpy as np
 import pytest
 
@@ -58,35 +65,39 @@ def _decode_planned(pa, torch, w, K, V, q, partition=0, k_scale=1.0, v_scale=1.0
     return out.double().cpu().numpy()
 
 
-def _check_decode_rows(w, got, qh, Kh, Vh, rows, tol, k_scale=None, v_scale=None):
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _check_decode_rows(w, got, qh, Kh, Vh, tol, k_scale=None, v_scale=None):
+    """Every row of the batch against the oracle, rows spread over threads."""
     lens = w.layout.seq_lens
     assert np.isfinite(got).all()
-    for b in rows:
+
+    def one(b):
         ref = oracle.paged_decode(qh[b:b + 1], Kh, Vh, w.layout.block_tables[b:b + 1], lens[b:b + 1], w.scale,
                                   k_scale=k_scale, v_scale=v_scale)
-        err = max_err(got[b:b + 1], ref)
-        assert err <= tol, "row %d (length %d): max abs error %.3g" % (b, lens[b], err)
+        return b, max_err(got[b:b + 1], ref)
 
-
-def _sample_rows(lens, n, seed):
-    """The longest and the shortest row, plus n - 2 others drawn with a seed."""
-    order = np.argsort(lens)
-    rng = np.random.default_rng(seed)
-    rest = rng.choice(order[1:-1], size=min(n - 2, len(order) - 2), replace=False)
-    return [int(order[-1]), int(order[0])] + [int(x) for x in rest]
+    order = [int(b) for b in np.argsort(-lens)]  # longest first keeps the pool busy
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_threads()) as ex:
+        errs = dict(ex.map(one, order))
+    worst = max(errs, key=errs.get)
+    assert errs[worst] <= tol, "row %d (length %d): max abs error %.3g" % (worst, lens[worst], errs[worst])
+    return errs
 
 
 DECODE_CONFIGS = [
-    # workload, partition, sampled rows
-    ("llama8b_decode", 0, 10),
-    ("llama70b_long", 0, 2),
-    ("llama70b_long", 512, 2),
-    ("shared_prefix", 0, 10),
+    # workload, partition
+    ("llama8b_decode", 0),
+    ("llama70b_long", 0),
+    ("llama70b_long", 512),
+    ("shared_prefix", 0),
 ]
 
 
-@pytest.mark.parametrize("name,partition,nrows", DECODE_CONFIGS)
-def test_full_config_decode_bf16(pa, name, partition, nrows):
+@pytest.mark.parametrize("name,partition", DECODE_CONFIGS)
+def test_full_config_decode_bf16(pa, name, partition):
     torch = torch_mod()
     w = getattr(W, name)()
     shape = w.cache_shape()
@@ -96,11 +107,12 @@ def test_full_config_decode_bf16(pa, name, partition, nrows):
     got = _decode_planned(pa, torch, w, K, V, q, partition)
     qh, Kh, Vh = to_host(q), to_host(K), to_host(V)
     del K, V
-    _check_decode_rows(w, got, qh, Kh, Vh, _sample_rows(w.layout.seq_lens, nrows, w.seed), TOL["bf16"])
+    errs = _check_decode_rows(w, got, qh, Kh, Vh, TOL["bf16"])
+    print("%s partition %d: %d rows, max abs error %.3e" % (name, partition, len(errs), max(errs.values())))
 
 
-@pytest.mark.parametrize("name,nrows", [("llama8b_decode", 8), ("llama70b_long", 2)])
-def test_full_config_decode_fp8(pa, name, nrows):
+@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_long"])
+def test_full_config_decode_fp8(pa, name):
     torch = torch_mod()
     w = getattr(W, name)()
     shape = w.cache_shape()
@@ -110,8 +122,8 @@ def test_full_config_decode_fp8(pa, name, nrows):
     got = _decode_planned(pa, torch, w, K, V, q, 0, ks, vs, fp8=True)
     qh, Kh, Vh = to_host(q), to_host(K), to_host(V)
     del K, V
-    _check_decode_rows(w, got, qh, Kh, Vh, _sample_rows(w.layout.seq_lens, nrows, w.seed), TOL["bf16"],
-                       k_scale=ks, v_scale=vs)
+    errs = _check_decode_rows(w, got, qh, Kh, Vh, TOL["bf16"], k_scale=ks, v_scale=vs)
+    print("%s fp8: %d rows, max abs error %.3e" % (name, len(errs), max(errs.values())))
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -145,12 +157,33 @@ def test_full_config_chunked_prefill(pa, kv):
     assert np.isfinite(got).all()
     qh, Kh, Vh = to_host(q), to_host(K), to_host(V)
     kvs = dict(k_scale=ks, v_scale=vs) if kv == "fp8" else {}
-    # rows of three sequences: the first chunk row, a middle one, the last one
-    for b in (0, B // 2, B - 1):
+    # two rows of every 32-row query tile of every sequence (a tile is one
+    # workgroup: 4 waves x 2 column groups x 4 chunk tokens of the 4-head
+    # group), at offsets that move from tile to tile, plus each sequence's
+    # first and last chunk row
+    tile_rows = 32
+    cases = []
+    for b in range(B):
+        n = int(w.chunk_lens[b])
+        rows = {0, n - 1}
+        for t in range((n + tile_rows - 1) // tile_rows):
+            for extra in (0, 17):
+                i = t * tile_rows + (b * 5 + t * 11 + extra) % tile_rows
+                if i < n:
+                    rows.add(i)
+        cases += [(b, i) for i in sorted(rows)]
+
+    def one(case):
+        b, i = case
         S, n = int(lay.seq_lens[b]), int(w.chunk_lens[b])
-        for i in (0, n // 2 + 3, n - 1):
-            r = int(qsl_h[b]) + i
-            ref = oracle.paged_prefill(qh[r:r + 1], Kh, Vh, lay.block_tables[b:b + 1], np.array([0, 1], np.int32),
-                                       np.array([S - n + i + 1], np.int32), w.scale, **kvs)
-            err = max_err(got[r:r + 1], ref)
-            assert err <= TOL["bf16"], "sequence %d chunk row %d: max abs error %.3g" % (b, i, err)
+        r = int(qsl_h[b]) + i
+        ref = oracle.paged_prefill(qh[r:r + 1], Kh, Vh, lay.block_tables[b:b + 1], np.array([0, 1], np.int32),
+                                   np.array([S - n + i + 1], np.int32), w.scale, **kvs)
+        return case, max_err(got[r:r + 1], ref)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_threads()) as ex:
+        errs = dict(ex.map(one, cases))
+    worst = max(errs, key=errs.get)
+    print("chunked prefill %s: %d rows checked, max abs error %.3e" % (kv, len(errs), errs[worst]))
+    assert len(cases) >= 2 * B * (int(w.chunk_lens.min()) // tile_rows)
+    assert errs[worst] <= TOL["bf16"], "sequence %d chunk row %d: max abs error %.3g" % (worst + (errs[worst],))

@@ -368,6 +368,62 @@ def test_prefill_mfma_block_sizes(pa, bs):
     assert err <= TOL["bf16"], err
 
 
+def repack_blocks(lay, k, v, lens, bs, seed, pool_factor=1.8):
+    """The same logical K/V under another physical block permutation (and a
+    larger pool): every block of every sequence moved, with its unused tail
+    slots, to the id a fresh seeded layout gives it; unused ids hold zeros."""
+    lay2 = synth.build_paged_layout(lens, bs, seed=seed, pool_factor=pool_factor)
+    k2 = np.zeros((lay2.num_blocks,) + k.shape[1:], k.dtype)
+    v2 = np.zeros_like(k2)
+    for b, L in enumerate(lens):
+        for j in range((L + bs - 1) // bs):
+            k2[lay2.block_tables[b, j]] = k[lay.block_tables[b, j]]
+            v2[lay2.block_tables[b, j]] = v[lay.block_tables[b, j]]
+    assert not np.array_equal(lay2.block_tables[:, :4], lay.block_tables[:, :4])
+    return lay2, k2, v2
+
+
+@pytest.mark.parametrize("kv,bs", [("bf16", 16), ("bf16", 8), ("fp8", 16), ("fp8", 8)])
+def test_prefill_permutation_bit_exact(pa, kv, bs):
+    """Paging changes where the KV lives, not what is computed (Lecture 7 §4.2; Lecture 16 §3.3): the
+    chunked prefill over the same logical K/V in another physical permutation gives identical bits,
+    for chunks that start mid-block, at 0, and span several query tiles."""
+    torch = torch_mod()
+    total = [40, 700, 17, 1029, 300, 1]
+    chunk = [13, 200, 1, 129, 37, 1]
+    Hq, Hkv, D = 32, 8, 128
+    lay = synth.build_paged_layout(total, bs, seed=31 + bs, pool_factor=1.3)
+    shape = (lay.num_blocks, Hkv, bs, D)
+    if kv == "fp8":
+        ks, vs = 0.0071, 0.0093
+        k = oracle.fp8_encode(W.host_values(shape, 1.0, 811, "f32") / np.float32(ks))
+        v = oracle.fp8_encode(W.host_values(shape, 1.0, 812, "f32") / np.float32(vs))
+    else:
+        k = W.host_values(shape, 1.0, 811, "bf16")
+        v = W.host_values(shape, 1.0, 812, "bf16")
+    q = W.host_values((sum(chunk), Hq, D), 1.0, 813, "bf16")
+    qsl = to_gpu(np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32))
+    lay2, k2, v2 = repack_blocks(lay, k, v, total, bs, seed=977 + bs)
+    outs = []
+    for L_, k_, v_ in ((lay, k, v), (lay2, k2, v2)):
+        out = torch.full((sum(chunk), Hq, D), float("nan"), device="cuda")
+        args = (to_gpu(L_.block_tables.astype(np.int32)), qsl, to_gpu(L_.seq_lens.astype(np.int32)), 0.0884,
+                int(max(chunk)), int(max(total)))
+        if kv == "fp8":
+            pa.paged_attn_prefill_chunk_fp8(out, to_gpu(q), to_gpu(k_), to_gpu(v_), ks, vs, *args)
+        else:
+            pa.paged_attn_prefill_chunk(out, to_gpu(q), to_gpu(k_), to_gpu(v_), *args)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0], outs[1]), "max difference %.3g" % np.max(np.abs(outs[0] - outs[1]))
+    # and the values are right
+    qsl_h = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    kvs = dict(k_scale=ks, v_scale=vs) if kv == "fp8" else {}
+    ref = oracle.paged_prefill(q, k, v, lay.block_tables, qsl_h, lay.seq_lens, 0.0884, **kvs)
+    assert max_err(outs[0].astype(np.float64), ref) <= TOL["bf16"]
+
+
 def test_prefill_one_row_equals_decode(pa):
     lens = [77, 300, 16]
     lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=8)
@@ -389,7 +445,8 @@ def test_decode_one_row_split_over_many_ranges(pa):
 
 
 def test_decode_workspace_reuse_and_garbage(pa):
-    """Tickets are tagged with the call generation: stale or garbage workspace contents are ignored."""
+    """Stale or garbage workspace contents are ignored: every piece the merge reads was written earlier in
+    the same call, so repeated calls on one workspace filled with garbage all match the oracle."""
     torch = torch_mod()
     lens = [300, 1, 0, 2048, 77, 0, 513]
     lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=17)
