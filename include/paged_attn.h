@@ -87,7 +87,8 @@ enum pa_status {
   PA_ERR_SHAPE = -2,       /* negative or inconsistent sizes                    */
   PA_ERR_UNSUPPORTED = -3, /* valid but not implemented (head_dim, block size)  */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
-  PA_ERR_LAUNCH = -5       /* HIP reported an error when launching              */
+  PA_ERR_LAUNCH = -5,      /* HIP reported an error when launching              */
+  PA_ERR_SCRATCH = -6      /* needs more than the built-in scratch buffer holds */
 };
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -294,6 +295,37 @@ PA_EXPORT int paged_attn_decode_fp8(void *out, int32_t out_dtype, const void *q,
                                     int32_t num_blocks, int32_t max_seq_len, float scale,
                                     int32_t partition_size, void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same call, arguments (kv_dtype PA_F32 or
+ * PA_BF16), kernels and results, bit for bit, but with no workspace
+ * argument.  The workspace is a fixed device array inside the library,
+ * PA_NOALLOC_SCRATCH_BYTES bytes, one copy on every GPU the library runs on,
+ * held until the process ends.  The call itself allocates nothing and calls
+ * no allocating routine; its first call on a device looks up the array's
+ * device address there (once per device).
+ *   - A call whose kernel needs more workspace than PA_NOALLOC_SCRATCH_BYTES
+ *     returns PA_ERR_SCRATCH and enqueues nothing.  The need never exceeds
+ *     paged_attn_decode_workspace_size(...) for the same sizes; the library's
+ *     default split needs about 1 MB for 64 sequences of an 8-KV-head,
+ *     128-dim layer and 4 MB for eight 32K-token sequences, and 512-token
+ *     partitions of eight 32K-token, 64-head rows need about 17 MB.
+ *   - Every call on one GPU shares that GPU's array: two calls that may run
+ *     at the same time on one GPU (different streams, or different host
+ *     threads) race and give unspecified results.  Calls ordered on one
+ *     stream are safe.  Nothing in the array needs to start at zero; it
+ *     keeps whatever the last call left.
+ *   - The device is the stream's (the current device for the null stream).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+PA_EXPORT int paged_attn_decode_noalloc(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                                        const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                        int32_t partition_size, void *stream);
 
 /*
  * paged_attn_prefill_chunk_fp8 -- paged_attn_prefill_chunk over FP8 caches

@@ -21,12 +21,13 @@ __all__ = [
     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in", "swap_host_bytes",
     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
-    "EXPORTED_SYMBOLS",
+    "paged_attn_decode_noalloc", "PA_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
 PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
+PA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's built-in decode scratch (include/paged_attn.h)
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
@@ -34,7 +35,8 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
                     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
                     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8",
-                    "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned")
+                    "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
+                    "paged_attn_decode_noalloc")
 
 
 class PagedAttnError(RuntimeError):
@@ -81,6 +83,9 @@ def _load():
     L.paged_attn_decode_planned.argtypes = ([vp, i32, vp, vp, vp, i32, f32, f32, vp, ctypes.c_size_t, vp, i32, vp]
                                             + [i32] * 7 + [f32, i32, vp, ctypes.c_size_t, vp])
     L.paged_attn_decode_planned.restype = ctypes.c_int
+    L.paged_attn_decode_noalloc.argtypes = ([vp, i32, vp, vp, vp, i32, vp, i32, vp] + [i32] * 7
+                                            + [ctypes.c_float, i32, vp])
+    L.paged_attn_decode_noalloc.restype = ctypes.c_int
     L.kv_swap_out.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
     L.kv_swap_out.restype = ctypes.c_int
     L.kv_swap_in.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_size_t] + [i32] * 5 + [vp]
@@ -391,3 +396,25 @@ def paged_attn_decode_planned(out, q, k_cache, v_cache, plan, block_tables, seq_
                                        bs, NB, int(max_seq_len), float(scale), int(partition_size), ws_ptr,
                                        ws_bytes, _stream(stream))
     _check("paged_attn_decode_planned", st)
+
+
+# ----------------------------------------------------------------------------- no allocation
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                              partition_size: int = 0, stream=None):
+    """paged_attn_decode with the library's built-in device scratch instead of a workspace (for callers that
+    cannot allocate).  Calls that may overlap on one GPU race on that scratch; calls on one stream do not."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, max_blocks], seq_lens [B]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and caches must share one dtype")
+    st = _L().paged_attn_decode_noalloc(_dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                       _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                                       _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                                       _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D, bs, NB,
+                                       int(max_seq_len), float(scale), int(partition_size), _stream(stream))
+    _check("paged_attn_decode_noalloc", st)

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "paged_attn.h"
 #include "pa_launch.h"
@@ -145,6 +147,7 @@ const char *pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block size or grid size";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case PA_ERR_SCRATCH: return "the call needs more scratch than the library's built-in buffer holds";
     default: return "unknown status";
   }
 }
@@ -535,6 +538,83 @@ int kv_swap_in(void *k_cache, void *v_cache, const int64_t *block_ids, int32_t n
                int32_t head_dim, int32_t dtype, void *stream) {
   return swap_blocks(false, k_cache, v_cache, block_ids, num_ids, const_cast<void *>(host_src), staging,
                      staging_bytes, num_blocks, num_kv_heads, block_size, head_dim, dtype, stream);
+}
+
+}  // extern "C"
+
+// -- Decode without allocation -------------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): paged_attn_decode with its workspace in a fixed device array of
+// this library instead of a caller buffer.  Each GPU the library runs on
+// holds its own copy of the array until the process ends.  Host code never
+// passes the array's name to a kernel (on the host that name is only a
+// stand-in): its device address is looked up once per device, with that
+// device current, and kept.  The decode kernels need no part of their
+// workspace cleared (every piece the merge reads is written earlier in the
+// same call), so the array is never initialised.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on `dev` (nullptr on failure), looked up on
+// first use with `dev` current; the caller's current device is restored.
+void *scratch_on_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return nullptr;
+  if (prev != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void *found = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&found, HIP_SYMBOL(scratch));
+  if (prev != dev) (void)hipSetDevice(prev);
+  if (e != hipSuccess || !found) {
+    (void)hipGetLastError();  // clear the sticky error of the failed lookup
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(found, std::memory_order_release);
+  return found;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_noalloc(void *out, int32_t out_dtype, const void *q, const void *k_cache,
+                              const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_seq_len, float scale, int32_t partition_size,
+                              void *stream) {
+  if (!dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  // every argument check of paged_attn_decode first, with an empty
+  // workspace: a call that needs none is served as is, one that needs some
+  // fails only with PA_ERR_WORKSPACE
+  int st = decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, 1.f, 1.f, block_tables, max_blocks_per_seq,
+                       seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
+                       scale, partition_size, nullptr, 0, stream);
+  if (st != PA_ERR_WORKSPACE) return st;
+  // the workspace of the kernel this call picks (the arguments are valid here)
+  const int64_t cap = std::min<int64_t>(max_seq_len, (int64_t)max_blocks_per_seq * block_size);
+  const DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len, cap,
+                                      partition_size,
+                                      mfma_decode_shape(kv_dtype, num_heads, num_kv_heads, head_dim, block_size));
+  if (plan.workspace_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return PA_ERR_LAUNCH;
+  void *ws = scratch_on_device(dev);
+  if (!ws) return PA_ERR_LAUNCH;
+  return decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, 1.f, 1.f, block_tables, max_blocks_per_seq,
+                     seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
+                     scale, partition_size, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

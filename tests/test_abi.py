@@ -13,6 +13,7 @@ HEADER = os.path.join(ROOT, "include", "paged_attn.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+PA_ERR_SCRATCH = -6
 
 
 @pytest.fixture(scope="module")
@@ -50,7 +51,7 @@ def test_abi_version_and_status_strings(pa):
     v = int(re.search(r"#define PA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert pa.pa_abi_version() == v
     assert pa.pa_status_string(0) == "ok"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         s = pa.pa_status_string(code)
         assert s and s != "unknown status"
     assert pa.pa_status_string(12345) == "unknown status"
@@ -97,6 +98,39 @@ def test_decode_validation(pa):
     need = pa.paged_attn_decode_workspace_size(2, 8, 2, 128, 16, 4096, 0)
     assert _dec(pa, max_len=4096, maxblk=256, ws=P, ws_bytes=need - 1) == PA_ERR_WORKSPACE
     assert _dec(pa, B=0) == PA_OK
+
+
+def _dec_noalloc(pa, **kw):
+    a = dict(out=P, out_dtype=0, q=P, k=P, v=P, kv_dtype=1, bt=P, maxblk=8, sl=P, B=2, Hq=8, Hkv=2,
+             D=128, bs=16, NB=64, max_len=128, scale=0.1, part=0)
+    a.update(kw)
+    return pa.lib.paged_attn_decode_noalloc(a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["kv_dtype"],
+                                            a["bt"], a["maxblk"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                            a["bs"], a["NB"], a["max_len"], a["scale"], a["part"], N)
+
+
+def test_decode_noalloc_validation(pa):
+    """The no-allocation decode checks its arguments as paged_attn_decode does, and refuses (before touching
+    the GPU) a call that needs more workspace than its built-in scratch holds."""
+    assert _dec_noalloc(pa, Hq=6, Hkv=4) == PA_ERR_SHAPE
+    assert _dec_noalloc(pa, D=96) == PA_ERR_UNSUPPORTED
+    assert _dec_noalloc(pa, kv_dtype=2) == PA_ERR_UNSUPPORTED          # FP8 caches: not this call
+    assert _dec_noalloc(pa, part=24) == PA_ERR_SHAPE
+    assert _dec_noalloc(pa, scale=float("nan")) == PA_ERR_SHAPE
+    assert _dec_noalloc(pa, q=N) == PA_ERR_NULL
+    assert _dec_noalloc(pa, B=0) == PA_OK
+    # 2048 rows of 64 heads, 1M tokens cut into 16-token partitions: the partition grid would need
+    # terabytes of workspace
+    big = dict(B=2048, Hq=64, Hkv=8, max_len=1 << 20, maxblk=1 << 16, part=16)
+    assert pa.paged_attn_decode_workspace_size(2048, 64, 8, 128, 16, 1 << 20, 16) > pa.PA_NOALLOC_SCRATCH_BYTES
+    assert _dec_noalloc(pa, **big) == PA_ERR_SCRATCH
+    # the binding's constant is the header's
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", open(HEADER).read())
+    assert int(m.group(1)) << 20 == pa.PA_NOALLOC_SCRATCH_BYTES
+    # the upper bound of the headline 8B shape fits, and so does 512-token partitioning of 8 x 32K rows of
+    # 64 heads (the partition grid: 8 * 64 * 64 partial rows)
+    assert pa.paged_attn_decode_workspace_size(64, 32, 8, 128, 16, 4096, 0) <= pa.PA_NOALLOC_SCRATCH_BYTES
+    assert pa.paged_attn_decode_workspace_size(8, 64, 8, 128, 16, 32768, 512) <= pa.PA_NOALLOC_SCRATCH_BYTES
 
 
 def _a256(x):
