@@ -69,6 +69,28 @@ def measured_traffic(workload: str):
         return None
     return e.get("hbm_bytes_per_call")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# Host threads the oracle may use: every core this process may run on, up to
+# the 16 host CPUs the GPU machine allots to one GPU.
+HOST_THREAD_CAP = 16
+
+
+def host_info() -> dict:
+    """Core counts and the CPU model of this host (for the CPU-baseline record)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "usable_cores": usable, "cpu_model": model,
+            "threads_used": max(1, min(HOST_THREAD_CAP, usable))}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
@@ -78,7 +100,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
-                    choices=["llama8b_decode", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
+                    choices=["llama8b_decode", "tiny_decode", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
                              "chunked_prefill_fp8", "shared_prefix", "shared_prefix_cow",
                              "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
                              "copy_calibration"])
@@ -96,6 +118,7 @@ def parse():
 
 
 STEP_STATS = {}  # per-step time distribution (ms) of the last graph-timed run
+GRAPHS = {}      # the last graph-timed run's step graph (for the cold-layer measurement)
 
 
 def time_calls(args, torch, layers, call):
@@ -194,6 +217,7 @@ def time_layers(args, torch, layers, write, call, out, pre=None):
     g_step, g_call = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step):
         step()
+    GRAPHS["step"] = g_step
     with torch.cuda.graph(g_call):
         if pre is not None:
             pre()
@@ -229,11 +253,32 @@ def time_layers(args, torch, layers, write, call, out, pre=None):
     return ms_step, ms_call, wall, "hip-graph"
 
 
-def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s, kv_scales=(None, None)):
-    """Time the oracle over whole passes of the batch (all sequences, one layer) on all host cores."""
+def cold_layer_ms(torch, step_graph_replay, one_layer, reps=5):
+    """Median GPU time of one layer's attention (its plan included) replayed right after a whole step,
+    so that layer's K/V has been pushed out of the caches by the other layers' streams."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_layer()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        step_graph_replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def cpu_oracle_decode(q, k, v, tables, lens, scale, budget_s, kv_scales=(None, None), threads=None):
+    """Time the oracle over whole passes of the batch (all sequences, one layer) on `threads` host threads
+    (default: every usable core up to HOST_THREAD_CAP); the first pass's output is returned for parity."""
     import oracle
     oracle.build(force=False)
-    cores = min(16, os.cpu_count() or 1)
+    cores = threads or host_info()["threads_used"]
     B = q.shape[0]
 
     def one(b):
@@ -327,13 +372,24 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_bytes / (ms_decode * 1e-3) / 1e9
 
-    # sampled parity + CPU baseline on layer 0 (the oracle on the host copies)
-    torch.cuda.synchronize()
-    if pre is not None:
-        pre()
-    call(0)
-    torch.cuda.synchronize()
-    gpu_out = out.double().cpu().numpy()
+    # one layer's attention (plan included) with its K/V cold: replayed right after a whole step
+    cold_ms = None
+    if mode == "hip-graph":
+        def one_layer():
+            if pre is not None:
+                pre()
+            call(0)
+        cold_ms = cold_layer_ms(torch, GRAPHS["step"].replay, one_layer)
+
+    # parity on the first and the last layer of the rotation, and the CPU baseline on layer 0 (the
+    # oracle on the host copies): all usable cores, then one core
+    def gpu_layer(l):
+        torch.cuda.synchronize()
+        if pre is not None:
+            pre()
+        call(l)
+        torch.cuda.synchronize()
+        return out.double().cpu().numpy()
 
     def host(t):
         t = t.contiguous().cpu()
@@ -341,15 +397,31 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
 
     cpu = None
     parity = None
+    parity_last = None
     if not args.no_cpu_baseline:
-        ref, passes, secs, cores = cpu_oracle_decode(host(q), host(K[0]), host(V[0]), w.layout.block_tables,
-                                                     lens, scale, args.cpu_seconds,
+        hi = host_info()
+        gpu_out = gpu_layer(0)
+        hq = host(q)
+        ref, passes, secs, cores = cpu_oracle_decode(hq, host(K[0]), host(V[0]), w.layout.block_tables,
+                                                     lens, scale, 0.6 * args.cpu_seconds,
                                                      (ks[0], vs[0]) if fp8 else (None, None))
         parity = float(np.max(np.abs(gpu_out - ref)))
+        _, passes1, secs1, _ = cpu_oracle_decode(hq, host(K[0]), host(V[0]), w.layout.block_tables, lens, scale,
+                                                 0.4 * args.cpu_seconds, (ks[0], vs[0]) if fp8 else (None, None),
+                                                 threads=1)
+        gpu_last = gpu_layer(layers - 1)
+        ref_last, _, _, _ = cpu_oracle_decode(hq, host(K[layers - 1]), host(V[layers - 1]), w.layout.block_tables,
+                                              lens, scale, 0.0,
+                                              (ks[layers - 1], vs[layers - 1]) if fp8 else (None, None))
+        parity_last = float(np.max(np.abs(gpu_last - ref_last)))
         cpu = {"value": round(passes * dec_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
                "sample": "%d full pass(es) of layer 0 (%d sequences, %d tokens) through the fp64 C oracle, "
-                         "%.1f s, sequences spread over %d threads" % (passes, B, int(lens.sum()), secs, cores)}
+                         "%.1f s, sequences spread over %d threads" % (passes, B, int(lens.sum()), secs, cores),
+               "one_core": {"value": round(passes1 * dec_bytes / secs1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": "%d full pass(es) of layer 0 on one thread, %.1f s" % (passes1, secs1)},
+               "query_tokens_per_s": round(passes * B / secs, 1),
+               "host": hi}
     res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -370,6 +442,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
+        "parity_max_abs_err_last_layer": parity_last,
+        "cold_layer_us": None if cold_ms is None else round(cold_ms * 1e3, 2),
         "timing": mode, "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")],
         "copy_GBs_read_plus_write": copy_gbs, "wall_s": round(wall, 3),
         "decode_plan": "one plan per step, shared by the layers" if use_plan else None,
@@ -437,9 +511,7 @@ def bench_prefill(args, torch, pa, W, w, layers, fp8=False):
         errs.append(float(np.max(np.abs(out[rows].double().cpu().numpy() - ref))))
     cpu = None
     if not args.no_cpu_baseline:
-        t0 = time.perf_counter()
-        rows_done = 0
-        cores = min(16, os.cpu_count() or 1)
+        hi = host_info()
         b = 0
         S, n = int(w.layout.seq_lens[b]), int(w.chunk_lens[b])
 
@@ -448,18 +520,32 @@ def bench_prefill(args, torch, pa, W, w, layers, fp8=False):
             return oracle.paged_prefill(hq[r_], hk, hv, w.layout.block_tables[b:b + 1], np.array([0, 1], np.int32),
                                         np.array([S - n + i + 1], np.int32), w.scale, **kvs)
 
-        with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as ex:
-            i = 0
-            while time.perf_counter() - t0 < args.cpu_seconds and i < n:
-                list(ex.map(one, range(i, min(i + 64, n))))
-                rows_done += min(64, n - i)
-                i += 64
-        secs = time.perf_counter() - t0
-        keys = sum((S - n + i + 1) for i in range(rows_done))
-        cpu = {"value": round(4.0 * keys * Hq * D / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+        def timed_rows(threads, budget):
+            """Chunk rows of sequence 0 (all query heads) through the oracle on `threads` threads, in
+            batches, until the budget is spent; returns (rows, seconds, TFLOP/s)."""
+            t0 = time.perf_counter()
+            rows_done = 0
+            step = 4 * threads
+            with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+                i = 0
+                while time.perf_counter() - t0 < budget and i < n:
+                    list(ex.map(one, range(i, min(i + step, n))))
+                    rows_done += min(step, n - i)
+                    i += step
+            secs = time.perf_counter() - t0
+            keys = sum((S - n + i + 1) for i in range(rows_done))
+            return rows_done, secs, 4.0 * keys * Hq * D / secs / 1e12
+
+        cores = hi["threads_used"]
+        rows_done, secs, tf = timed_rows(cores, 0.6 * args.cpu_seconds)
+        rows1, secs1, tf1 = timed_rows(1, 0.4 * args.cpu_seconds)
+        cpu = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": cores,
                "kind": "oracle",
                "sample": "%d chunk rows of sequence 0 (all %d query heads) through the fp64 C oracle, %.1f s, "
-                         "rows spread over %d threads" % (rows_done, Hq, secs, cores)}
+                         "rows spread over %d threads" % (rows_done, Hq, secs, cores),
+               "one_core": {"value": round(tf1, 6), "unit": "TFLOP/s", "cores": 1,
+                            "sample": "%d chunk rows of sequence 0 on one thread, %.1f s" % (rows1, secs1)},
+               "host": hi}
     return {
         "metric": "chunked prefill attention TFLOP/s and query tokens/s per layer", "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -853,6 +939,11 @@ def main():
         layers = args.layers or 32
         part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part, fp8=fp8)
+    elif args.workload == "tiny_decode":
+        w = W.tiny_decode()
+        layers = args.layers or 32
+        part = 0 if args.partition < 0 else args.partition
+        res = bench_decode(args, torch, pa, W, w, layers, part)
     elif args.workload in ("llama70b_long", "llama70b_long_fp8"):
         w = W.llama70b_long(block_size=args.block_size)
         layers = args.layers or 4
