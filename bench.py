@@ -100,7 +100,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
-                    choices=["llama8b_decode", "tiny_decode", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
+                    choices=["llama8b_decode", "tiny_decode", "llama8b_decode_f32", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
                              "chunked_prefill_fp8", "shared_prefix", "shared_prefix_cow",
                              "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
                              "copy_calibration"])
@@ -939,8 +939,8 @@ def main():
         layers = args.layers or 32
         part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part, fp8=fp8)
-    elif args.workload == "tiny_decode":
-        w = W.tiny_decode()
+    elif args.workload in ("tiny_decode", "llama8b_decode_f32"):
+        w = W.tiny_decode() if args.workload == "tiny_decode" else W.llama8b_decode(dtype="f32")
         layers = args.layers or 32
         part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part)

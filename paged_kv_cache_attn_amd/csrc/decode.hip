@@ -24,11 +24,15 @@
 //     online softmax), so the result depends only on logical positions and
 //     is bit-identical under any physical block permutation.
 #include "attn_core.h"
+#include "attn_vec.h"
 #include "pa_launch.h"
 
 namespace pa {
 
 namespace {
+
+// Vector kernels: waves per workgroup, and query heads served per pass.
+constexpr int kVecWaves = 4;
 
 __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, float v) {
   if (out_bf16) {
@@ -202,73 +206,56 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
 }
 
 // ----------------------------------------------------------------------------
-// Generic VALU kernel: fp32 or bf16 KV, head_dim 64 or 128, any group size.
-// One wave per (partition, query head, sequence); lane owns D/64 dims; one
-// token per step with a wave-wide dot-product reduction.
+// Vector kernel: fp32 or bf16 KV, head_dim 64 or 128, any group size and
+// block size (the shapes the MFMA kernel does not take).  One workgroup per
+// (partition, KV head, sequence) serves the whole GQA group (attn_vec.h), so
+// each K/V row of the partition is read once per group, with 16-byte loads.
 // ----------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
-  constexpr int DPL = D / 64;
-  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+template <int D, bool BF16, int GC>
+__global__ __launch_bounds__(64 * kVecWaves) void decode_vec_kernel(DecodeParams p) {
+  constexpr int NW = kVecWaves;
+  using G = VecGeom<D, BF16>;
+  __shared__ float red[(NW + 1) * GC * (D + 2)];
+  const int part = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int g = p.num_heads / p.num_kv_heads;
-  const int kh = h / g;
   const int bs = p.block_size;
   const int L = clamp_len(p.seq_lens[b], p.max_len_cap);
   const int nblk = (L + bs - 1) / bs;
   const int nparts = nblk == 0 ? 1 : (nblk + p.part_blocks - 1) / p.part_blocks;
-  if (part >= nparts) return;
-  const int j0 = part * p.part_blocks;
-  const int j1 = min(j0 + p.part_blocks, nblk);
-  const int lane = threadIdx.x;
-
-  auto ld = [&](const void *base, int64_t idx) -> float {
-    if (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[idx]);
-    return reinterpret_cast<const float *>(base)[idx];
-  };
-
-  const int64_t row = (int64_t)b * p.num_heads + h;
-  float qv[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) qv[i] = ld(p.q, row * D + lane * DPL + i);
+  if (part >= nparts) return;  // the whole workgroup leaves together
+  const int t0 = part * p.part_blocks * bs;
+  const int t1 = min(L, t0 + p.part_blocks * bs);
+  const int col = ((threadIdx.x & 63) % G::kLPR) * G::kVPL;
   const float sl2 = p.scale * kLog2e;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  float m = kNegInf, l = 0.f, acc[DPL];
+  const uint8_t *qb = reinterpret_cast<const uint8_t *>(p.q);
+  for (int h0 = 0; h0 < g; h0 += GC) {
+    float q[GC][G::kVPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-
-  for (int j = j0; j < j1; ++j) {
-    const int phys = table[j];
-    if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
-    const int valid = min(bs, L - j * bs);
-    for (int o = 0; o < valid; ++o) {
-      const int64_t base = (((int64_t)phys * p.num_kv_heads + kh) * bs + o) * D + lane * DPL;
-      float part_dot = 0.f;
+    for (int hh = 0; hh < GC; ++hh) {
+      const int h = kh * g + min(h0 + hh, g - 1);  // heads past the group repeat the last one, unused
+      const uint8_t *qr = qb + (((int64_t)b * p.num_heads + h) * D + col) * G::kElem;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) part_dot += qv[i] * ld(p.k_cache, base + i);
-#pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) part_dot += shfl_xor_f(part_dot, s);
-      const float t = part_dot * sl2;
-      const float m_new = fmaxf(m, t);
-      const float corr = fast_exp2(m - m_new);
-      const float e = fast_exp2(t - m_new);
-      l = l * corr + e;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * corr + e * ld(p.v_cache, base + i);
-      m = m_new;
+      for (int c = 0; c < G::kCPL; ++c) unpack16<BF16>(ld16(qr + 16 * c), &q[hh][c * (G::kVPL / G::kCPL)]);
     }
-  }
-  if (nparts == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) store_out(p.out, p.out_bf16, row * D + lane * DPL + i, acc[i] * inv);
-  } else {
-    float *wo = p.ws_o + (row * p.nparts_max + part) * D;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) wo[lane * DPL + i] = acc[i];
-    if (lane == 0) {
-      p.ws_ml[(row * p.nparts_max + part) * 2 + 0] = m;
-      p.ws_ml[(row * p.nparts_max + part) * 2 + 1] = l;
+    const float *res = vec_attend<D, BF16, NW, GC>(red, q, p.k_cache, p.v_cache, table, t0, t1, kh,
+                                                   p.num_kv_heads, bs, p.num_blocks, sl2);
+    for (int idx = threadIdx.x; idx < GC * D; idx += 64 * NW) {
+      const int hh = idx / D, d = idx - hh * D;
+      if (h0 + hh >= g) continue;
+      const float *e = res + hh * (D + 2);
+      const int64_t row = (int64_t)b * p.num_heads + (int64_t)kh * g + h0 + hh;
+      if (nparts == 1) {
+        store_out(p.out, p.out_bf16, row * D + d, e[D + 1] > 0.f ? e[d] / e[D + 1] : 0.f);
+      } else {
+        p.ws_o[(row * p.nparts_max + part) * D + d] = e[d];
+        if (d == 0) {
+          p.ws_ml[(row * p.nparts_max + part) * 2 + 0] = e[D];
+          p.ws_ml[(row * p.nparts_max + part) * 2 + 1] = e[D + 1];
+        }
+      }
     }
+    __syncthreads();  // the next chunk of heads reuses `red`
   }
 }
 
@@ -341,6 +328,21 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
   }
 }
 
+// The vector kernel with the head chunk GC that fits the group: the group
+// size rounded up to a power of two, at most 8.
+template <int D, bool BF16, class Params>
+void launch_vec(dim3 grid, dim3 block, hipStream_t stream, const Params &p) {
+  const int g = p.num_heads / p.num_kv_heads;
+  if (g <= 1)
+    hipLaunchKernelGGL((decode_vec_kernel<D, BF16, 1>), grid, block, 0, stream, p);
+  else if (g <= 2)
+    hipLaunchKernelGGL((decode_vec_kernel<D, BF16, 2>), grid, block, 0, stream, p);
+  else if (g <= 4)
+    hipLaunchKernelGGL((decode_vec_kernel<D, BF16, 4>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_vec_kernel<D, BF16, 8>), grid, block, 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
@@ -368,17 +370,17 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
       }
     }
   } else {
-    dim3 grid(p.nparts_max, p.num_heads, p.num_seqs);
+    const dim3 grid(p.nparts_max, p.num_kv_heads, p.num_seqs), block(64 * kVecWaves);
     if (p.head_dim == 64) {
       if (p.kv_bf16)
-        hipLaunchKernelGGL((decode_valu_kernel<64, true>), grid, dim3(64), 0, stream, p);
+        launch_vec<64, true>(grid, block, stream, p);
       else
-        hipLaunchKernelGGL((decode_valu_kernel<64, false>), grid, dim3(64), 0, stream, p);
+        launch_vec<64, false>(grid, block, stream, p);
     } else {
       if (p.kv_bf16)
-        hipLaunchKernelGGL((decode_valu_kernel<128, true>), grid, dim3(64), 0, stream, p);
+        launch_vec<128, true>(grid, block, stream, p);
       else
-        hipLaunchKernelGGL((decode_valu_kernel<128, false>), grid, dim3(64), 0, stream, p);
+        launch_vec<128, false>(grid, block, stream, p);
     }
   }
   hipError_t e = hipGetLastError();

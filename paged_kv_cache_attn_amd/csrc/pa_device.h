@@ -98,9 +98,6 @@ __device__ __forceinline__ floatx4 mfma_16x16x16_bf16(const u32x2 &a, const u32x
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// Lane-crossing helpers (wave64).  xor 16 / xor 32 exchange between rows.
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-
 // The four lanes of a column (c, c+16, c+32, c+48) combine through the
 // gfx950 row swaps: v_permlane16_swap exchanges rows 1 and 3 of its first
 // operand with rows 0 and 2 of its second, v_permlane32_swap the upper half

@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "attn_core.h"
+#include "attn_vec.h"
 #include "pa_launch.h"
 
 #ifndef PA_PREFILL_WAVES
@@ -481,57 +482,63 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-// Generic VALU kernel: any dtype / head_dim 64 or 128 / group size / block
-// size.  One wave per (chunk row, query head, sequence).
-template <int D, bool BF16>
-__global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillParams p) {
-  constexpr int DPL = D / 64;
-  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Vector kernel: fp32 or bf16 KV, head_dim 64 or 128, any group size and
+// block size (the shapes the MFMA kernel does not take).  One workgroup per
+// (chunk row, KV head, sequence) serves the row's whole GQA group over its
+// causal keys (attn_vec.h): each K/V row is read once per group.
+constexpr int kVecWaves = 4;
+
+template <int D, bool BF16, int GC>
+__global__ __launch_bounds__(64 * kVecWaves) void prefill_vec_kernel(PrefillParams p) {
+  constexpr int NW = kVecWaves;
+  using G = VecGeom<D, BF16>;
+  __shared__ float red[(NW + 1) * GC * (D + 2)];
+  const int qi = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.query_start_loc[b];
   const int n_b = p.query_start_loc[b + 1] - q0;
+  // (uniform over the workgroup: it leaves together)
   if (qi >= n_b || q0 < 0 || (int64_t)q0 + qi >= p.num_query_tokens) return;
   const int g = p.num_heads / p.num_kv_heads;
-  const int kh = h / g;
-  const int bs = p.block_size;
   const int S = clamp_len(p.seq_lens[b], p.max_len_cap);
-  int nkeys = S - n_b + qi + 1;
-  nkeys = nkeys < 0 ? 0 : (nkeys > S ? S : nkeys);
-  const int lane = threadIdx.x;
-  auto ld = [&](const void *base, int64_t idx) -> float {
-    if (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[idx]);
-    return reinterpret_cast<const float *>(base)[idx];
-  };
-  const int64_t row = (int64_t)(q0 + qi) * p.num_heads + h;
-  float qv[DPL], acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    qv[i] = ld(p.q, row * D + lane * DPL + i);
-    acc[i] = 0.f;
-  }
+  const int nkeys = max(0, min(S, S - n_b + qi + 1));
+  const int col = ((threadIdx.x & 63) % G::kLPR) * G::kVPL;
   const float sl2 = p.scale * kLog2e;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  float m = kNegInf, l = 0.f;
-  for (int t = 0; t < nkeys; ++t) {
-    const int phys = table[t / bs];
-    if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
-    const int64_t base = (((int64_t)phys * p.num_kv_heads + kh) * bs + t % bs) * D + lane * DPL;
-    float dot = 0.f;
+  const uint8_t *qb = reinterpret_cast<const uint8_t *>(p.q);
+  const int64_t qrow = (int64_t)(q0 + qi) * p.num_heads + (int64_t)kh * g;
+  for (int h0 = 0; h0 < g; h0 += GC) {
+    float q[GC][G::kVPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) dot += qv[i] * ld(p.k_cache, base + i);
+    for (int hh = 0; hh < GC; ++hh) {  // heads past the group repeat the last one, unused
+      const uint8_t *qr = qb + ((qrow + min(h0 + hh, g - 1)) * D + col) * G::kElem;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s, 64);
-    const float x = dot * sl2;
-    const float m_new = fmaxf(m, x);
-    const float corr = fast_exp2(m - m_new);
-    const float e = fast_exp2(x - m_new);
-    l = l * corr + e;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * corr + e * ld(p.v_cache, base + i);
-    m = m_new;
+      for (int c = 0; c < G::kCPL; ++c) unpack16<BF16>(ld16(qr + 16 * c), &q[hh][c * (G::kVPL / G::kCPL)]);
+    }
+    const float *res = vec_attend<D, BF16, NW, GC>(red, q, p.k_cache, p.v_cache, table, 0, nkeys, kh,
+                                                   p.num_kv_heads, p.block_size, p.num_blocks, sl2);
+    for (int idx = threadIdx.x; idx < GC * D; idx += 64 * NW) {
+      const int hh = idx / D, d = idx - hh * D;
+      if (h0 + hh >= g) continue;
+      const float *e = res + hh * (D + 2);
+      store_out(p.out, p.out_bf16, (qrow + h0 + hh) * D + d, e[D + 1] > 0.f ? e[d] / e[D + 1] : 0.f);
+    }
+    __syncthreads();  // the next chunk of heads reuses `red`
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) store_out(p.out, p.out_bf16, row * D + lane * DPL + i, acc[i] * inv);
+}
+
+// The vector kernel with the head chunk GC that fits the group: the group
+// size rounded up to a power of two, at most 8.
+template <int D, bool BF16, class Params>
+void launch_vec(dim3 grid, dim3 block, hipStream_t stream, const Params &p) {
+  const int g = p.num_heads / p.num_kv_heads;
+  if (g <= 1)
+    hipLaunchKernelGGL((prefill_vec_kernel<D, BF16, 1>), grid, block, 0, stream, p);
+  else if (g <= 2)
+    hipLaunchKernelGGL((prefill_vec_kernel<D, BF16, 2>), grid, block, 0, stream, p);
+  else if (g <= 4)
+    hipLaunchKernelGGL((prefill_vec_kernel<D, BF16, 4>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_vec_kernel<D, BF16, 8>), grid, block, 0, stream, p);
 }
 
 }  // namespace
@@ -569,17 +576,17 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     }
 #undef PA_PREFILL_LAUNCH
   } else {
-    dim3 grid(p.max_query_len, p.num_heads, p.num_seqs);
+    const dim3 grid(p.max_query_len, p.num_kv_heads, p.num_seqs), block(64 * kVecWaves);
     if (p.head_dim == 64) {
       if (p.kv_bf16)
-        hipLaunchKernelGGL((prefill_valu_kernel<64, true>), grid, dim3(64), 0, stream, p);
+        launch_vec<64, true>(grid, block, stream, p);
       else
-        hipLaunchKernelGGL((prefill_valu_kernel<64, false>), grid, dim3(64), 0, stream, p);
+        launch_vec<64, false>(grid, block, stream, p);
     } else {
       if (p.kv_bf16)
-        hipLaunchKernelGGL((prefill_valu_kernel<128, true>), grid, dim3(64), 0, stream, p);
+        launch_vec<128, true>(grid, block, stream, p);
       else
-        hipLaunchKernelGGL((prefill_valu_kernel<128, false>), grid, dim3(64), 0, stream, p);
+        launch_vec<128, false>(grid, block, stream, p);
     }
   }
   return hipGetLastError();

@@ -131,12 +131,13 @@ def tiny_decode() -> DecodeWorkload:
     return DecodeWorkload("tiny_decode_fp32", lay, 8, 2, 64, "f32", 1.0, seed=1)
 
 
-def llama8b_decode(batch: int = 64, seed: int = 2, block_size: int = 16) -> DecodeWorkload:
-    """The same lengths at any block size (the pool is 1.25x the blocks they need)."""
+def llama8b_decode(batch: int = 64, seed: int = 2, block_size: int = 16, dtype: str = "bf16") -> DecodeWorkload:
+    """The same lengths at any block size (the pool is 1.25x the blocks they need); dtype "f32" gives the
+    same batch with fp32 K/V and q (the vector kernels' shape)."""
     lens = lognormal_lengths(batch, 390, SIGMA_8B, 16, 4096, seed=seed)
     lay = build_paged_layout(lens, block_size, seed=seed + 1000, pool_factor=1.25)
-    name = "llama8b_decode_bf16" + ("" if block_size == 16 else "_bs%d" % block_size)
-    return DecodeWorkload(name, lay, 32, 8, 128, "bf16", 0.5, seed=seed)
+    name = "llama8b_decode_" + dtype + ("" if block_size == 16 else "_bs%d" % block_size)
+    return DecodeWorkload(name, lay, 32, 8, 128, dtype, 0.5, seed=seed)
 
 
 def llama70b_long(batch: int = 8, seq_len: int = 32768, seed: int = 4, block_size: int = 16) -> DecodeWorkload:
