@@ -112,6 +112,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plan", action="store_true",
                     help="decode without a per-step plan (each call stages its own split)")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="decode steps as two calls per layer (kv_cache_write, then the planned decode) instead "
+                         "of paged_attn_decode_append")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every call from Python instead of replaying captured HIP graphs")
     return ap.parse_args()
@@ -349,7 +352,13 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         write = lambda l: pa.kv_cache_write_fp8(newk, newv, K[l], V[l], slots, ks[l], vs[l])
     else:
         write = lambda l: pa.kv_cache_write(newk, newv, K[l], V[l], slots)
-    if use_plan:
+    # the step's write folded into the attention call (the balanced bf16 path)
+    fold = use_plan and not fp8 and w.dtype == "bf16" and not args.no_fold
+    if fold:
+        write = lambda l: None
+        call = lambda l: pa.paged_attn_decode_append(out, q, newk, newv, slots, K[l], V[l], plan, bt, sl, scale,
+                                                     max_len, partition, ws)
+    elif use_plan:
         call = lambda l: pa.paged_attn_decode_planned(out, q, K[l], V[l], plan, bt, sl, scale, max_len, partition,
                                                       ws, k_scale=ks[l] if fp8 else 1.0,
                                                       v_scale=vs[l] if fp8 else 1.0)
@@ -370,7 +379,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         write_bytes = B * Hkv * D * w.elem_bytes * 2 * 2 + 8 * B
     step_bytes = layers * (dec_bytes + write_bytes)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_bytes / (ms_decode * 1e-3) / 1e9
+    call_bytes = dec_bytes + (write_bytes if fold else 0)  # a folded call also moves the new rows
+    achieved = call_bytes / (ms_decode * 1e-3) / 1e9
 
     # one layer's attention (plan included) with its K/V cold: replayed right after a whole step
     cold_ms = None
@@ -437,8 +447,9 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic((w.name.replace("_bf16", "_fp8") if fp8 else w.name)),
                      "traffic_unit": "bytes per call",
-                     "kernel": "paged_attn_decode_fp8 call" if fp8 else "paged_attn_decode call",
-                     "bytes_per_launch": dec_bytes,
+                     "kernel": ("paged_attn_decode_fp8 call" if fp8 else
+                                "paged_attn_decode_append call (write folded in)" if fold else "paged_attn_decode call"),
+                     "bytes_per_launch": call_bytes,
                      "avg_launch_ms": round(ms_decode, 5)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
@@ -447,6 +458,8 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
         "timing": mode, "ms_per_step_p10_p50_p90": [STEP_STATS.get(k) for k in ("p10", "p50", "p90")],
         "copy_GBs_read_plus_write": copy_gbs, "wall_s": round(wall, 3),
         "decode_plan": "one plan per step, shared by the layers" if use_plan else None,
+        "step_calls_per_layer": ("paged_attn_decode_append (the new token's K/V write folded into the attention "
+                                 "kernels)" if fold else "kv_cache_write, then the decode"),
     }
     return res
 

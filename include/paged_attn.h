@@ -282,6 +282,42 @@ PA_EXPORT int paged_attn_decode_planned(void *out, int32_t out_dtype, const void
                                         void *stream);
 
 /*
+ * paged_attn_decode_append -- one layer of a decode step: every sequence's
+ * new token is written into its slot and the sequence's query then attends
+ * to its cache, new token included ([L7] §4.3: the KV write and the
+ * attention through the block table are the fused kernels of the pages'
+ * design; [L7] §4.1: a decode step appends one token to each sequence's last
+ * block).  The result, output and caches, is bit for bit that of
+ * kv_cache_write(key, value, slot_mapping) followed by
+ * paged_attn_decode_planned with the same arguments, provided every
+ * slot_mapping[b] is negative (no write) or the slot that the block table
+ * gives position seq_lens[b] - 1 of sequence b (the append itself), and no
+ * other sequence's first seq_lens tokens use that slot (a shared last block
+ * is copied before it is written, [L7] §5.1).  Otherwise the output is
+ * unspecified (the caches are still written as kv_cache_write would).
+ *
+ *   key, value    [num_seqs][num_kv_heads][head_dim]: the new token's K and V
+ *                 rows; bf16 for PA_BF16 and PA_FP8_E4M3 caches (quantised
+ *                 as kv_cache_write_fp8 does), fp32 for PA_F32 caches.
+ *   slot_mapping  [num_seqs] int64: the new token's slot (< 0: none).
+ *   k_cache, v_cache  written.  All other arguments, the plan, the workspace
+ *                 and the guarantees as in paged_attn_decode_planned.
+ * On the balanced split with a bf16 cache the write costs no launch of its
+ * own: the attention kernel reads the new rows in place of position
+ * seq_lens[b] - 1 and the split-merge kernel, after every read, stores them.
+ * Other shapes run kv_cache_write(_fp8) and then the decode.
+ */
+PA_EXPORT int paged_attn_decode_append(void *out, int32_t out_dtype, const void *q, const void *key,
+                                       const void *value, const int64_t *slot_mapping, void *k_cache,
+                                       void *v_cache, int32_t kv_dtype, float k_scale, float v_scale,
+                                       const void *plan, size_t plan_bytes, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                       int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/*
  * paged_attn_decode_fp8 -- paged_attn_decode over FP8 caches (q bf16
  * [num_seqs][num_heads][head_dim], out PA_F32 or PA_BF16).  All other
  * arguments, the workspace (paged_attn_decode_workspace_size covers it) and

@@ -21,7 +21,7 @@ __all__ = [
     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in", "swap_host_bytes",
     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
-    "paged_attn_decode_noalloc", "PA_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
+    "paged_attn_decode_noalloc", "PA_NOALLOC_SCRATCH_BYTES", "paged_attn_decode_append", "EXPORTED_SYMBOLS",
 ]
 
 PA_F32 = 0
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
                     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8",
                     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
-                    "paged_attn_decode_noalloc")
+                    "paged_attn_decode_noalloc", "paged_attn_decode_append")
 
 
 class PagedAttnError(RuntimeError):
@@ -83,6 +83,9 @@ def _load():
     L.paged_attn_decode_planned.argtypes = ([vp, i32, vp, vp, vp, i32, f32, f32, vp, ctypes.c_size_t, vp, i32, vp]
                                             + [i32] * 7 + [f32, i32, vp, ctypes.c_size_t, vp])
     L.paged_attn_decode_planned.restype = ctypes.c_int
+    L.paged_attn_decode_append.argtypes = ([vp, i32, vp, vp, vp, vp, vp, vp, i32, f32, f32, vp, ctypes.c_size_t,
+                                            vp, i32, vp] + [i32] * 7 + [f32, i32, vp, ctypes.c_size_t, vp])
+    L.paged_attn_decode_append.restype = ctypes.c_int
     L.paged_attn_decode_noalloc.argtypes = ([vp, i32, vp, vp, vp, i32, vp, i32, vp] + [i32] * 7
                                             + [ctypes.c_float, i32, vp])
     L.paged_attn_decode_noalloc.restype = ctypes.c_int
@@ -396,6 +399,39 @@ def paged_attn_decode_planned(out, q, k_cache, v_cache, plan, block_tables, seq_
                                        bs, NB, int(max_seq_len), float(scale), int(partition_size), ws_ptr,
                                        ws_bytes, _stream(stream))
     _check("paged_attn_decode_planned", st)
+
+
+def paged_attn_decode_append(out, q, key, value, slot_mapping, k_cache, v_cache, plan, block_tables, seq_lens,
+                             scale: float, max_seq_len: int, partition_size: int = 0, workspace=None,
+                             k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """One decode step of one layer: key/value [B, Hkv, D] (the new token's rows) written at slot_mapping [B]
+    (int64) and the decode over the caches (dtype picks bf16 / fp32 / FP8), the plan from
+    paged_attn_decode_plan.  Same result as kv_cache_write(_fp8) followed by paged_attn_decode_planned."""
+    torch = _torch()
+    NB, Hkv, bs, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if tuple(key.shape) != (B, Hkv, D) or value.shape != key.shape or tuple(slot_mapping.shape) != (B,):
+        raise ValueError("key/value must be [B, Hkv, D] and slot_mapping [B]")
+    if key.dtype != q.dtype or value.dtype != q.dtype:
+        raise TypeError("key and value must have q's dtype")
+    pptr, pbytes = ctypes.c_void_p(0), 0
+    if plan is not None:
+        pptr, pbytes = _dev(plan, "plan"), plan.numel() * plan.element_size()
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _L().paged_attn_decode_append(_dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dev(key, "key"),
+                                      _dev(value, "value"), _dev(slot_mapping, "slot_mapping", torch.int64),
+                                      _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                                      float(k_scale), float(v_scale), pptr, pbytes,
+                                      _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                                      _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D, bs, NB,
+                                      int(max_seq_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                                      _stream(stream))
+    _check("paged_attn_decode_append", st)
 
 
 # ----------------------------------------------------------------------------- no allocation

@@ -210,6 +210,14 @@ bool mfma_decode_shape(int32_t kv_dtype, int32_t num_heads, int32_t num_kv_heads
          num_heads / num_kv_heads <= 16;
 }
 
+// The new token of every sequence for a decode step that also writes it:
+// key/value [num_seqs][num_kv_heads][head_dim] (bf16 for bf16 and FP8
+// caches, fp32 for fp32 caches), slot_mapping [num_seqs].
+struct AppendRows {
+  const void *key, *value;
+  const int64_t *slot_mapping;
+};
+
 // Every decode entry point.  kv_dtype PA_FP8_E4M3: the caches hold E4M3
 // codes read as value * k_scale / v_scale, q is bf16, and only the MFMA
 // shapes are served.  plan (may be NULL): a plan from
@@ -220,7 +228,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_seq_len, float scale, int32_t partition_size, void *workspace,
                 size_t workspace_bytes, void *stream, bool planned = false, const void *plan_buf = nullptr,
-                size_t plan_bytes = 0) {
+                size_t plan_bytes = 0, const AppendRows *append = nullptr) {
   const bool fp8 = kv_dtype == PA_FP8_E4M3;
   int st = check_attention_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                   max_blocks_per_seq, max_seq_len, fp8 ? PA_BF16 : kv_dtype, out_dtype);
@@ -243,6 +251,22 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return PA_ERR_WORKSPACE;
   if (planned && plan.streamk && (!plan_buf || plan_bytes < plan.plan_bytes)) return PA_ERR_WORKSPACE;
+  // the step's write: folded into the planned bf16 balanced kernels (the
+  // main kernel reads the new rows in place of position L - 1, the merge
+  // kernel writes them to their slots), otherwise written first
+  const bool fold = append && planned && plan.streamk && kv_dtype == PA_BF16;
+  if (append) {
+    if (!append->key || !append->value || !append->slot_mapping) return PA_ERR_NULL;
+    if (!fold) {
+      void *kcw = const_cast<void *>(k_cache), *vcw = const_cast<void *>(v_cache);
+      const int ws = fp8 ? kv_cache_write_fp8(append->key, append->value, PA_BF16, kcw, vcw, append->slot_mapping,
+                                              num_seqs, num_blocks, num_kv_heads, block_size, head_dim, k_scale,
+                                              v_scale, stream)
+                         : kv_cache_write(append->key, append->value, kcw, vcw, append->slot_mapping, num_seqs,
+                                          num_blocks, num_kv_heads, block_size, head_dim, kv_dtype, stream);
+      if (ws != PA_OK) return ws;
+    }
+  }
 
   pa::DecodeParams p = {};
   p.out = out;
@@ -280,6 +304,11 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
       p.plan_rec2 = reinterpret_cast<int2 *>(pb + plan.plan_off_rec2);
       p.sk_desc = reinterpret_cast<int4 *>(pb + plan.plan_off_desc);  // the plan's merge descriptors
       p.plan_stride = plan.plan_stride;
+    }
+    if (fold) {
+      p.new_k = append->key;
+      p.new_v = append->value;
+      p.slot_mapping = append->slot_mapping;
     }
     return launch_status(pa::launch_decode_streamk(p, s));
   }
@@ -374,6 +403,21 @@ int paged_attn_decode_planned(void *out, int32_t out_dtype, const void *q, const
                      max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_seq_len, scale, partition_size, workspace, workspace_bytes, stream, true,
                      plan_buf, plan_bytes);
+}
+
+int paged_attn_decode_append(void *out, int32_t out_dtype, const void *q, const void *key, const void *value,
+                             const int64_t *slot_mapping, void *k_cache, void *v_cache, int32_t kv_dtype,
+                             float k_scale, float v_scale, const void *plan_buf, size_t plan_bytes,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                             int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+  if (kv_dtype != PA_FP8_E4M3 && !dtype_ok(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  const AppendRows rows = {key, value, slot_mapping};
+  return decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_seq_len, scale, partition_size, workspace, workspace_bytes, stream, true,
+                     plan_buf, plan_bytes, &rows);
 }
 
 int paged_attn_decode_fp8(void *out, int32_t out_dtype, const void *q, const void *k_cache, const void *v_cache,

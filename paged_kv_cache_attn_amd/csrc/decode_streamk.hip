@@ -80,9 +80,10 @@ __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, 
 // layer of a decode step.
 enum : int { kFused = 0, kPlanOnly = 1, kPlanned = 2 };
 
-template <int NW, bool FP8, int MODE>
+template <int NW, bool FP8, int MODE, bool APPEND = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
     DecodeParams p) {
+  static_assert(!APPEND || (MODE == kPlanned && !FP8), "the folded write serves planned bf16 calls");
   using F = KVFormat<FP8>;
   __shared__ int s_pref[MODE == kPlanned ? 1 : kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[MODE == kPlanned ? 1 : kStreamKMaxSeqs];       // clamped sequence lengths
@@ -296,6 +297,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     typename F::Raw t;
     bf16x8 q[4];
     int lim;
+    // APPEND: the step's new K/V row of this tile's (sequence, KV head),
+    // loaded with a row's last tile; `last` (uniform) marks such a tile, `at`
+    // is the element offset of position L - 1 in the cache and `sm` the slot
+    // the caller gives the new row: the row replaces position L - 1 only when
+    // the two name the same place.
+    u32x4 nk[4], nv;
+    int64_t at, sm;
+    int last, tpos;
   };
   auto load_slot = [&](int li, Slot &sl, int dist) {
     const int lp = li - dist;
@@ -313,6 +322,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // a masked tile reads the first rows of the cache
     const bool stream = __builtin_amdgcn_readfirstlane(s_keep[li]) == 0;
     F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c, stream);
+    if constexpr (APPEND) {
+      const int2 ln = s_ln[li];
+      sl.last = ok && s_pj[li] == ln.y - 1;  // uniform: the position's record
+      if (sl.last) {
+        sl.tpos = (ln.x - 1) & 15;  // position L - 1 inside the tile
+        sl.at = (sl.tpos < 8 ? (int64_t)u.x << 10 : (int64_t)u.y << 10) + (sl.tpos & 7) * kD;
+        sl.sm = p.slot_mapping[b];
+        const uint16_t *nkr = reinterpret_cast<const uint16_t *>(p.new_k) + ((int64_t)b * Hkv + kh) * kD;
+        const uint16_t *nvr = reinterpret_cast<const uint16_t *>(p.new_v) + ((int64_t)b * Hkv + kh) * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sl.nk[i] = ld16(nkr + 32 * i + 8 * r);
+        sl.nv = ld16(nvr + 8 * c);
+      }
+    }
     const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
     if (__builtin_amdgcn_readfirstlane((int)need_q))
       F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
@@ -382,6 +405,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       auto one = [&](int li, auto kc) __attribute__((always_inline)) -> bool {
         constexpr int k = decltype(kc)::value;
         load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS);
+        if constexpr (APPEND) {
+          if (s[k].last) {
+            // the new row replaces position L - 1 (lane (r, c) holds K of
+            // token c and V of tokens 4r .. 4r+3) when the slot names it
+            // (block sizes of this path are powers of two)
+            const int64_t sm = s[k].sm;
+            const int lb = __builtin_ctz((unsigned)p.block_size);
+            const bool hit = sm >= 0 && sm < ((int64_t)p.num_blocks << lb) &&
+                             ((((sm >> lb) * Hkv + s_prow[li] % Hkv) << lb) + (sm & (p.block_size - 1))) * kD ==
+                                 s[k].at;
+            if (hit) {
+              const int tp = s[k].tpos;
+              if (c == tp) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[k].t.k[i] = s[k].nk[i];
+              }
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (4 * r + v == tp) s[k].t.v[v] = s[k].nv;
+            }
+          }
+        }
         st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
         return after_step(li);
       };
@@ -499,6 +544,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // range gi -- so those are loaded together with the descriptor, in one
 // memory round trip; rows with more pieces take a second one.  A thread
 // owns output elements (column, dim).
+//
+// APPEND: the workgroups also write the step's new K/V rows to their slots
+// (row gi, gi + grid, ...), after every read of the main kernel, as
+// kv_cache_write does: slot < 0 or past the cache skips the row.
+template <bool APPEND>
 __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
   constexpr int kPer = 2;  // the launch uses g * kD / 2 threads: two elements each
@@ -524,6 +574,17 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
       so[k][u] = p.sk_part[pc[k] * kD + d];
     }
   }
+  // APPEND: row gi's new K (threads 0 .. 15) or V (16 .. 31) chunk and its
+  // slot, loaded with the rest
+  int64_t wsm = -1;
+  u32x4 wdat = {0u, 0u, 0u, 0u};
+  const int wpart = threadIdx.x / (kD / 8), wch = threadIdx.x % (kD / 8);
+  if constexpr (APPEND) {
+    if (gi < nrows && threadIdx.x < 2 * (kD / 8)) {
+      wsm = p.slot_mapping[gi / p.num_kv_heads];
+      wdat = ld16(reinterpret_cast<const uint16_t *>(wpart ? p.new_v : p.new_k) + (int64_t)gi * kD + 8 * wch);
+    }
+  }
   asm volatile("" ::: "memory");  // keep those loads ahead of the branch below
   // rows with no tokens (no piece, no range) get zeros, spread over the
   // workgroups: row gi, gi + grid, ...
@@ -532,6 +593,26 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
     const int b = zr / p.num_kv_heads, kh = zr - b * p.num_kv_heads;
     for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x)
       store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
+  }
+  if constexpr (APPEND) {
+    // rows gi, gi + grid, ...: 16-byte chunks, threads 0 .. 15 the K row,
+    // 16 .. 31 the V row (block sizes of this path are powers of two)
+    const int lb = __builtin_ctz((unsigned)p.block_size);
+    const int64_t nslots = (int64_t)p.num_blocks << lb;
+    for (int wr = gi; wr < nrows; wr += (int)gridDim.x) {
+      if (threadIdx.x >= 2 * (kD / 8)) break;
+      const int kh = wr % p.num_kv_heads;
+      int64_t sm = wsm;
+      u32x4 dat = wdat;
+      if (wr != gi) {  // beyond the first row: loaded here
+        sm = p.slot_mapping[wr / p.num_kv_heads];
+        dat = ld16(reinterpret_cast<const uint16_t *>(wpart ? p.new_v : p.new_k) + (int64_t)wr * kD + 8 * wch);
+      }
+      if (sm < 0 || sm >= nslots) continue;
+      const int64_t dst = ((((sm >> lb) * p.num_kv_heads + kh) << lb) + (sm & (p.block_size - 1))) * kD;
+      uint16_t *cache = reinterpret_cast<uint16_t *>(const_cast<void *>(wpart ? p.v_cache : p.k_cache));
+      st16(cache + dst + 8 * wch, dat);
+    }
   }
   // a planned call's descriptors come from the plan: trusted for their
   // values, not for their bounds (a stale or foreign plan gives wrong
@@ -605,6 +686,15 @@ hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
   const size_t park = (size_t)PA_DECODE_WAVES * 2 * g * (kD + 2) * sizeof(float);
   const dim3 grid(p.sk_ranges), block(64 * PA_DECODE_WAVES);
   const bool planned = p.plan_hdr != nullptr;
+  if (p.new_k) {
+    // the step's write folded in (planned bf16 calls only; the caller checks)
+    hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kPlanned, true>), grid, block, park, stream,
+                       p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_streamk_merge_kernel<true>, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.kv_fp8 && planned)
     hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, true, kPlanned>), grid, block, park, stream, p);
   else if (p.kv_fp8)
@@ -615,7 +705,7 @@ hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kFused>), grid, block, park, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_streamk_merge_kernel, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
+  hipLaunchKernelGGL(decode_streamk_merge_kernel<false>, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -86,6 +86,10 @@ struct DecodeParams {
   int2 *plan_rec2;         // [ranges][plan_stride] {sequence length, blocks of the row
                            //   | kKeepTile if a neighbouring row uses the tile's block}
   int plan_stride;         // positions per range in the plan (>= every range's size)
+  // the step's write folded into a planned bf16 call (nullptr: none)
+  const void *new_k;       // [B][Hkv][D] bf16: the new token's K row of every sequence
+  const void *new_v;       // [B][Hkv][D]
+  const int64_t *slot_mapping;  // [B]: its slot (< 0: none)
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);

@@ -283,6 +283,30 @@ def test_plan_validation(pa):
     assert run(*r[:13], 0, *r[14:]) == PA_OK
 
 
+def test_decode_append_validation(pa):
+    f = pa.lib.paged_attn_decode_append
+    n = pa.lib.paged_attn_decode_plan_size(64, 32, 8, 128, 16, 128, 2048, 0, 1)
+    need = pa.paged_attn_decode_workspace_size(64, 32, 8, 128, 16, 2048, 0)
+    # out, odt, q, key, value, slots, k, v, kvdt, ks, vs, plan, bytes, bt, maxblk, sl, B, Hq, Hkv, D, bs, NB,
+    # max_len, scale, part, ws, wsb, stream
+    a = [P, 0, P, P, P, P, P, P, 1, 1.0, 1.0, P, n, P, 128, P, 64, 32, 8, 128, 16, 4096, 2048, 0.1, 0, P, need, N]
+
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return f(*b)
+
+    assert call(a3=N) == PA_ERR_NULL          # key
+    assert call(a4=N) == PA_ERR_NULL          # value
+    assert call(a5=N) == PA_ERR_NULL          # slot_mapping
+    assert call(a8=7) == PA_ERR_UNSUPPORTED
+    assert call(a11=N) == PA_ERR_WORKSPACE    # the plan
+    assert call(a26=16) == PA_ERR_WORKSPACE      # far below what the split needs
+    assert call(a17=30) == PA_ERR_SHAPE       # Hq not a multiple of Hkv
+    assert call(a16=0) == PA_OK               # no sequences: nothing to write or read
+
+
 def test_binding_refuses_cpu_tensors(pa):
     import torch
     k = torch.zeros(4, 2, 16, 64)
