@@ -98,6 +98,29 @@ PA_EXPORT const char *pa_status_string(int status);
 PA_EXPORT int pa_abi_version(void);
 
 /*
+ * pa_debug_flags -- what the kernels' bounds checks have masked since the
+ * last clear (host; the debug build libpagedattn_debug.so only).  In every
+ * build the kernels skip or mask out-of-range device-side ids without
+ * dereferencing them; the debug build also records each kind it meets as a
+ * bit of a per-device flag word, and checks two caller contracts the release
+ * build trusts (no duplicate slots in one kv_cache_write, no conflicting
+ * pairs in one block_copy).  Waits for the current device to finish
+ * (hipDeviceSynchronize), stores the OR of the flags in *flags and clears
+ * them if `clear` is nonzero.  The release build stores 0 and returns
+ * PA_ERR_UNSUPPORTED.
+ */
+#define PA_DEBUG_SLOT_RANGE (1u << 0)     /* slot >= num_blocks * block_size (skipped)         */
+#define PA_DEBUG_SLOT_DUP (1u << 1)       /* two tokens of one kv_cache_write share a slot      */
+#define PA_DEBUG_BLOCK_RANGE (1u << 2)    /* block-table entry outside [0, num_blocks) (masked) */
+#define PA_DEBUG_PAIR_RANGE (1u << 3)     /* block_copy id outside [0, num_blocks) (skipped)    */
+#define PA_DEBUG_PAIR_CONFLICT (1u << 4)  /* a dst twice, or a dst that is another pair's src   */
+#define PA_DEBUG_LEN_CLAMPED (1u << 5)    /* seq_lens < 0 or past the call's bound (clamped)    */
+#define PA_DEBUG_QUERY_LOC (1u << 6)      /* query_start_loc not a partition of the query rows  */
+#define PA_DEBUG_SWAP_RANGE (1u << 7)     /* swap id outside [0, num_blocks)                    */
+#define PA_DEBUG_PLAN (1u << 8)           /* plan record outside the call's cache or rows       */
+PA_EXPORT int pa_debug_flags(unsigned *flags, int clear);
+
+/*
  * kv_cache_write -- scatter new K/V rows into their cache slots
  * ([L7] §4.3 first fused kernel; [L7] §4.1 and [L16] §3.3: a token lands in
  * the next free slot of its sequence's last block).

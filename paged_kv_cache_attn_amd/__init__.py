@@ -22,6 +22,7 @@ __all__ = [
     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
     "paged_attn_decode_noalloc", "PA_NOALLOC_SCRATCH_BYTES", "paged_attn_decode_append", "EXPORTED_SYMBOLS",
+    "load_debug_library", "debug_flags", "DEBUG_BITS",
 ]
 
 PA_F32 = 0
@@ -30,13 +31,14 @@ PA_FP8_E4M3 = 2
 PA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's built-in decode scratch (include/paged_attn.h)
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+debug_library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn_debug.so")
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
                     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
                     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8",
                     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
-                    "paged_attn_decode_noalloc", "paged_attn_decode_append")
+                    "paged_attn_decode_noalloc", "paged_attn_decode_append", "pa_debug_flags")
 
 
 class PagedAttnError(RuntimeError):
@@ -45,16 +47,19 @@ class PagedAttnError(RuntimeError):
         self.status = status
 
 
-def _load():
-    if not os.path.exists(library_path):
-        raise ImportError("libpagedattn.so is not built (run `python -m paged_kv_cache_attn_amd.build`); "
-                          "there is no fallback path")
-    L = ctypes.CDLL(library_path)
+def _load(path=None):
+    path = path or library_path
+    if not os.path.exists(path):
+        raise ImportError("%s is not built (run `python -m paged_kv_cache_attn_amd.build`); "
+                          "there is no fallback path" % os.path.basename(path))
+    L = ctypes.CDLL(path)
     vp, i32, i64p, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []
     L.pa_abi_version.restype = ctypes.c_int
+    L.pa_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int]
+    L.pa_debug_flags.restype = ctypes.c_int
     L.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [vp]
     L.kv_cache_write.restype = ctypes.c_int
     L.paged_attn_decode_workspace_size.argtypes = [i32] * 7
@@ -454,3 +459,23 @@ def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, 
                                        _dev(seq_lens, "seq_lens", torch.int32), B, Hq, Hkv, D, bs, NB,
                                        int(max_seq_len), float(scale), int(partition_size), _stream(stream))
     _check("paged_attn_decode_noalloc", st)
+
+
+# ----------------------------------------------------------------------------- debug build
+# Bits of pa_debug_flags (include/paged_attn.h).
+DEBUG_BITS = {"slot_range": 1 << 0, "slot_dup": 1 << 1, "block_range": 1 << 2, "pair_range": 1 << 3,
+              "pair_conflict": 1 << 4, "len_clamped": 1 << 5, "query_loc": 1 << 6, "swap_range": 1 << 7,
+              "plan": 1 << 8}
+
+
+def load_debug_library():
+    """The debug build (libpagedattn_debug.so) as a ctypes library with the same signatures, for calling
+    directly; its kernels also record what their bounds checks mask (read with debug_flags)."""
+    return _load(debug_library_path)
+
+
+def debug_flags(lib, clear: bool = True) -> int:
+    """pa_debug_flags of `lib` (waits for the device): the OR of the recorded bits (DEBUG_BITS)."""
+    v = ctypes.c_uint(0)
+    _check("pa_debug_flags", lib.pa_debug_flags(ctypes.byref(v), int(bool(clear))))
+    return int(v.value)

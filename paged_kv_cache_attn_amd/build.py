@@ -1,9 +1,12 @@
 """Build libpagedattn.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m paged_kv_cache_attn_amd.build
+    python -m paged_kv_cache_attn_amd.build [--debug | --all]
 
 Each .hip source is compiled to an object under _build/ (in parallel), then
-linked into paged_kv_cache_attn_amd/libpagedattn.so.  Always rebuilds.
+linked into paged_kv_cache_attn_amd/libpagedattn.so.  The debug build
+(PAGED_ATTN_DEBUG=1: the kernels also report what their bounds checks mask,
+read with pa_debug_flags) goes to libpagedattn_debug.so, its objects under
+_build/debug/.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -19,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
+DEBUG_LIB = os.path.join(PKG, "libpagedattn_debug.so")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -38,9 +42,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, "debug" if debug else "", os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC] + CFLAGS + (["-DPAGED_ATTN_DEBUG=1"] if debug else []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -51,23 +55,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, debug: bool = False) -> str:
+    """Compile and link the release library (or, with debug=True, the debug one); returns its path."""
+    lib = DEBUG_LIB if debug else LIB
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, debug), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
     # -z defs: a symbol the objects leave undefined (a kernel stub the host
     # pass did not emit, say) fails the link instead of the first dlopen
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    if "--all" in sys.argv[1:]:
+        build()
+        build(debug=True)
+    else:
+        build(debug="--debug" in sys.argv[1:])

@@ -154,6 +154,31 @@ const char *pa_status_string(int status) {
 
 int pa_abi_version(void) { return PA_ABI_VERSION; }
 
+int pa_debug_flags(unsigned *flags, int clear) {
+#if PAGED_ATTN_DEBUG
+  if (!flags) return PA_ERR_NULL;
+  if (hipDeviceSynchronize() != hipSuccess) return PA_ERR_LAUNCH;
+  hipError_t (*const words[])(void **) = {pa::debug_word_ops, pa::debug_word_decode, pa::debug_word_streamk,
+                                          pa::debug_word_prefill};
+  unsigned all = 0;
+  for (auto word : words) {
+    void *p = nullptr;
+    unsigned v = 0;
+    if (word(&p) != hipSuccess || hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+      return PA_ERR_LAUNCH;
+    all |= v;
+    if (clear && hipMemset(p, 0, sizeof v) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (clear && hipDeviceSynchronize() != hipSuccess) return PA_ERR_LAUNCH;
+  *flags = all;
+  return PA_OK;
+#else
+  (void)clear;
+  if (flags) *flags = 0;
+  return PA_ERR_UNSUPPORTED;
+#endif
+}
+
 int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
                    const int64_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,

@@ -48,8 +48,9 @@ __device__ __forceinline__ void load_kv_tile_d128(KVTile &t, const uint16_t *kt,
 // is described by two table-derived entries e0, e1:
 //   bs >= 16: e0 = physical block, e1 = sub-tile index inside it;
 //   bs == 8:  e0, e1 = physical blocks of its two halves.
-// An entry out of range is replaced by block 0 and reported, so the caller
-// masks the tile instead of dereferencing it.  nblk_tab = ceil(L / bs) is the
+// An entry out of range is replaced by block 0 and reported to the caller,
+// which masks the tile instead of dereferencing it (and, in the debug build,
+// records it).  nblk_tab = ceil(L / bs) is the
 // number of table entries the row uses; the second half of a bs = 8 tile past
 // it is never read (its tokens are past L and masked).
 struct TileRows {

@@ -130,6 +130,7 @@ __device__ __forceinline__ float *vec_attend(float *red, const float (&q)[GC][Ve
     for (int u = 0; u < U; ++u) {
       const int t = tok(k, u);
       const int e = t < t1 ? table[t / bs] : -1;
+      debug_report(t < t1 && (unsigned)e >= (unsigned)num_blocks, kDbgBlockRange);
       ph[u] = (unsigned)e < (unsigned)num_blocks ? e : -1;  // -1: masked
     }
   };

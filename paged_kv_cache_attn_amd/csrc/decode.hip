@@ -105,6 +105,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_d128_kernel(DecodeParams 
   auto load = [&](int j, typename F::Raw &t, int &lim) {
     int e0, e1;
     const bool ok = map.entries(table, j, nblk_tab, e0, e1);
+    debug_report(!ok, kDbgBlockRange);
     lim = ok ? L : 0;
     F::load(t, kc, vc, map.rows(e0, e1, kh), r, c, stream);
   };
@@ -344,6 +345,10 @@ void launch_vec(dim3 grid, dim3 block, hipStream_t stream, const Params &p) {
 }
 
 }  // namespace
+
+#if PAGED_ATTN_DEBUG
+PA_DEBUG_WORD_ACCESSOR(debug_word_decode)
+#endif
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int g = p.num_heads / p.num_kv_heads;

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // one wave scans with cross-lane adds; a single barrier publishes it
       if (w == 0) {
         int L = lane < B ? p.seq_lens[lane] : 0;
-        L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
+        L = clamp_len(L, p.max_len_cap);
         const int v = ((L + kBS - 1) / kBS) * Hkv;
         int incl = v;
   #pragma unroll
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       int local = 0;
       for (int b = b0; b < b1; ++b) {
         int L = p.seq_lens[b];
-        L = L < 0 ? 0 : (L > p.max_len_cap ? p.max_len_cap : L);
+        L = clamp_len(L, p.max_len_cap);
         s_len[b] = L;
         local += ((L + kBS - 1) / kBS) * Hkv;
       }
@@ -194,6 +194,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       int e0, e1;
       const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
                                   (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
+      debug_report(!ok, kDbgBlockRange);
       const TileRows tr = map.rows(e0, e1, kh);
       // A tile read by this row only streams through the caches (non-temporal
       // loads); one whose block the previous or the next sequence also uses at
@@ -265,6 +266,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (li < e - s) {
         const bool ok = ra[k].x >= -1 && ra[k].x < units && ra[k].y >= 0 && ra[k].y < units && ra[k].z >= 0 &&
                         ra[k].z < B * Hkv && ra[k].w >= 0;
+        debug_report(!ok, kDbgPlan);
         s_rows[li] = ok ? int2{ra[k].x, ra[k].y} : int2{-1, 0};
         s_prow[li] = ok ? ra[k].z : 0;
         s_pj[li] = ok ? ra[k].w : 0;
@@ -674,6 +676,10 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
 }
 
 }  // namespace
+
+#if PAGED_ATTN_DEBUG
+PA_DEBUG_WORD_ACCESSOR(debug_word_streamk)
+#endif
 
 hipError_t launch_decode_streamk_plan(const DecodeParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kPlanOnly>), dim3(p.sk_ranges),

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   // Consume all three loads before the slot test, so the compiler cannot sink
   // the data loads behind it: they are issued together, one round trip.
   asm volatile("" ::"v"(kv), "v"(vv), "v"(slot));
+  debug_report(slot >= num_slots, kDbgSlotRange);
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot - blk * block_size);
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(256) void kv_cache_write_fp8_kernel(
   }
   const int64_t slot = slot_mapping[t];
   asm volatile("" ::"v"(ks[0]), "v"(vs[0]), "v"(slot));
+  debug_report(slot >= num_slots, kDbgSlotRange);
   if (slot < 0 || slot >= num_slots) return;
   // source value j (0..15) of a row piece
   auto val = [&](const u32x4 *s, int j) -> float {
@@ -103,6 +105,38 @@ __global__ __launch_bounds__(256) void kv_cache_write_fp8_kernel(
   st16(v_cache + dst, vq);
 }
 
+#if PAGED_ATTN_DEBUG
+PA_DEBUG_WORD_ACCESSOR(debug_word_ops)
+
+// Debug build: thread t compares its slot with those of the later tokens.
+__global__ __launch_bounds__(256) void debug_dup_slots_kernel(const int64_t *__restrict__ slots, int n,
+                                                              int64_t num_slots) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_slots) return;
+  bool dup = false;
+  for (int u = t + 1; u < n; ++u) dup |= slots[u] == s;
+  debug_report(dup, kDbgSlotDup);
+}
+
+// Debug build: pair i against every other pair j: a dst used twice, or a dst
+// that is another pair's src (the copies run concurrently).
+__global__ __launch_bounds__(256) void debug_pair_conflicts_kernel(const int64_t *__restrict__ pairs, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t src = pairs[2 * (int64_t)i], dst = pairs[2 * (int64_t)i + 1];
+  if (src == dst) return;  // a no-op
+  bool bad = false;
+  for (int j = 0; j < n; ++j) {
+    const int64_t s2 = pairs[2 * (int64_t)j], d2 = pairs[2 * (int64_t)j + 1];
+    if (j == i || s2 == d2) continue;  // itself, or another no-op
+    bad |= d2 == dst || s2 == dst || d2 == src;
+  }
+  debug_report(bad, kDbgPairConflict);
+}
+#endif
+
 hipError_t launch_kv_cache_write_fp8(const void *key, const void *value, int src_bf16, void *k_cache,
                                      void *v_cache, const int64_t *slot_mapping, int num_tokens,
                                      int num_blocks, int num_kv_heads, int block_size, int head_dim,
@@ -115,6 +149,10 @@ hipError_t launch_kv_cache_write_fp8(const void *key, const void *value, int src
   const uint8_t *k8 = (const uint8_t *)key, *v8 = (const uint8_t *)value;
   uint8_t *kc = (uint8_t *)k_cache, *vc = (uint8_t *)v_cache;
   const bool narrow = total < INT32_MAX && num_slots < INT32_MAX;
+#if PAGED_ATTN_DEBUG
+  hipLaunchKernelGGL(debug_dup_slots_kernel, dim3((num_tokens + 255) / 256), dim3(256), 0, stream, slot_mapping,
+                     num_tokens, num_slots);
+#endif
   if (narrow && src_bf16)
     hipLaunchKernelGGL((kv_cache_write_fp8_kernel<uint32_t, true>), dim3((unsigned)grid), dim3(256), 0, stream,
                        k8, v8, kc, vc, slot_mapping, (uint32_t)total, num_kv_heads, block_size, row_chunks,
@@ -142,6 +180,7 @@ __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t *__restrict__ k
                                                          int64_t num_blocks, int block_chunks) {
   const int64_t src = pairs[2 * (int64_t)blockIdx.x];
   const int64_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  debug_report(threadIdx.x == 0 && (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks), kDbgPairRange);
   if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
   uint8_t *cache = blockIdx.y == 0 ? k_cache : v_cache;
   const int64_t bytes = (int64_t)block_chunks * 16;
@@ -172,6 +211,7 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(uint8_t *__restrict__ 
                                                           int64_t num_blocks, int block_chunks) {
   const int64_t id = ids[blockIdx.x];
   const bool ok = id >= 0 && id < num_blocks;
+  debug_report(threadIdx.x == 0 && !ok, kDbgSwapRange);
   if (!kGather && !ok) return;
   const int64_t bytes = (int64_t)block_chunks * 16;
   uint8_t *blk = (blockIdx.y == 0 ? k_cache : v_cache) + (ok ? id : 0) * bytes;
@@ -215,6 +255,10 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, void *k_cac
   if (total == 0) return hipSuccess;
   const int64_t grid = (total + 255) / 256;
   const int64_t num_slots = (int64_t)num_blocks * block_size;
+#if PAGED_ATTN_DEBUG
+  hipLaunchKernelGGL(debug_dup_slots_kernel, dim3((num_tokens + 255) / 256), dim3(256), 0, stream, slot_mapping,
+                     num_tokens, num_slots);
+#endif
   if (total < INT32_MAX && num_slots < INT32_MAX)
     hipLaunchKernelGGL(kv_cache_write_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, stream,
                        (const uint8_t *)key, (const uint8_t *)value, (uint8_t *)k_cache, (uint8_t *)v_cache,
@@ -231,6 +275,10 @@ hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs,
                              int elem_bytes, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
   const int block_chunks = num_kv_heads * block_size * head_dim * elem_bytes / 16;
+#if PAGED_ATTN_DEBUG
+  hipLaunchKernelGGL(debug_pair_conflicts_kernel, dim3((num_pairs + 255) / 256), dim3(256), 0, stream, pairs,
+                     num_pairs);
+#endif
   hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)num_pairs, 2), dim3(256), 0, stream,
                      (uint8_t *)k_cache, (uint8_t *)v_cache, pairs, (int64_t)num_blocks,
                      block_chunks);

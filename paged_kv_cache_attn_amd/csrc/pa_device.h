@@ -39,9 +39,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// -- Debug build ---------------------------------------------------------------
+// Built with PAGED_ATTN_DEBUG=1, the kernels also report what their bounds
+// checks mask (they never dereference it, in either build): each bit below is
+// set in a flag word when the condition is met at least once.  Every
+// translation unit has its own word (a file-scope device variable); the host
+// reads them all through pa_debug_flags.  In the release build the reports
+// compile to nothing.
+#ifndef PAGED_ATTN_DEBUG
+#define PAGED_ATTN_DEBUG 0
+#endif
+enum : unsigned {
+  kDbgSlotRange = 1u << 0,     // a slot at or past num_blocks * block_size (skipped)
+  kDbgSlotDup = 1u << 1,       // two tokens of one kv_cache_write with the same slot
+  kDbgBlockRange = 1u << 2,    // a block-table entry outside [0, num_blocks) (masked)
+  kDbgPairRange = 1u << 3,     // a block_copy id outside [0, num_blocks) (skipped)
+  kDbgPairConflict = 1u << 4,  // a dst used twice, or a dst that is another pair's src
+  kDbgLenClamped = 1u << 5,    // a sequence length < 0 or past the call's bound (clamped)
+  kDbgQueryLoc = 1u << 6,      // query_start_loc not a valid partition of the query rows
+  kDbgSwapRange = 1u << 7,     // a swap id outside [0, num_blocks)
+  kDbgPlan = 1u << 8,          // a plan record outside the call's cache or rows (masked)
+};
+#if PAGED_ATTN_DEBUG
+static __device__ unsigned pa_debug_word;
+// Device address of this translation unit's flag word (host).
+#define PA_DEBUG_WORD_ACCESSOR(name) \
+  hipError_t name(void **p) { return hipGetSymbolAddress(p, HIP_SYMBOL(pa_debug_word)); }
+#endif
+__device__ __forceinline__ void debug_report(bool cond, unsigned bit) {
+#if PAGED_ATTN_DEBUG
+  // a wave-uniform branch (so values the caller keeps in scalar registers
+  // stay uniform), then one lane's vector atomic in global memory
+  if (__builtin_amdgcn_ballot_w64(cond) != 0) {
+    if (cond && __builtin_amdgcn_readfirstlane(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) ==
+                    __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)))
+      atomicOr(&pa_debug_word, bit);
+  }
+#else
+  (void)cond;
+  (void)bit;
+#endif
+}
+
 // A sequence length clamped to [0, cap] (cap: the tokens the table and the
 // host bound admit).
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+__device__ __forceinline__ int clamp_len(int L, int cap) {
+  debug_report(L < 0 || L > cap, kDbgLenClamped);
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
 
 // One 16-byte load per lane from global memory straight into LDS: lane i's
 // bytes land at lds_base + 16 i (lds_base is the same for the whole wave).

@@ -119,4 +119,16 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 
+#ifndef PAGED_ATTN_DEBUG
+#define PAGED_ATTN_DEBUG 0
+#endif
+#if PAGED_ATTN_DEBUG
+// Device addresses of the debug flag words of the four kernel files (debug
+// build only; see pa_device.h).
+hipError_t debug_word_ops(void **p);
+hipError_t debug_word_decode(void **p);
+hipError_t debug_word_streamk(void **p);
+hipError_t debug_word_prefill(void **p);
+#endif
+
 }  // namespace pa

@@ -111,8 +111,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int tpg = NW * tpw;              // per workgroup
   const int q0 = p.query_start_loc[b];
   const int n_b = p.query_start_loc[b + 1] - q0;
-  if (tile * tpg >= n_b || q0 < 0) return;  // the whole workgroup leaves together
   const int S = clamp_len(p.seq_lens[b], p.max_len_cap);
+  debug_report(threadIdx.x == 0 && (q0 < 0 || n_b < 0 || n_b > S || (int64_t)q0 + n_b > p.num_query_tokens),
+               kDbgQueryLoc);
+  if (tile * tpg >= n_b || q0 < 0) return;  // the whole workgroup leaves together
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -166,7 +168,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ja = 2 * pr, jb = 2 * pr + 1;
     int a0, a1, b0, b1;
     const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
-    const bool okb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1) && jb < nblk;
+    const bool entb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1);
+    const bool okb = entb && jb < nblk;
+    const int bad = !oka || (jb < nblk && !entb);  // an entry out of range (bit 2 of the result)
     const TileRows ra = map.rows(a0, a1, kh);
     const TileRows rb = map.rows(b0, b1, kh);  // the odd tail repeats tile nblk - 1, masked
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int64_t base = (uw & (kTileChunks / 2)) == 0 ? tr.lo : tr.hi - 8 * D;
       regs[k] = ld16(((kind & 1) ? vc : kc) + base + ((uw & (kTileChunks - 1)) + lane) * kChunkElems);
     }
-    return (int)oka | ((int)okb << 1);
+    return (int)oka | ((int)okb << 1) | (bad << 2);
   };
   // Direct pair load (bf16): the k-th load of wave w fills the 64 consecutive
   // 16-byte slots of the stage from slot (k * NW + w) * 64 on, one per lane
@@ -199,7 +203,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ja = 2 * pr, jb = 2 * pr + 1;
     int a0, a1, b0, b1;
     const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
-    const bool okb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1) && jb < nblk;
+    const bool entb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1);
+    const bool okb = entb && jb < nblk;
+    const int bad = !oka || (jb < nblk && !entb);  // an entry out of range (bit 2 of the result)
     const TileRows ra = map.rows(a0, a1, kh);
     const TileRows rb = map.rows(b0, b1, kh);
     if constexpr (kRowsContig) {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         load_lds16(src, stage_mem(st) + slot0 * 16);
       }
     }
-    return (int)oka | ((int)okb << 1);
+    return (int)oka | ((int)okb << 1) | (bad << 2);
   };
   // LDS byte offset of bf16 chunk kc (0..15) of row t in a K or a V tile
   auto lds_off = [](bool is_v, int t, int kc) -> int {
@@ -306,6 +312,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   MfmaAttnPairState st[CG];
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) st[cg].init();
+  int seen = 0;  // OR of the pairs' load results: bit 2 = a block-table entry out of range
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -352,6 +359,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       lread_v(cur, vt);
       lread_k(nxt, ka, kb);
       const int okbits = ok[decltype(cur)::value];
+      seen |= okbits;
       const int tok0 = 32 * X;
       const bool oka = okbits & 1, okb = okbits & 2;
       const bool full0 = tok0 + 32 <= lim_min[0] && oka && okb;
@@ -423,6 +431,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       vm_wait<2 * kChunksPerThread>();
       workgroup_barrier();
       ok[decltype(nxt)::value] = dma(X + 3, nxt);
+      seen |= ok[decltype(cur)::value];
       compute(cur, X, ok[decltype(cur)::value], st);
       return X + 1 < npair;
     };
@@ -449,6 +458,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (X + 1 < npair) lstore(std::integral_constant<int, j1>(), rs[j1]);
       ok_s[j1] = ok_r[j1];
       ok_r[j] = gload(X + 3, rs[j]);
+      seen |= ok_s[j];
       compute(phase, X, ok_s[j], st);
       return X + 1 < npair;
     };
@@ -459,6 +469,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
 
+  // (reported after the loop: a report inside it would keep the table out of
+  // the scalar cache in the debug build)
+  debug_report((seen >> 2) & 1, kDbgBlockRange);
+  (void)seen;
   // acc[t][i] = O[column c][dim 16t + 4r + i]
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
@@ -496,10 +510,13 @@ __global__ __launch_bounds__(64 * kVecWaves) void prefill_vec_kernel(PrefillPara
   const int qi = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.query_start_loc[b];
   const int n_b = p.query_start_loc[b + 1] - q0;
+  const int S = clamp_len(p.seq_lens[b], p.max_len_cap);
+  debug_report(qi == 0 && threadIdx.x == 0 &&
+                   (q0 < 0 || n_b < 0 || n_b > S || (int64_t)q0 + n_b > p.num_query_tokens),
+               kDbgQueryLoc);
   // (uniform over the workgroup: it leaves together)
   if (qi >= n_b || q0 < 0 || (int64_t)q0 + qi >= p.num_query_tokens) return;
   const int g = p.num_heads / p.num_kv_heads;
-  const int S = clamp_len(p.seq_lens[b], p.max_len_cap);
   const int nkeys = max(0, min(S, S - n_b + qi + 1));
   const int col = ((threadIdx.x & 63) % G::kLPR) * G::kVPL;
   const float sl2 = p.scale * kLog2e;
@@ -542,6 +559,10 @@ void launch_vec(dim3 grid, dim3 block, hipStream_t stream, const Params &p) {
 }
 
 }  // namespace
+
+#if PAGED_ATTN_DEBUG
+PA_DEBUG_WORD_ACCESSOR(debug_word_prefill)
+#endif
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_query_len == 0) return hipSuccess;

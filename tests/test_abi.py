@@ -11,6 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_attn.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn.so")
+DEBUG_LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn_debug.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 PA_ERR_SCRATCH = -6
@@ -45,6 +46,30 @@ def test_library_exports_every_declared_symbol(pa):
         assert n in exported, n
         assert hasattr(pa.lib, n)
     assert set(pa.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_debug_library_exports_every_declared_symbol(pa):
+    if not os.path.exists(DEBUG_LIB):
+        from paged_kv_cache_attn_amd import build as b
+        b.build(debug=True)
+    out = subprocess.run(["nm", "-D", "--defined-only", DEBUG_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in declared_functions():
+        assert n in exported, n
+
+
+def test_debug_flags_release_and_debug(pa):
+    """The release build has no flag words: pa_debug_flags stores 0 and says so; the debug build refuses a
+    NULL destination before it touches the GPU.  The bits match the header."""
+    v = ctypes.c_uint(7)
+    assert pa.lib.pa_debug_flags(ctypes.byref(v), 1) == PA_ERR_UNSUPPORTED and v.value == 0
+    dlib = pa.load_debug_library()
+    assert dlib.pa_debug_flags(None, 1) == PA_ERR_NULL
+    text = open(HEADER).read()
+    for name, bit in pa.DEBUG_BITS.items():
+        m = re.search(r"#define PA_DEBUG_%s \(1u << (\d+)\)" % name.upper(), text)
+        assert m and (1 << int(m.group(1))) == bit, name
 
 
 def test_abi_version_and_status_strings(pa):
