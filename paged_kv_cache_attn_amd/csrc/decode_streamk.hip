@@ -94,6 +94,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int s_pj[kStreamKTabCache];       // block index inside the row
   __shared__ int2 s_ln[kStreamKTabCache];      // {sequence length, blocks of the row} of each position
   __shared__ int s_keep[kStreamKTabCache];     // 1: a neighbouring row uses the position's block
+  __shared__ int64_t s_slot[APPEND ? kStreamKMaxSeqs : 1];  // APPEND: each sequence's new-token slot
   __shared__ int s_brow[NW][2];                // row start of each parked boundary state (-1: none)
   __shared__ int s_brid[NW][2];                // its row, b * Hkv + kh
   __shared__ int s_bnb[NW][2];                 // its blocks
@@ -247,7 +248,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       ra[k] = p.plan_rec[(int64_t)gi * p.plan_stride + li];
       rb[k] = p.plan_rec2[(int64_t)gi * p.plan_stride + li];
     }
+    // APPEND: the slots of the step's new tokens, in the same round trip
+    constexpr int kSlotPer = APPEND ? kStreamKMaxSeqs / (64 * NW) : 1;
+    int64_t sv[kSlotPer];
+    if constexpr (APPEND) {
+#pragma unroll
+      for (int k = 0; k < kSlotPer; ++k) {
+        const int bi = tid + k * 64 * NW;
+        sv[k] = bi < B ? p.slot_mapping[bi] : -1;
+      }
+    }
     asm volatile("" ::: "memory");  // issue those loads before the header is tested
+    if constexpr (APPEND) {
+#pragma unroll
+      for (int k = 0; k < kSlotPer; ++k)
+        if (tid + k * 64 * NW < B) s_slot[tid + k * 64 * NW] = sv[k];
+    }
     s = h.x;
     e = h.y;
     T = h.z;
@@ -299,14 +315,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     typename F::Raw t;
     bf16x8 q[4];
     int lim;
-    // APPEND: the step's new K/V row of this tile's (sequence, KV head),
-    // loaded with a row's last tile; `last` (uniform) marks such a tile, `at`
-    // is the element offset of position L - 1 in the cache and `sm` the slot
-    // the caller gives the new row: the row replaces position L - 1 only when
-    // the two name the same place.
-    u32x4 nk[4], nv;
-    int64_t at, sm;
-    int last, tpos;
   };
   auto load_slot = [&](int li, Slot &sl, int dist) {
     const int lp = li - dist;
@@ -323,20 +331,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     sl.lim = ok ? s_ln[li].x : 0;
     // a masked tile reads the first rows of the cache
     const bool stream = __builtin_amdgcn_readfirstlane(s_keep[li]) == 0;
-    F::load(sl.t, kc, vc, TileRows{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10}, r, c, stream);
+    const TileRows tr{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10};
+    bool subst = false;
+    int tpos = 0;
     if constexpr (APPEND) {
+      // A row's last tile holds position L - 1; when the caller's slot for
+      // the sequence's new token names that place, the new K/V row is read
+      // in its stead.  (Block sizes of this path are powers of two.)
       const int2 ln = s_ln[li];
-      sl.last = ok && s_pj[li] == ln.y - 1;  // uniform: the position's record
-      if (sl.last) {
-        sl.tpos = (ln.x - 1) & 15;  // position L - 1 inside the tile
-        sl.at = (sl.tpos < 8 ? (int64_t)u.x << 10 : (int64_t)u.y << 10) + (sl.tpos & 7) * kD;
-        sl.sm = p.slot_mapping[b];
-        const uint16_t *nkr = reinterpret_cast<const uint16_t *>(p.new_k) + ((int64_t)b * Hkv + kh) * kD;
-        const uint16_t *nvr = reinterpret_cast<const uint16_t *>(p.new_v) + ((int64_t)b * Hkv + kh) * kD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sl.nk[i] = ld16(nkr + 32 * i + 8 * r);
-        sl.nv = ld16(nvr + 8 * c);
+      if (ok && s_pj[li] == ln.y - 1) {  // uniform: the position's record
+        tpos = (ln.x - 1) & 15;
+        const int64_t at = (tpos < 8 ? tr.lo : tr.hi) + (tpos & 7) * kD;
+        const int64_t sm = s_slot[b];
+        const int lb = __builtin_ctz((unsigned)p.block_size);
+        subst = sm >= 0 && sm < ((int64_t)p.num_blocks << lb) &&
+                ((((sm >> lb) * Hkv + kh) << lb) + (sm & (p.block_size - 1))) * kD == at;
       }
+    }
+    if constexpr (APPEND) {
+      if (subst)
+        load_kv_tile_rows_subst(sl.t, kc, vc, tr, r, c, stream, tpos,
+                                reinterpret_cast<const uint16_t *>(p.new_k) + ((int64_t)b * Hkv + kh) * kD,
+                                reinterpret_cast<const uint16_t *>(p.new_v) + ((int64_t)b * Hkv + kh) * kD);
+      else
+        F::load(sl.t, kc, vc, tr, r, c, stream);
+    } else {
+      (void)subst;
+      (void)tpos;
+      F::load(sl.t, kc, vc, tr, r, c, stream);
     }
     const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
     if (__builtin_amdgcn_readfirstlane((int)need_q))
@@ -407,28 +429,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       auto one = [&](int li, auto kc) __attribute__((always_inline)) -> bool {
         constexpr int k = decltype(kc)::value;
         load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS);
-        if constexpr (APPEND) {
-          if (s[k].last) {
-            // the new row replaces position L - 1 (lane (r, c) holds K of
-            // token c and V of tokens 4r .. 4r+3) when the slot names it
-            // (block sizes of this path are powers of two)
-            const int64_t sm = s[k].sm;
-            const int lb = __builtin_ctz((unsigned)p.block_size);
-            const bool hit = sm >= 0 && sm < ((int64_t)p.num_blocks << lb) &&
-                             ((((sm >> lb) * Hkv + s_prow[li] % Hkv) << lb) + (sm & (p.block_size - 1))) * kD ==
-                                 s[k].at;
-            if (hit) {
-              const int tp = s[k].tpos;
-              if (c == tp) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[k].t.k[i] = s[k].nk[i];
-              }
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (4 * r + v == tp) s[k].t.v[v] = s[k].nv;
-            }
-          }
-        }
         st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
         return after_step(li);
       };
