@@ -103,7 +103,7 @@ def parse():
                     choices=["llama8b_decode", "tiny_decode", "llama8b_decode_f32", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
                              "chunked_prefill_fp8", "shared_prefix", "shared_prefix_cow",
                              "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
-                             "copy_calibration"])
+                             "copy_calibration", "llama8b_decode_timeline", "llama70b_long_timeline"])
     ap.add_argument("--layers", type=int, default=0, help="layer pools to rotate (0 = workload default)")
     ap.add_argument("--block-size", type=int, default=16,
                     help="cache block size of the decode and prefill workloads (the headline runs use 16)")
@@ -462,6 +462,129 @@ def bench_decode(args, torch, pa, W, w, layers, partition, fp8=False):
                                  "kernels)" if fold else "kv_cache_write, then the decode"),
     }
     return res
+
+
+def bench_decode_timeline(args, torch, pa, W, w, layers):
+    """Phases of one folded decode call (plan once per step, then paged_attn_decode_append per layer) from
+    the timestamp build: each workgroup of the main and merge kernels records the s_memrealtime clock
+    (100 MHz) at fixed points (include/paged_attn.h, pa_timeline).  The step is captured as a HIP graph
+    and replayed; after each replay the stamps hold the step's last call, which ran right after the one
+    before it.  Each XCD has its own clock, so stamps are only compared within an XCD; workgroup id i is
+    taken to run on XCD i mod 8 (the dispatch's round robin), which the start spread on each XCD checks."""
+    dev = "cuda"
+    B, Hq, Hkv, D = w.layout.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    lens = w.layout.seq_lens
+    max_len = int(lens.max())
+    tlib = pa.load_timeline_library()
+    with pa.using_library(tlib):
+        K = [W.device_values(w.cache_shape(), w.std, w.seed * 1000 + 2 * l, w.dtype) for l in range(layers)]
+        V = [W.device_values(w.cache_shape(), w.std, w.seed * 1000 + 2 * l + 1, w.dtype) for l in range(layers)]
+        q = W.device_values((B, Hq, D), w.std, w.seed * 1000 - 1, w.dtype)
+        newk = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 2, w.dtype)
+        newv = W.device_values((B, Hkv, D), w.std, w.seed * 1000 - 3, w.dtype)
+        slots = torch.from_numpy(np.array([w.layout.block_tables[b, (lens[b] - 1) // w.block_size] * w.block_size
+                                           + (lens[b] - 1) % w.block_size for b in range(B)], np.int64)).to(dev)
+        bt = torch.from_numpy(w.layout.block_tables).to(dev)
+        sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        out = torch.empty(B, Hq, D, device=dev, dtype=torch.float32)
+        ws = torch.empty(max(pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, w.block_size, max_len, 0), 1),
+                         dtype=torch.uint8, device=dev)
+        psize = pa.paged_attn_decode_plan_size(B, Hq, Hkv, D, w.block_size, w.layout.block_tables.shape[1],
+                                               max_len, 0, pa.PA_BF16)
+        plan = torch.empty(max(psize, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            pa.paged_attn_decode_plan(plan, K[0], bt, sl, Hq, max_len, 0)
+            for l in range(layers):
+                pa.paged_attn_decode_append(out, q, newk, newv, slots, K[l], V[l], plan, bt, sl, w.scale,
+                                            max_len, 0, ws)
+
+        for _ in range(max(args.warmup, 1)):
+            step()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        pa.timeline(tlib, pa.PA_TIMELINE_ROWS, clear=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / args.steps
+        reps = []
+        for _ in range(args.steps):
+            g.replay()
+            reps.append(pa.timeline(tlib, pa.PA_TIMELINE_ROWS, clear=True))
+
+    def pct(a, q):
+        return float(np.percentile(a, q)) if len(a) else None
+
+    per = []
+    for main, merge in reps:
+        m = main.astype(np.int64)
+        g_ = merge.astype(np.int64)
+        ids = np.nonzero(m[:, 0] > 0)[0]
+        mids = np.nonzero(g_[:, 0] > 0)[0]
+        mm = m[ids] / 100.0  # us
+        waves = mm[:, 2:6]
+        r = {"workgroups": int(len(ids)), "merge_workgroups": int(len(mids)),
+             "prologue": mm[:, 1] - mm[:, 0], "stream": (waves - mm[:, 1:2]).ravel(),
+             "wave_spread": waves.max(1) - waves.min(1), "barrier": mm[:, 6] - waves.max(1),
+             "combine": mm[:, 7] - mm[:, 6], "workgroup": mm[:, 7] - mm[:, 0],
+             "merge": (g_[mids, 1] - g_[mids, 0]) / 100.0}
+        xs = {k: [] for k in ("start_spread", "main_span", "tail", "boundary", "merge_span", "call")}
+        for x in range(8):
+            ix = ids[ids % 8 == x]
+            gx = mids[mids % 8 == x]
+            if not len(ix) or not len(gx):
+                continue
+            st, en = m[ix, 0] / 100.0, m[ix, 7] / 100.0
+            ms_, me_ = g_[gx, 0] / 100.0, g_[gx, 1] / 100.0
+            xs["start_spread"].append(st.max() - st.min())
+            xs["main_span"].append(en.max() - st.min())
+            xs["tail"].append(en.max() - np.median(en))
+            xs["boundary"].append(ms_.min() - en.max())
+            xs["merge_span"].append(me_.max() - ms_.min())
+            xs["call"].append(me_.max() - st.min())
+        r.update({k: np.array(v) for k, v in xs.items()})
+        per.append(r)
+
+    def summary(key, qs=(5, 50, 95)):
+        # per call: the percentiles over its workgroups (or XCDs); then the median over calls
+        vals = [[pct(r[key], q_) for q_ in qs] for r in per if len(r[key])]
+        return [round(float(np.median([v[i] for v in vals])), 2) for i in range(len(qs))] if vals else None
+
+    phases = {
+        "main_start_spread_per_xcd_us_p5_p50_p95": summary("start_spread"),
+        "prologue_us_p5_p50_p95": summary("prologue"),
+        "stream_per_wave_us_p5_p50_p95": summary("stream"),
+        "wave_end_spread_in_workgroup_us_p5_p50_p95": summary("wave_spread"),
+        "barrier_after_last_wave_us_p5_p50_p95": summary("barrier"),
+        "combine_us_p5_p50_p95": summary("combine"),
+        "workgroup_start_to_end_us_p5_p50_p95": summary("workgroup"),
+        "main_kernel_span_per_xcd_us_p5_p50_p95": summary("main_span"),
+        "main_tail_after_median_workgroup_end_per_xcd_us_p5_p50_p95": summary("tail"),
+        "boundary_main_end_to_merge_start_per_xcd_us_p5_p50_p95": summary("boundary"),
+        "merge_workgroup_us_p5_p50_p95": summary("merge"),
+        "merge_span_per_xcd_us_p5_p50_p95": summary("merge_span"),
+        "call_span_per_xcd_us_p5_p50_p95": summary("call"),
+    }
+    call = phases["call_span_per_xcd_us_p5_p50_p95"]
+    spread = phases["main_start_spread_per_xcd_us_p5_p50_p95"]
+    return {
+        "metric": "phases of one paged_attn_decode_append call (timestamp build, per-workgroup clocks)",
+        "value": call[1] if call else None, "unit": "us (median over XCDs of main start to merge end)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + "_timeline", "batch": B, "num_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": w.block_size, "layers": layers, "total_tokens": int(lens.sum())},
+        "workgroups": per[0]["workgroups"] if per else 0, "merge_workgroups": per[0]["merge_workgroups"] if per else 0,
+        "calls_sampled": len(per), "phases": phases,
+        "xcd_round_robin_consistent": bool(spread is not None and spread[2] < 5.0),
+        "graph_us_per_call_timestamp_build": round(ms_step * 1e3 / layers, 2),
+    }
 
 
 def host_copy(torch, t):
@@ -976,6 +1099,10 @@ def main():
         res = bench_swap(args, torch, pa, W)
     elif args.workload == "copy_calibration":
         res = bench_copy(args, torch)
+    elif args.workload in ("llama8b_decode_timeline", "llama70b_long_timeline"):
+        w = W.llama8b_decode() if args.workload.startswith("llama8b") else W.llama70b_long()
+        res = bench_decode_timeline(args, torch, pa, W, w, args.layers or (32 if args.workload.startswith("llama8b")
+                                                                            else 4))
     else:
         raise SystemExit("workload %s: not wired into the bench yet" % args.workload)
     print(json.dumps(res), flush=True)

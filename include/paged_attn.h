@@ -121,6 +121,28 @@ PA_EXPORT int pa_abi_version(void);
 PA_EXPORT int pa_debug_flags(unsigned *flags, int clear);
 
 /*
+ * pa_timeline -- per-workgroup timestamps of the balanced decode's planned
+ * kernels (host; the timestamp build libpagedattn_timeline.so only), for
+ * breaking one call's time into its phases.  Each workgroup of the main
+ * kernel records, by its hardware workgroup id, the s_memrealtime clock
+ * (100 MHz; every XCD has its own, offset from the others, so only stamps
+ * taken on one XCD compare) at 8 points:
+ *   [0] start, [1] its range's plan records staged, [2..5] the stream end
+ *   of waves 0..3, [6] the combine's start (after the barrier), [7] the end;
+ * each merge-kernel workgroup records [0] start and [1] end.  A point a
+ * workgroup does not reach stays 0.  Later calls overwrite earlier stamps.
+ *
+ *   main_stamps   host [rows][8] uint64 (written)
+ *   merge_stamps  host [rows][2] uint64 (written)
+ *   rows          workgroup ids 0 .. rows - 1 to copy, 1 <= rows <= PA_TIMELINE_ROWS
+ * Waits for the current device to finish (hipDeviceSynchronize), copies the
+ * stamps and sets them all to zero if `clear` is nonzero.  The release
+ * build returns PA_ERR_UNSUPPORTED.
+ */
+#define PA_TIMELINE_ROWS 4096
+PA_EXPORT int pa_timeline(uint64_t *main_stamps, uint64_t *merge_stamps, int32_t rows, int32_t clear);
+
+/*
  * kv_cache_write -- scatter new K/V rows into their cache slots
  * ([L7] §4.3 first fused kernel; [L7] §4.1 and [L16] §3.3: a token lands in
  * the next free slot of its sequence's last block).

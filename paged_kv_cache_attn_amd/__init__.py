@@ -22,7 +22,7 @@ __all__ = [
     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8", "PA_FP8_E4M3",
     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
     "paged_attn_decode_noalloc", "PA_NOALLOC_SCRATCH_BYTES", "paged_attn_decode_append", "EXPORTED_SYMBOLS",
-    "load_debug_library", "debug_flags", "DEBUG_BITS",
+    "load_debug_library", "debug_flags", "DEBUG_BITS", "load_timeline_library", "timeline", "using_library",
 ]
 
 PA_F32 = 0
@@ -32,13 +32,15 @@ PA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's built-in decode scr
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 debug_library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn_debug.so")
+timeline_library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn_timeline.so")
+PA_TIMELINE_ROWS = 4096  # workgroup ids with timestamps (include/paged_attn.h)
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_abi_version", "kv_cache_write",
                     "paged_attn_decode_workspace_size", "paged_attn_decode",
                     "paged_attn_prefill_chunk", "block_copy", "kv_swap_out", "kv_swap_in",
                     "kv_cache_write_fp8", "paged_attn_decode_fp8", "paged_attn_prefill_chunk_fp8",
                     "paged_attn_decode_plan_size", "paged_attn_decode_plan", "paged_attn_decode_planned",
-                    "paged_attn_decode_noalloc", "paged_attn_decode_append", "pa_debug_flags")
+                    "paged_attn_decode_noalloc", "paged_attn_decode_append", "pa_debug_flags", "pa_timeline")
 
 
 class PagedAttnError(RuntimeError):
@@ -60,6 +62,8 @@ def _load(path=None):
     L.pa_abi_version.restype = ctypes.c_int
     L.pa_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int]
     L.pa_debug_flags.restype = ctypes.c_int
+    L.pa_timeline.argtypes = [vp, vp, i32, i32]
+    L.pa_timeline.restype = ctypes.c_int
     L.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [vp]
     L.kv_cache_write.restype = ctypes.c_int
     L.paged_attn_decode_workspace_size.argtypes = [i32] * 7
@@ -472,6 +476,41 @@ def load_debug_library():
     """The debug build (libpagedattn_debug.so) as a ctypes library with the same signatures, for calling
     directly; its kernels also record what their bounds checks mask (read with debug_flags)."""
     return _load(debug_library_path)
+
+
+def load_timeline_library():
+    """The timestamp build (libpagedattn_timeline.so) as a ctypes library with the same signatures; its
+    balanced-decode kernels record per-workgroup timestamps (read with timeline)."""
+    return _load(timeline_library_path)
+
+
+class using_library:
+    """Route the call wrappers of this module through another build of the library (the debug or the
+    timestamp build) inside a `with` block."""
+
+    def __init__(self, lib):
+        self.lib, self.saved = lib, None
+
+    def __enter__(self):
+        global _lib
+        self.saved, _lib = _lib, self.lib
+        return self.lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def timeline(lib, rows: int, clear: bool = True):
+    """pa_timeline of `lib` (waits for the device): the stamps of workgroup ids 0 .. rows - 1 as numpy uint64
+    arrays, main kernel [rows, 8] and merge kernel [rows, 2] (points in include/paged_attn.h)."""
+    import numpy as np
+    main = np.zeros((rows, 8), np.uint64)
+    merge = np.zeros((rows, 2), np.uint64)
+    _check("pa_timeline", lib.pa_timeline(main.ctypes.data_as(ctypes.c_void_p),
+                                          merge.ctypes.data_as(ctypes.c_void_p), int(rows), int(bool(clear))))
+    return main, merge
 
 
 def debug_flags(lib, clear: bool = True) -> int:

@@ -1,12 +1,15 @@
 """Build libpagedattn.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m paged_kv_cache_attn_amd.build [--debug | --all]
+    python -m paged_kv_cache_attn_amd.build [--debug | --timeline | --all]
 
 Each .hip source is compiled to an object under _build/ (in parallel), then
 linked into paged_kv_cache_attn_amd/libpagedattn.so.  The debug build
 (PAGED_ATTN_DEBUG=1: the kernels also report what their bounds checks mask,
 read with pa_debug_flags) goes to libpagedattn_debug.so, its objects under
-_build/debug/.  Always rebuilds.
+_build/debug/.  The timestamp build (PAGED_ATTN_TIMELINE=1: the balanced
+decode's planned kernels record per-workgroup timestamps, read with
+pa_timeline) goes to libpagedattn_timeline.so, its objects under
+_build/timeline/.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -23,6 +26,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 DEBUG_LIB = os.path.join(PKG, "libpagedattn_debug.so")
+TIMELINE_LIB = os.path.join(PKG, "libpagedattn_timeline.so")
+VARIANTS = {"release": ("", [], LIB), "debug": ("debug", ["-DPAGED_ATTN_DEBUG=1"], DEBUG_LIB),
+            "timeline": ("timeline", ["-DPAGED_ATTN_TIMELINE=1"], TIMELINE_LIB)}
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -42,9 +48,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, debug: bool = False) -> str:
-    obj = os.path.join(BUILD, "debug" if debug else "", os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + (["-DPAGED_ATTN_DEBUG=1"] if debug else []) + ["-c", src, "-o", obj]
+def _compile(src: str, variant: str = "release") -> str:
+    sub, defs, _ = VARIANTS[variant]
+    obj = os.path.join(BUILD, sub, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC] + CFLAGS + defs + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -55,13 +62,15 @@ def _compile(src: str, debug: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = True, debug: bool = False) -> str:
-    """Compile and link the release library (or, with debug=True, the debug one); returns its path."""
-    lib = DEBUG_LIB if debug else LIB
-    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+def build(verbose: bool = True, debug: bool = False, timeline: bool = False) -> str:
+    """Compile and link the release library (or, with debug=True, the debug one; with timeline=True, the
+    timestamp one); returns its path."""
+    variant = "debug" if debug else "timeline" if timeline else "release"
+    sub, _, lib = VARIANTS[variant]
+    os.makedirs(os.path.join(BUILD, sub), exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, debug), srcs))
+        objs = list(ex.map(lambda src: _compile(src, variant), srcs))
     tmp = lib + ".tmp%d" % os.getpid()
     # -z defs: a symbol the objects leave undefined (a kernel stub the host
     # pass did not emit, say) fails the link instead of the first dlopen
@@ -76,8 +85,10 @@ def build(verbose: bool = True, debug: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    if "--all" in sys.argv[1:]:
+    args = sys.argv[1:]
+    if "--all" in args:
         build()
         build(debug=True)
+        build(timeline=True)
     else:
-        build(debug="--debug" in sys.argv[1:])
+        build(debug="--debug" in args, timeline="--timeline" in args)

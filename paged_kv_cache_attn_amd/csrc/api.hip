@@ -179,6 +179,32 @@ int pa_debug_flags(unsigned *flags, int clear) {
 #endif
 }
 
+int pa_timeline(uint64_t *main_stamps, uint64_t *merge_stamps, int32_t rows, int32_t clear) {
+#if PAGED_ATTN_TIMELINE
+  if (!main_stamps || !merge_stamps) return PA_ERR_NULL;
+  if (rows < 1 || rows > PA_TIMELINE_ROWS) return PA_ERR_SHAPE;
+  if (hipDeviceSynchronize() != hipSuccess) return PA_ERR_LAUNCH;
+  void *m = nullptr, *g = nullptr;
+  if (pa::timeline_symbols(&m, &g) != hipSuccess) return PA_ERR_LAUNCH;
+  if (hipMemcpy(main_stamps, m, (size_t)rows * 8 * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(merge_stamps, g, (size_t)rows * 2 * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  if (clear) {
+    if (hipMemset(m, 0, (size_t)PA_TIMELINE_ROWS * 8 * sizeof(uint64_t)) != hipSuccess ||
+        hipMemset(g, 0, (size_t)PA_TIMELINE_ROWS * 2 * sizeof(uint64_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+      return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+#else
+  (void)main_stamps;
+  (void)merge_stamps;
+  (void)rows;
+  (void)clear;
+  return PA_ERR_UNSUPPORTED;
+#endif
+}
+
 int kv_cache_write(const void *key, const void *value, void *k_cache, void *v_cache,
                    const int64_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,

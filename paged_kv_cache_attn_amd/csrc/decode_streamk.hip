@@ -80,6 +80,33 @@ __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, 
 // layer of a decode step.
 enum : int { kFused = 0, kPlanOnly = 1, kPlanned = 2 };
 
+// Timestamp build (PAGED_ATTN_TIMELINE=1): the planned main kernel and the
+// merge kernel record the s_memrealtime clock at fixed points of every
+// workgroup, by hardware workgroup id, for pa_timeline (points listed in
+// include/paged_attn.h).  The release build compiles none of it.
+#if PAGED_ATTN_TIMELINE
+#include "paged_attn.h"  // PA_TIMELINE_ROWS
+static __device__ unsigned long long tl_main[PA_TIMELINE_ROWS][8];
+static __device__ unsigned long long tl_merge[PA_TIMELINE_ROWS][2];
+#define TL_MAIN(col, who)                                                          \
+  do {                                                                             \
+    if ((who) && blockIdx.x < PA_TIMELINE_ROWS)                                    \
+      tl_main[blockIdx.x][(col)] = __builtin_amdgcn_s_memrealtime();               \
+  } while (0)
+#define TL_MERGE(col)                                                              \
+  do {                                                                             \
+    if (threadIdx.x == 0 && blockIdx.x < PA_TIMELINE_ROWS)                         \
+      tl_merge[blockIdx.x][(col)] = __builtin_amdgcn_s_memrealtime();              \
+  } while (0)
+#else
+#define TL_MAIN(col, who) \
+  do {                    \
+  } while (0)
+#define TL_MERGE(col) \
+  do {                \
+  } while (0)
+#endif
+
 template <int NW, bool FP8, int MODE, bool APPEND = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_streamk_kernel(
     DecodeParams p) {
@@ -108,6 +135,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int g = p.num_heads / Hkv;
   const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);  // this workgroup's range
   const int R = p.sk_range_blocks;
+  if constexpr (MODE == kPlanned) TL_MAIN(0, tid == 0);
 
   int T, G, s, e;
   if constexpr (MODE != kPlanned) {
@@ -292,6 +320,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     if (tid == 0) s_prow[e - s] = -1;
     __syncthreads();
+    TL_MAIN(1, tid == 0);
   }
 
   // this wave's share of the range, in local positions [ls, le)
@@ -450,7 +479,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
   }
+  if constexpr (MODE == kPlanned) TL_MAIN(2 + (w & 3), lane == 0);
   __syncthreads();
+  if constexpr (MODE == kPlanned) TL_MAIN(6, tid == 0);
 
   // -- combine the parked boundary rows, in wave order -----------------------
   // The 2 * NW entries (w, k), in order, form runs of equal row start, one
@@ -537,6 +568,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
   }
+  if constexpr (MODE == kPlanned) TL_MAIN(7, tid == 0);
 }
 
 // One workgroup per range gi: if the range holds the last piece of a row
@@ -552,6 +584,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // kv_cache_write does: slot < 0 or past the cache skips the row.
 template <bool APPEND>
 __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams p) {
+  TL_MERGE(0);
   constexpr int kBatch = 8;
   constexpr int kPer = 2;  // the launch uses g * kD / 2 threads: two elements each
   // the same range numbering as the main kernel, so this workgroup runs on
@@ -620,7 +653,10 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   // values, not for their bounds (a stale or foreign plan gives wrong
   // results, never an access out of bounds)
   const int row = dsc.x;
-  if (row < 0 || row >= nrows) return;
+  if (row < 0 || row >= nrows) {
+    TL_MERGE(1);
+    return;
+  }
   const int g_first = min(max(dsc.y, 0), gi), s_first = dsc.z & 1, nc = gi - g_first + 1;
   const int b = row / p.num_kv_heads, kh = row - b * p.num_kv_heads;
   const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
@@ -638,6 +674,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
       const float o = so[f][u] * w0 + so[2][u] * w1;
       store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, ls > 0.f ? o * p.v_scale / ls : 0.f);
     }
+    TL_MERGE(1);
     return;
   }
   auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
@@ -673,12 +710,21 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
     }
     store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
   }
+  TL_MERGE(1);
 }
 
 }  // namespace
 
 #if PAGED_ATTN_DEBUG
 PA_DEBUG_WORD_ACCESSOR(debug_word_streamk)
+#endif
+
+#if PAGED_ATTN_TIMELINE
+hipError_t timeline_symbols(void **main_stamps, void **merge_stamps) {
+  const hipError_t e = hipGetSymbolAddress(main_stamps, HIP_SYMBOL(tl_main));
+  if (e != hipSuccess) return e;
+  return hipGetSymbolAddress(merge_stamps, HIP_SYMBOL(tl_merge));
+}
 #endif
 
 hipError_t launch_decode_streamk_plan(const DecodeParams &p, hipStream_t stream) {

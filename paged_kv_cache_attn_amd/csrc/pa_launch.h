@@ -131,4 +131,14 @@ hipError_t debug_word_streamk(void **p);
 hipError_t debug_word_prefill(void **p);
 #endif
 
+#ifndef PAGED_ATTN_TIMELINE
+#define PAGED_ATTN_TIMELINE 0
+#endif
+#if PAGED_ATTN_TIMELINE
+// Device addresses of the balanced decode's timestamp arrays (timestamp build
+// only): [PA_TIMELINE_ROWS][8] for the main kernel, [PA_TIMELINE_ROWS][2] for
+// the merge kernel, uint64 each.
+hipError_t timeline_symbols(void **main_stamps, void **merge_stamps);
+#endif
+
 }  // namespace pa

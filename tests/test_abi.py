@@ -12,6 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_attn.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn.so")
 DEBUG_LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn_debug.so")
+TIMELINE_LIB = os.path.join(ROOT, "paged_kv_cache_attn_amd", "libpagedattn_timeline.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 PA_ERR_SCRATCH = -6
@@ -48,11 +49,13 @@ def test_library_exports_every_declared_symbol(pa):
     assert set(pa.EXPORTED_SYMBOLS) == set(declared_functions())
 
 
-def test_debug_library_exports_every_declared_symbol(pa):
-    if not os.path.exists(DEBUG_LIB):
+@pytest.mark.parametrize("variant", ["debug", "timeline"])
+def test_variant_library_exports_every_declared_symbol(pa, variant):
+    path = DEBUG_LIB if variant == "debug" else TIMELINE_LIB
+    if not os.path.exists(path):
         from paged_kv_cache_attn_amd import build as b
-        b.build(debug=True)
-    out = subprocess.run(["nm", "-D", "--defined-only", DEBUG_LIB], capture_output=True, text=True,
+        b.build(debug=variant == "debug", timeline=variant == "timeline")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in declared_functions():
@@ -70,6 +73,20 @@ def test_debug_flags_release_and_debug(pa):
     for name, bit in pa.DEBUG_BITS.items():
         m = re.search(r"#define PA_DEBUG_%s \(1u << (\d+)\)" % name.upper(), text)
         assert m and (1 << int(m.group(1))) == bit, name
+
+
+def test_timeline_release_and_timestamp_build(pa):
+    """The release build records no timestamps and says so; the timestamp build refuses NULL destinations
+    and a row count outside 1 .. PA_TIMELINE_ROWS before it touches the GPU."""
+    m = (ctypes.c_uint64 * 16)()
+    g = (ctypes.c_uint64 * 4)()
+    assert pa.lib.pa_timeline(m, g, 2, 0) == PA_ERR_UNSUPPORTED
+    tlib = pa.load_timeline_library()
+    assert tlib.pa_timeline(None, g, 2, 0) == PA_ERR_NULL
+    assert tlib.pa_timeline(m, None, 2, 0) == PA_ERR_NULL
+    assert tlib.pa_timeline(m, g, 0, 0) == PA_ERR_SHAPE
+    assert tlib.pa_timeline(m, g, pa.PA_TIMELINE_ROWS + 1, 0) == PA_ERR_SHAPE
+    assert re.search(r"#define PA_TIMELINE_ROWS %d\b" % pa.PA_TIMELINE_ROWS, open(HEADER).read())
 
 
 def test_abi_version_and_status_strings(pa):
