@@ -74,16 +74,25 @@ struct TileMap {
   // this stays one basic block.
   // Table index of the (first) entry that tile j lives in.
   __device__ __forceinline__ int first_index(int j) const { return sh < 0 ? 2 * j : j >> (sh & 31); }
-  template <typename TablePtr>
-  __device__ __forceinline__ bool entries(TablePtr table, int j, int nblk_tab, int &e0, int &e1) const {
+  // the table indices of tile j's entries
+  __device__ __forceinline__ void indices(int j, int nblk_tab, int &i0, int &i1) const {
     const bool halves = sh < 0;
-    const int i0 = halves ? 2 * j : j >> (sh & 31);
-    const int i1 = halves && 2 * j + 1 < nblk_tab ? 2 * j + 1 : i0;
-    const int t0 = table[i0], t1 = table[i1];
+    i0 = halves ? 2 * j : j >> (sh & 31);
+    i1 = halves && 2 * j + 1 < nblk_tab ? 2 * j + 1 : i0;
+  }
+  // tile j's entries from the table values t0, t1 read at those indices
+  __device__ __forceinline__ bool entries_from(int t0, int t1, int j, int &e0, int &e1) const {
+    const bool halves = sh < 0;
     const bool ok = (unsigned)t0 < (unsigned)num_blocks && (!halves || (unsigned)t1 < (unsigned)num_blocks);
     e0 = ok ? t0 : 0;
     e1 = halves ? (ok ? t1 : 0) : j & ((1 << (sh & 31)) - 1);
     return ok;
+  }
+  template <typename TablePtr>
+  __device__ __forceinline__ bool entries(TablePtr table, int j, int nblk_tab, int &e0, int &e1) const {
+    int i0, i1;
+    indices(j, nblk_tab, i0, i1);
+    return entries_from(table[i0], table[i1], j, e0, e1);
   }
   // the rows of the tile with entries e0, e1 in KV head kh (32-bit selects
   // only, then one multiply-add per row, so nothing here becomes a branch)

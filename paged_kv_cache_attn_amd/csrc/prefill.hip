@@ -163,12 +163,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // read from block 0 and masked later.  Which tile, K or V, and which half
   // of the tile (rows 0-7 or 8-15) a thread loads is the same for its whole
   // wave, so the two row bases are selected in scalar registers.
-  auto gload = [&](int pr, u32x4 *regs) -> int {
+  // The table values a pair's tiles live in (read through the scalar cache),
+  // apart from the loads they address, so a loop can read them one pair early.
+  auto pair_table = [&](int pr) __attribute__((always_inline)) -> int4 {
+    pr = min(pr, max(npair - 1, 0));
+    int ia0, ia1, ib0, ib1;
+    map.indices(2 * pr, nblk_tab, ia0, ia1);
+    map.indices(max(0, min(2 * pr + 1, nblk - 1)), nblk_tab, ib0, ib1);
+    return int4{table[ia0], table[ia1], table[ib0], table[ib1]};
+  };
+  auto gload_from = [&](int pr, u32x4 *regs, int4 tv) __attribute__((always_inline)) -> int {
     pr = min(pr, max(npair - 1, 0));
     const int ja = 2 * pr, jb = 2 * pr + 1;
     int a0, a1, b0, b1;
-    const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
-    const bool entb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1);
+    const bool oka = map.entries_from(tv.x, tv.y, ja, a0, a1);
+    const bool entb = map.entries_from(tv.z, tv.w, max(0, min(jb, nblk - 1)), b0, b1);
     const bool okb = entb && jb < nblk;
     const int bad = !oka || (jb < nblk && !entb);  // an entry out of range (bit 2 of the result)
     const TileRows ra = map.rows(a0, a1, kh);
@@ -184,6 +193,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     return (int)oka | ((int)okb << 1) | (bad << 2);
   };
+  auto gload = [&](int pr, u32x4 *regs) -> int { return gload_from(pr, regs, pair_table(pr)); };
   // Direct pair load (bf16): the k-th load of wave w fills the 64 consecutive
   // 16-byte slots of the stage from slot (k * NW + w) * 64 on, one per lane
   // (64 slots = 4 rows of one tile), so each lane fetches the global chunk
@@ -198,12 +208,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int trow = 4 * w + (lane >> 4), tcol = lane & 15;
   const uint32_t off_k = (uint32_t)(trow * D + (tcol ^ trow) * 8) * 2u;
   const uint32_t off_v = (uint32_t)(trow * D + ((((tcol >> 1) ^ (trow & 7)) << 1) | (tcol & 1)) * 8) * 2u;
-  auto dma = [&](int pr, auto st) __attribute__((always_inline)) -> int {
+  auto dma_from = [&](int pr, auto st, int4 tv) __attribute__((always_inline)) -> int {
     pr = min(pr, max(npair - 1, 0));
     const int ja = 2 * pr, jb = 2 * pr + 1;
     int a0, a1, b0, b1;
-    const bool oka = map.entries(table, ja, nblk_tab, a0, a1);
-    const bool entb = map.entries(table, max(0, min(jb, nblk - 1)), nblk_tab, b0, b1);
+    const bool oka = map.entries_from(tv.x, tv.y, ja, a0, a1);
+    const bool entb = map.entries_from(tv.z, tv.w, max(0, min(jb, nblk - 1)), b0, b1);
     const bool okb = entb && jb < nblk;
     const int bad = !oka || (jb < nblk && !entb);  // an entry out of range (bit 2 of the result)
     const TileRows ra = map.rows(a0, a1, kh);
@@ -234,6 +244,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     return (int)oka | ((int)okb << 1) | (bad << 2);
   };
+  auto dma = [&](int pr, auto st) __attribute__((always_inline)) -> int { return dma_from(pr, st, pair_table(pr)); };
   // LDS byte offset of bf16 chunk kc (0..15) of row t in a K or a V tile
   auto lds_off = [](bool is_v, int t, int kc) -> int {
     return is_v ? t * 256 + ((((kc >> 1) ^ (t & 7)) << 5) | ((kc & 1) << 4)) : (t * 16 + (kc ^ t)) << 4;
@@ -335,6 +346,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     ok[0] = dma(0, S0());
     if (npair > 1) ok[1] = dma(1, S1());
     if (npair > 2) ok[2] = dma(2, S2());
+    // the table values of the pair the next iteration loads, read one
+    // iteration early so that no scalar-cache round trip sits between the
+    // barrier and the loads
+    int4 tv_next = pair_table(3);
     float x0[8], x1[8];  // scores of the pair the next iteration finishes
     if (npair > 2)
       vm_wait<2 * kChunksPerThread>();
@@ -353,7 +368,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       else
         vm_wait<0>();
       workgroup_barrier();
-      if (X + 3 < npair) ok[decltype(ld)::value] = dma(X + 3, ld);
+      if (X + 3 < npair) ok[decltype(ld)::value] = dma_from(X + 3, ld, tv_next);
+      tv_next = pair_table(X + 4);
       bf16x8 vt[8];
       u32x4 ka[4], kb[4];
       lread_v(cur, vt);
@@ -452,12 +468,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     ok_s[0] = ok_r[0];
     ok_r[1] = gload(1, rs[1]);
     ok_r[2] = gload(2, rs[2]);
+    int4 tv_next = pair_table(3);  // read one pair early, as in the loop above
     auto iter = [&](int X, auto phase) -> bool {
       constexpr int j = decltype(phase)::value, j1 = (j + 1) % 3;
       __syncthreads();
       if (X + 1 < npair) lstore(std::integral_constant<int, j1>(), rs[j1]);
       ok_s[j1] = ok_r[j1];
-      ok_r[j] = gload(X + 3, rs[j]);
+      ok_r[j] = gload_from(X + 3, rs[j], tv_next);
+      tv_next = pair_table(X + 4);
       seen |= ok_s[j];
       compute(phase, X, ok_s[j], st);
       return X + 1 < npair;
