@@ -520,50 +520,75 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = h; i < NE; ++i) mem |= (ers[i] == rs ? 1u : 0u) << i;
     const bool single = (mem & (mem - 1)) == 0;
-    for (int idx = tid; idx < g * kD; idx += 64 * NW) {
-      const int cc = idx / kD, d = idx - cc * kD;
-      float M, lsum, o;
+    // Two output elements per thread and pass (all of them at g <= 4), so
+    // that the members' LDS reads of both go out together.
+    constexpr int kPer = 2;
+    for (int idx0 = tid; idx0 < g * kD; idx0 += kPer * 64 * NW) {
+      float M[kPer], lsum[kPer], o[kPer];
+      int cc[kPer], d[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int idx = min(idx0 + u * 64 * NW, g * kD - 1);  // a past-the-end element repeats the last one
+        cc[u] = idx / kD;
+        d[u] = idx - cc[u] * kD;
+      }
       if (single) {
         // weight exp2(0) = 1 (an all-masked entry carries zero sum and output)
-        const float *pc = s_park + ((size_t)h * g + cc) * (kD + 2);
-        M = pc[kD];
-        lsum = pc[kD + 1];
-        o = pc[d];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const float *pc = s_park + ((size_t)h * g + cc[u]) * (kD + 2);
+          M[u] = pc[kD];
+          lsum[u] = pc[kD + 1];
+          o[u] = pc[d[u]];
+        }
       } else {
-        float mv[NE], lv[NE], ov[NE];
+        float mv[NE][kPer], lv[NE][kPer], ov[NE][kPer];
 #pragma unroll
         for (int i = h; i < NE; ++i) {
           if ((mem >> i) & 1u) {
-            const float *pc = s_park + ((size_t)i * g + cc) * (kD + 2);
-            mv[i] = pc[kD];
-            lv[i] = pc[kD + 1];
-            ov[i] = pc[d];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+              const float *pc = s_park + ((size_t)i * g + cc[u]) * (kD + 2);
+              mv[i][u] = pc[kD];
+              lv[i][u] = pc[kD + 1];
+              ov[i][u] = pc[d[u]];
+            }
           }
         }
-        M = kNegInf;
 #pragma unroll
-        for (int i = h; i < NE; ++i)
-          if ((mem >> i) & 1u) M = fmaxf(M, mv[i]);
-        const float M_use = M == kNegInf ? 0.f : M;
-        lsum = 0.f;
-        o = 0.f;
+        for (int u = 0; u < kPer; ++u) {
+          float Mx = kNegInf;
 #pragma unroll
-        for (int i = h; i < NE; ++i) {
-          if ((mem >> i) & 1u) {
-            const float wgt = fast_exp2(mv[i] - M_use);
-            lsum += lv[i] * wgt;
-            o += ov[i] * wgt;
+          for (int i = h; i < NE; ++i)
+            if ((mem >> i) & 1u) Mx = fmaxf(Mx, mv[i][u]);
+          const float M_use = Mx == kNegInf ? 0.f : Mx;
+          float ls = 0.f, ov_ = 0.f;
+#pragma unroll
+          for (int i = h; i < NE; ++i) {
+            if ((mem >> i) & 1u) {
+              const float wgt = fast_exp2(mv[i][u] - M_use);
+              ls += lv[i][u] * wgt;
+              ov_ += ov[i][u] * wgt;
+            }
           }
+          M[u] = Mx;
+          lsum[u] = ls;
+          o[u] = ov_;
         }
       }
-      if (whole) {
-        store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lsum > 0.f ? o * p.v_scale / lsum : 0.f);
-      } else {
-        const int64_t base = ((int64_t)gi * 2 + slot) * g + cc;
-        p.sk_part[base * kD + d] = o;
-        if (d == 0) {
-          p.sk_ml[base * 2 + 0] = M;
-          p.sk_ml[base * 2 + 1] = lsum;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        if (idx0 + u * 64 * NW >= g * kD) continue;
+        if (whole) {
+          store_value(p.out, p.out_bf16, (out_row0 + cc[u]) * kD + d[u],
+                      lsum[u] > 0.f ? o[u] * p.v_scale / lsum[u] : 0.f);
+        } else {
+          const int64_t base = ((int64_t)gi * 2 + slot) * g + cc[u];
+          p.sk_part[base * kD + d[u]] = o[u];
+          if (d[u] == 0) {
+            p.sk_ml[base * 2 + 0] = M[u];
+            p.sk_ml[base * 2 + 1] = lsum[u];
+          }
         }
       }
     }
