@@ -65,7 +65,13 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // written during the call), so the K/V loads are the only vector-memory
 // operations of the loop and a wait for one pair never waits on table reads.
 //
-// Within a head the query tiles go heaviest (last in the chunk) first; a
+// Dispatch order: each XCD takes a contiguous run of (sequence, KV head)
+// groups; within the run, sets of kset groups go one after another, and a
+// set's tiles go heaviest first (the last query tile of the chunk, which
+// reads the most keys) across all of its groups, then the next heaviest.
+// With kset * ntiles about one XCD's workgroup slots, a set fills the XCD,
+// the long tiles start first and the short ones fill in behind them (longest
+// processing time first), while the set's K/V still fits that XCD's L2.  A
 // column group past its causal bound is fully masked (every wave joins every
 // barrier).  grid = ntiles * Hkv * B workgroups, ntiles =
 // ceil(max_query_len / (NW * CG * 16 / g)).  The block size BSZ is a template
@@ -102,9 +108,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   const unsigned item = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int tile = ntiles - 1 - (int)(item % (unsigned)ntiles);
-  const int kh = (int)((item / (unsigned)ntiles) % (unsigned)p.num_kv_heads);
-  const int b = (int)(item / (unsigned)ntiles / (unsigned)p.num_kv_heads);
+  const unsigned nt = (unsigned)ntiles, ngrp = gridDim.x / nt;
+  constexpr unsigned kXcdSlots = 32 * 2;  // CUs per XCD x workgroups per CU
+  const unsigned kset = nt >= kXcdSlots ? 1u : kXcdSlots / nt;
+  const unsigned set = item / (kset * nt), off = item - set * kset * nt;
+  const unsigned nset = min(kset, ngrp - set * kset);  // groups in this set
+  // the quotients are uniform; readfirstlane keeps them (and the addresses
+  // built from them) in scalar registers
+  const unsigned grp = __builtin_amdgcn_readfirstlane(set * kset + off % nset);
+  const int tile = __builtin_amdgcn_readfirstlane(ntiles - 1 - (int)(off / nset));
+  const int kh = (int)(grp % (unsigned)p.num_kv_heads);
+  const int b = (int)(grp / (unsigned)p.num_kv_heads);
   const int g = p.num_heads / p.num_kv_heads;
   const int tpgrp = 16 / g;              // chunk tokens per column group
   const int tpw = CG * tpgrp;            // per wave
