@@ -192,6 +192,22 @@ __device__ __forceinline__ void load_kv_tile_rows_fp8(KVTile8 &t, const uint8_t 
   }
 }
 
+// The same loads with the load kind a template argument, for a loop that
+// fixes it for a whole share: one load sequence, no branch between two.
+template <bool STREAM>
+__device__ __forceinline__ void load_kv_tile_rows_fp8_as(KVTile8 &t, const uint8_t *kc, const uint8_t *vc,
+                                                         const TileRows &tr, int r, int c) {
+  const int64_t kr = (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128 + 16 * r;
+  const int64_t vr = r < 2 ? tr.lo : tr.hi;
+  t.k[0] = STREAM ? ld16_stream(kc + kr) : ld16(kc + kr);
+  t.k[1] = STREAM ? ld16_stream(kc + kr + 64) : ld16(kc + kr + 64);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint8_t *src = vc + vr + ((4 * r + v) & 7) * 128 + 8 * c;
+    t.v[v] = STREAM ? ld8_stream(src) : ld8(src);
+  }
+}
+
 __device__ __forceinline__ KVTile expand_fp8_tile(const KVTile8 &s) {
   KVTile t;
   t.k[0] = fp8x8_to_bf16x8(s.k[0][0], s.k[0][1]);
@@ -225,6 +241,11 @@ struct KVFormat<false> {
                                               int c, bool stream) {
     load_kv_tile_rows(t, kc, vc, tr, r, c, stream);
   }
+  template <bool STREAM>
+  static __device__ __forceinline__ void load_as(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
+                                                 int c) {
+    load_kv_tile_rows(t, kc, vc, tr, r, c, STREAM);
+  }
   static __device__ __forceinline__ KVTile expand(const Raw &t) { return t; }
   static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r);
 };
@@ -235,6 +256,11 @@ struct KVFormat<true> {
   static __device__ __forceinline__ void load(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
                                               int c, bool stream) {
     load_kv_tile_rows_fp8(t, kc, vc, tr, r, c, stream);
+  }
+  template <bool STREAM>
+  static __device__ __forceinline__ void load_as(Raw &t, const Elem *kc, const Elem *vc, const TileRows &tr, int r,
+                                                 int c) {
+    load_kv_tile_rows_fp8_as<STREAM>(t, kc, vc, tr, r, c);
   }
   static __device__ __forceinline__ KVTile expand(const Raw &t) { return expand_fp8_tile(t); }
   static __device__ __forceinline__ void load_q(bf16x8 qb[4], const uint16_t *qrow, int r) {
