@@ -35,6 +35,19 @@ int64_t effective_partition(int32_t partition_size, int32_t block_size) {
   return ceil_div(kDefaultPartitionTokens, block_size) * block_size;
 }
 
+// The vector kernels' pieces when the caller leaves the size to the library:
+// the longest power of two from 256 to 4096 tokens that still gives about
+// 1,024 workgroups with keys (four per CU, over two rounds) when every row is
+// max_seq_len long.  A long piece spreads a workgroup's fixed cost (its q
+// loads, the merge of its waves, its share of the merge launch) over more
+// keys.  It depends only on arguments the workspace query also takes, so
+// that query's answer covers every call it was made for.
+int64_t vec_default_partition(int64_t rows, int64_t max_seq_len, int32_t block_size) {
+  int64_t P = kDefaultPartitionTokens;
+  while (P < 4096 && rows * ceil_div(std::max<int64_t>(max_seq_len, 1), 2 * P) >= 1024) P *= 2;
+  return ceil_div(P, block_size) * block_size;
+}
+
 // Shape checks shared by both attention calls.
 int check_attention_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
@@ -78,7 +91,6 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   const int64_t part_units = partition_size > 0 ? std::max<int64_t>(1, partition_size / unit) : 0;
   const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, unit) : 0;
   const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
-  (void)max_seq_len;
   // The balanced split pays off when the rows are many and split into few
   // pieces; a long row cut into dozens of balanced pieces is better served by
   // the partition grid.  Estimate the pieces per row from the host-side bound.
@@ -117,7 +129,8 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     pl.plan_bytes = pl.plan_off_desc + align256((size_t)pl.ranges * 4 * sizeof(int));
     return pl;
   }
-  const int64_t P = effective_partition(partition_size, block_size);
+  const int64_t P = !mfma_shape && partition_size <= 0 ? vec_default_partition(rows, max_seq_len, block_size)
+                                                       : effective_partition(partition_size, block_size);
   const int64_t pu = std::max<int64_t>(1, P / unit);  // units per partition
   const int64_t nparts = cap > 0 ? ceil_div(blocks_per_row, pu) : 1;
   if (nparts > 0x7fffffff) {

@@ -118,41 +118,44 @@ __device__ __forceinline__ float *vec_attend(float *red, const float (&q)[GC][Ve
   // The slot's tokens go in batches of U: batch k is tokens t0 + slot +
   // (k * U + u) * STRIDE, u < U.  The K/V chunks of batch k + 1 are in flight
   // while batch k is used, and the block-table entries of batch k + 2 while
-  // those load, so no load waits on a table read of its own iteration.  A
-  // token past t1 or with a block id out of range loads nothing, carries
-  // zeros (a masked token then adds 0 * 0) and is masked.
+  // those load, so no load waits on a table read of its own iteration.
+  // Every load is issued whatever the token: a token past t1 reads the
+  // table entry of the range's last token, and a masked token (past t1, or
+  // with a block id out of range) reads row t % bs of block 0.  Its score is
+  // masked and its V values are taken as zeros, so what it read never
+  // counts.  (A load skipped on some paths would make the compiler's wait
+  // counting, which merges the paths, wait for every load in flight before
+  // each batch, the next batch's included.)
   struct KV {
     u32x4 k[U][CPL], v[U][CPL];
+    bool ok[U];  // the token is in range and its block id valid
   };
   auto tok = [&](int k, int u) { return t0 + slot + (k * U + u) * STRIDE; };
-  auto load_table = [&](int k, int (&ph)[U]) {
+  // raw table entries only: they are tested where the K/V loads use them, a
+  // batch later, so nothing waits for them here
+  auto load_table = [&](int k, int (&ent)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) ent[u] = table[min(tok(k, u), t1 - 1) / bs];  // t1 > t0 + slot here
+  };
+  auto load_kv = [&](int k, const int (&ent)[U], KV &kv) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = tok(k, u);
-      const int e = t < t1 ? table[t / bs] : -1;
-      debug_report(t < t1 && (unsigned)e >= (unsigned)num_blocks, kDbgBlockRange);
-      ph[u] = (unsigned)e < (unsigned)num_blocks ? e : -1;  // -1: masked
-    }
-  };
-  auto load_kv = [&](int k, const int (&ph)[U], KV &kv) {
+      debug_report(t < t1 && (unsigned)ent[u] >= (unsigned)num_blocks, kDbgBlockRange);
+      kv.ok[u] = t < t1 && (unsigned)ent[u] < (unsigned)num_blocks;
+      const int e = kv.ok[u] ? ent[u] : 0;
+      const int64_t off = (((int64_t)e * num_kv_heads + kh) * bs + (t % bs)) * row_bytes + col_bytes;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) kv.k[u][c] = kv.v[u][c] = u32x4{0u, 0u, 0u, 0u};
-      if (ph[u] >= 0) {
-        const int64_t off = (((int64_t)ph[u] * num_kv_heads + kh) * bs + (tok(k, u) % bs)) * row_bytes + col_bytes;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          kv.k[u][c] = ld16(kc + off + 16 * c);
-          kv.v[u][c] = ld16(vc + off + 16 * c);
-        }
+      for (int c = 0; c < CPL; ++c) {
+        kv.k[u][c] = ld16(kc + off + 16 * c);
+        kv.v[u][c] = ld16(vc + off + 16 * c);
       }
     }
   };
   // One batch: the U scores of every head first, then one max update and
   // rescale per head for the whole batch (the online-softmax rule of Month
   // 2 "PagedAttention" §5.4, applied to U keys at a time).
-  auto step = [&](const KV &kv, const int (&ph)[U]) {
+  auto step = [&](const KV &kv) {
     float kx[U][VPL];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -167,13 +170,16 @@ __device__ __forceinline__ float *vec_attend(float *red, const float (&q)[GC][Ve
 #pragma unroll
         for (int j = 0; j < VPL; ++j) sdot = __builtin_fmaf(q[h][j], kx[u][j], sdot);
         sdot = group_sum<LPR>(sdot);  // every lane of the slot: the whole dot product
-        x[h][u] = ph[u] >= 0 ? sdot * sl2 : kNegInf;
+        x[h][u] = kv.ok[u] ? sdot * sl2 : kNegInf;
       }
     float vx[U][VPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) unpack16<BF16>(kv.v[u][c], &vx[u][c * (VPL / CPL)]);
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) vx[u][j] = kv.ok[u] ? vx[u][j] : 0.f;  // a masked token adds 0 * 0
+    }
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
       float mx = x[h][0];
@@ -202,7 +208,12 @@ __device__ __forceinline__ float *vec_attend(float *red, const float (&q)[GC][Ve
 
   // Two fixed K/V register sets used in turn (no register of a load in
   // flight is ever copied), table entries of batches k, k + 1, k + 2 in p0,
-  // p1, p2.
+  // p1, p2.  The loop has one exit, at the bottom: each turn loads the next
+  // two batches whether or not they exist, so every path issues the same
+  // loads and each step waits for its own batch only.  A batch past the
+  // slot's last one is fully masked: it reads rows of block 0 and its step
+  // changes nothing (the max stays, the correction is exp2(0) = 1, every
+  // weight is 0), so the result is that of stopping at the last batch.
   const int nbatch = t1 > t0 + slot ? (t1 - t0 - slot + U * STRIDE - 1) / (U * STRIDE) : 0;
   if (nbatch > 0) {
     KV kv0, kv1;
@@ -210,15 +221,17 @@ __device__ __forceinline__ float *vec_attend(float *red, const float (&q)[GC][Ve
     load_table(0, p0);
     load_table(1, p1);
     load_kv(0, p0, kv0);
-    for (int k = 0;; k += 2) {
+    for (int k = 0; k < nbatch; k += 2) {
+      // (the scheduling barriers keep each step's arithmetic, which waits
+      // for its batch, from moving above the next batch's loads)
       load_table(k + 2, p2);
       load_kv(k + 1, p1, kv1);
-      step(kv0, p0);
-      if (k + 1 >= nbatch) break;
+      __builtin_amdgcn_sched_barrier(0);
+      step(kv0);
       load_table(k + 3, p0);
       load_kv(k + 2, p2, kv0);
-      step(kv1, p1);
-      if (k + 2 >= nbatch) break;
+      __builtin_amdgcn_sched_barrier(0);
+      step(kv1);
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // batch k + 2's entries to p0, k + 3's to p1
         const int t = p0[u];

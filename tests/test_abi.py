@@ -186,8 +186,13 @@ def test_decode_workspace_size(pa):
     g = Hq // Hkv
     ranges = 512
     streamk = _a256(ranges * 2 * g * D * 4) + _a256(ranges * 2 * g * 2 * 4) + _a256(ranges * 16)
-    grid = _a256(B * Hq * 16 * D * 4) + _a256(B * Hq * 16 * 2 * 4)       # 4096 / 256 partitions
+    # the vector kernels' pieces: the longest power of two (256 .. 4096 tokens) that keeps
+    # 512 rows x ceil(4096 / piece) >= 1024 workgroups: 2048 tokens, 2 per row
+    grid = _a256(B * Hq * 2 * D * 4) + _a256(B * Hq * 2 * 2 * 4)
     assert f(B, Hq, Hkv, D, bs, 4096, 0) == max(streamk, grid)
+    # few rows: the vector pieces stay at 256 tokens (8 rows x 8 pieces of 512 < 1024), so the
+    # workspace covers 16 pieces per row
+    assert f(4, 8, 2, 64, 16, 4096, 0) >= _a256(4 * 8 * 16 * 64 * 4) + _a256(4 * 8 * 16 * 2 * 4)
     # fixed 512-token pieces on 32K-token rows: 64 pieces per row, so the partition grid
     B, Hq, Hkv = 8, 64, 8
     grid = _a256(B * Hq * 64 * D * 4) + _a256(B * Hq * 64 * 2 * 4)
