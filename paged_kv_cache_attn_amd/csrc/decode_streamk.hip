@@ -2,7 +2,7 @@
 //
 // Same arithmetic as the MFMA decode tile step (attn_core.h), different work
 // split.  The blocks of all (sequence, KV head) rows are laid end to end in
-// one flat index space (sequence-major, then KV head, then logical block) and
+// one flat index space (KV head major, then sequence, then logical block) and
 // cut into equal contiguous ranges, one per workgroup, so every workgroup
 // streams the same number of 8 KB K+V tiles whatever the length mix.  A
 // range covers whole rows, whose output it writes directly, and at most two
@@ -143,13 +143,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   int T, G, s, e;
   if constexpr (MODE != kPlanned) {
-    // -- flat index space: exclusive prefix over sequences of blocks * Hkv ----
+    // -- flat index space: KV head major, then sequence, then tile ------------
+    // (s_pref: exclusive prefix over sequences of tiles; a KV head's rows span
+    // s_pref[B] positions).  Each XCD takes a contiguous run of ranges, so with
+    // the heads outermost an XCD serves one or two KV heads of every
+    // sequence: blocks that sequences share (a common prompt) are then read
+    // from HBM about once, not once per XCD, and the rows that share a block
+    // sit next to each other.
     if (B <= 64) {
       // one wave scans with cross-lane adds; a single barrier publishes it
       if (w == 0) {
         int L = lane < B ? p.seq_lens[lane] : 0;
         L = clamp_len(L, p.max_len_cap);
-        const int v = ((L + kBS - 1) / kBS) * Hkv;
+        const int v = (L + kBS - 1) / kBS;
         int incl = v;
   #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         int L = p.seq_lens[b];
         L = clamp_len(L, p.max_len_cap);
         s_len[b] = L;
-        local += ((L + kBS - 1) / kBS) * Hkv;
+        local += (L + kBS - 1) / kBS;
       }
       s_scan[tid] = local;
       if (tid < 2 * NW) s_brow[tid >> 1][tid & 1] = -1;
@@ -187,12 +193,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       int run = s_scan[tid] - local;
       for (int b = b0; b < b1; ++b) {
         s_pref[b] = run;
-        run += ((s_len[b] + kBS - 1) / kBS) * Hkv;
+        run += (s_len[b] + kBS - 1) / kBS;
       }
       if (tid == nt - 1) s_pref[B] = s_scan[tid];
       __syncthreads();
     }
-    T = s_pref[B];
+    const int Th = s_pref[B];  // positions of one KV head (the host keeps Th * Hkv within int)
+    T = Th * Hkv;
     G = ranges_used((int)gridDim.x, T, R);
 
     // no split row ends in this range unless the combine below (or, for a
@@ -216,14 +223,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // planner keeps ranges within kStreamKTabCache positions; the host keeps a
     // cache below 2^41 elements, so the offsets / 1024 fit in 31 bits.
     for (int pos = s + tid; pos < e; pos += 64 * NW) {
+      const int kh = pos / Th, rem = pos - kh * Th;  // pos < T, so Th > 0
       int lo = 0, hi = B;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= pos) lo = mid; else hi = mid;
+        if (s_pref[mid] <= rem) lo = mid; else hi = mid;
       }
-      const int nb = (s_pref[lo + 1] - s_pref[lo]) / Hkv;
-      const int off = pos - s_pref[lo];
-      const int kh = off / nb, j = off - kh * nb;
+      const int nb = s_pref[lo + 1] - s_pref[lo];
+      const int j = rem - s_pref[lo];
       int e0, e1;
       const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
                                   (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
