@@ -271,6 +271,21 @@ def test_decode_partition_size_independence(pa):
         assert max_err(out, ref) <= TOL["bf16"], part
 
 
+def test_decode_vector_default_pieces_many_rows(pa):
+    """fp32 caches at the 8B shape's row count (64 sequences x 8 KV heads): with partition_size 0 the vector
+    path takes long pieces (here 1024 tokens, so the longest rows split in two and go through the merge),
+    and every row matches the oracle; explicit 256-token pieces agree with it to the same bar."""
+    rng = np.random.default_rng(93)
+    lens = [int(x) for x in rng.integers(1, 1100, size=60)] + [1, 1023, 1024, 1025]
+    lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "f32", seed=93)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.088)
+    out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.088, "f32", 0))
+    assert max_err(out, ref) <= TOL["f32"]
+    out256 = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.088, "f32", 256))
+    assert max_err(out256, ref) <= TOL["f32"]
+    assert np.isfinite(out).all()
+
+
 def test_decode_zero_length_gives_zeros(pa):
     lens = [0, 20, 0]
     lay, q, k, v = rand_problem(lens, 32, 8, 128, 16, "bf16", seed=5)
