@@ -132,30 +132,23 @@ __device__ __forceinline__ void load_kv_tile_rows(KVTile &t, const uint16_t *kc,
   }
 }
 
-// The same tile with token `tpos` (0 .. 15) read from the rows nk, nv (one
-// K row and one V row of 128 bf16) instead of the cache: the lanes that hold
-// that token take their addresses from those rows, so every register is
-// still filled by exactly one load.
-__device__ __forceinline__ void load_kv_tile_rows_subst(KVTile &t, const uint16_t *kc, const uint16_t *vc,
-                                                        const TileRows &tr, int r, int c, bool stream, int tpos,
-                                                        const uint16_t *nk, const uint16_t *nv) {
+// The tile of load_kv_tile_rows with token `tpos` (0 .. 15; -1: none) read
+// from the rows nk, nv (one K row and one V row of 128 bf16) instead of the
+// cache: the lanes that hold that token take their addresses from those
+// rows, so every register is still filled by exactly one load and every
+// tile issues the same load sequence.  STREAM picks the load kind.
+template <bool STREAM>
+__device__ __forceinline__ void load_kv_tile_rows_subst_as(KVTile &t, const uint16_t *kc, const uint16_t *vc,
+                                                           const TileRows &tr, int r, int c, int tpos,
+                                                           const uint16_t *nk, const uint16_t *nv) {
   const uint16_t *krow = c == tpos ? nk : kc + (c < 8 ? tr.lo : tr.hi) + (c & 7) * 128;
   const int64_t vr = r < 2 ? tr.lo : tr.hi;
-  const uint16_t *vrow[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) vrow[v] = 4 * r + v == tpos ? nv : vc + vr + ((4 * r + v) & 7) * 128;
-  if (stream) {
-    asm volatile("");  // see load_kv_tile_rows
+  for (int i = 0; i < 4; ++i) t.k[i] = STREAM ? ld16_stream(krow + 32 * i + 8 * r) : ld16(krow + 32 * i + 8 * r);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = ld16_stream(krow + 32 * i + 8 * r);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) t.v[v] = ld16_stream(vrow[v] + 8 * c);
-    asm volatile("");
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = ld16(krow + 32 * i + 8 * r);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) t.v[v] = ld16(vrow[v] + 8 * c);
+  for (int v = 0; v < 4; ++v) {
+    const uint16_t *vrow = 4 * r + v == tpos ? nv : vc + vr + ((4 * r + v) & 7) * 128;
+    t.v[v] = STREAM ? ld16_stream(vrow + 8 * c) : ld16(vrow + 8 * c);
   }
 }
 

@@ -112,10 +112,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     DecodeParams p) {
   static_assert(!APPEND || (MODE == kPlanned && !FP8), "the folded write serves planned bf16 calls");
   using F = KVFormat<FP8>;
-  // FP8 kernels (which never fold the write in) fix the load kind per share
-  // so that each step waits for its own tile only; the bf16 kernels keep the
-  // per-tile choice, whose smaller loop suits their short shares better.
-  constexpr bool kExactWaits = FP8 && !APPEND;
   __shared__ int s_pref[MODE == kPlanned ? 1 : kStreamKMaxSeqs + 1];  // first flat block of each sequence
   __shared__ int s_len[MODE == kPlanned ? 1 : kStreamKMaxSeqs];       // clamped sequence lengths
   __shared__ int s_scan[64 * NW];
@@ -356,73 +352,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bf16x8 q[4];
     int lim;
   };
-  //
-  // KIND 0 picks the load kind tile by tile (a branch between two load
-  // sequences) and loads q after the tile.  KIND 1 (non-temporal) and 2
-  // (ordinary) fix it for the share and load q first, so the tile's loads are
-  // always the last a slot issues (see the loop below).
+  // Position li (< le) into slot sl.  The load kind is fixed for the share
+  // (KIND 1 non-temporal, 2 ordinary), and q, when loaded, goes out before
+  // the tile, so a slot's last loads are always its tile's and every path
+  // issues the same ones (see the loop below).
   auto load_slot = [&](int li, Slot &sl, int dist, auto kind) __attribute__((always_inline)) {
-    constexpr int KIND = decltype(kind)::value;
+    constexpr bool STREAM = decltype(kind)::value == 1;
     const int lp = li - dist;
-    if constexpr (KIND == 0) {
-      // past the share: nothing to load (a dummy load there would be a memory
-      // round trip the combine below waits for, since its registers are reused)
-      if (li >= le) {
-        sl.lim = 0;
-        return;
-      }
-    }
     const int2 u = s_rows[li];
     const int row = s_prow[li];
     const int b = row / Hkv, kh = row - b * Hkv;
     const bool ok = u.x >= 0;
-    if constexpr (KIND != 0) {
-      const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
-      if (__builtin_amdgcn_readfirstlane((int)need_q))
-        F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
-    }
+    const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
+    if (__builtin_amdgcn_readfirstlane((int)need_q))
+      F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
     sl.lim = ok ? s_ln[li].x : 0;
     // a masked tile reads the first rows of the cache
-    const bool stream = __builtin_amdgcn_readfirstlane(s_keep[li]) == 0;
     const TileRows tr{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10};
-    bool subst = false;
-    int tpos = 0;
     if constexpr (APPEND) {
       // A row's last tile holds position L - 1; when the caller's slot for
-      // the sequence's new token names that place, the new K/V row is read
-      // in its stead.  (Block sizes of this path are powers of two.)
+      // the sequence's new token names that place, the lanes that hold that
+      // token read the new K/V row in its stead (the same load instructions
+      // for every tile).  (Block sizes of this path are powers of two.)
+      int tpos = -1;
       const int2 ln = s_ln[li];
       if (ok && s_pj[li] == ln.y - 1) {  // uniform: the position's record
-        tpos = (ln.x - 1) & 15;
-        const int64_t at = (tpos < 8 ? tr.lo : tr.hi) + (tpos & 7) * kD;
+        const int at_pos = (ln.x - 1) & 15;
+        const int64_t at = (at_pos < 8 ? tr.lo : tr.hi) + (at_pos & 7) * kD;
         const int64_t sm = s_slot[b];
         const int lb = __builtin_ctz((unsigned)p.block_size);
-        subst = sm >= 0 && sm < ((int64_t)p.num_blocks << lb) &&
-                ((((sm >> lb) * Hkv + kh) << lb) + (sm & (p.block_size - 1))) * kD == at;
+        if (sm >= 0 && sm < ((int64_t)p.num_blocks << lb) &&
+            ((((sm >> lb) * Hkv + kh) << lb) + (sm & (p.block_size - 1))) * kD == at)
+          tpos = at_pos;
       }
-    }
-    if constexpr (KIND != 0) {
-      static_assert(!APPEND, "the folded write takes the per-tile load choice");
-      (void)stream;
-      (void)subst;
-      (void)tpos;
-      F::template load_as<KIND == 1>(sl.t, kc, vc, tr, r, c);
-    } else if constexpr (APPEND) {
-      if (subst)
-        load_kv_tile_rows_subst(sl.t, kc, vc, tr, r, c, stream, tpos,
-                                reinterpret_cast<const uint16_t *>(p.new_k) + ((int64_t)b * Hkv + kh) * kD,
-                                reinterpret_cast<const uint16_t *>(p.new_v) + ((int64_t)b * Hkv + kh) * kD);
-      else
-        F::load(sl.t, kc, vc, tr, r, c, stream);
+      load_kv_tile_rows_subst_as<STREAM>(
+          sl.t, kc, vc, tr, r, c, tpos,
+          reinterpret_cast<const uint16_t *>(p.new_k) + ((int64_t)b * Hkv + kh) * kD,
+          reinterpret_cast<const uint16_t *>(p.new_v) + ((int64_t)b * Hkv + kh) * kD);
     } else {
-      (void)subst;
-      (void)tpos;
-      F::load(sl.t, kc, vc, tr, r, c, stream);
-    }
-    if constexpr (KIND == 0) {
-      const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
-      if (__builtin_amdgcn_readfirstlane((int)need_q))
-        F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
+      F::template load_as<STREAM>(sl.t, kc, vc, tr, r, c);
     }
   };
 
@@ -431,12 +399,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     st.init();
     int slot_used = 0;
     int seg_j0 = s_pj[ls];  // first block of the current row inside this share
-    // close the current row if position li was its last one in the share;
-    // returns false when the share is done
-    auto after_step = [&](int li) -> bool {
+    // close the current row if position li was its last one in the share
+    auto after_step = [&](int li) {
       const int row = s_prow[li];
       const bool row_end = li + 1 == le || s_prow[li + 1] != row;
-      if (!row_end) return true;
+      if (!row_end) return;
       const int b = row / Hkv, kh = row - b * Hkv;
       const int nb = s_ln[li].y;
       const float lw = row_sum4(st.l);
@@ -472,119 +439,84 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           s_bnb[w][k] = nb;
         }
       }
-      if (li + 1 == le) return false;
+      if (li + 1 == le) return;
       seg_j0 = s_pj[li + 1];
       st.init();
-      return true;
     };
-    using K0 = std::integral_constant<int, 0>;
-    if constexpr (!kExactWaits) {
-      {
-        // kSlots fixed register slots: position li lives in slot (li - ls) mod
-        // kSlots, so no tile register is copied while its load is in flight.
-        // Two slots (one tile computed while the next one loads) keep about
-        // 128 KB in flight per CU, which streams as fast as three (bf16) and
-        // leaves the registers to the scheduler.
-        constexpr int NS = kSlots;
-        Slot s[NS];
-  #pragma unroll
-        for (int i = 0; i < NS - 1; ++i) load_slot(ls + i, s[i], NS, K0());
-        auto one = [&](int li, auto kc) __attribute__((always_inline)) -> bool {
-          constexpr int k = decltype(kc)::value;
-          load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS, K0());
-          st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
-          return after_step(li);
-        };
-        for (int li = ls;; li += NS) {
-          if (!one(li, std::integral_constant<int, 0>())) break;
-          if (!one(li + 1, std::integral_constant<int, 1>())) break;
-          if constexpr (NS > 2) {
-            if (!one(li + 2, std::integral_constant<int, 2>())) break;
-          }
-          if constexpr (NS > 3) {
-            if (!one(li + 3, std::integral_constant<int, 3>())) break;
-          }
-          if constexpr (NS > 4) {
-            if (!one(li + 4, std::integral_constant<int, 4>())) break;
-          }
-          if constexpr (NS > 5) {
-            if (!one(li + 5, std::integral_constant<int, 5>())) break;
-          }
-        }
-      }
-    } else {
-      // The same ring with the load kind fixed for the share, and the share's
-      // last NS - 1 positions (which load nothing) run apart.  Every slot then
-      // issues its tile's loads last on every path, so the compiler's wait
-      // before a step covers that step's own tile and leaves the later
-      // NS - 1 tiles in flight.  (With a branch between the two load kinds,
-      // or a path that loads nothing, its counting merges paths with
-      // different numbers of loads in flight and it waits for all of them,
-      // the next tile's prefetch included.)  The share takes ordinary loads
-      // throughout when any of its tiles is marked as shared with a
-      // neighbouring row, else non-temporal ones.
-      bool keep_any = false;
-      for (int k = ls + lane; k < le; k += 64) keep_any |= s_keep[k] != 0;
-      auto run = [&](auto kind) __attribute__((always_inline)) {
-        constexpr int NS = kSlots;
-        Slot s[NS];
+    // kSlots fixed register slots: position li lives in slot (li - ls) mod
+    // kSlots, so no tile register is copied while its load is in flight.  Two
+    // slots (one tile computed while the next one loads) keep about 128 KB in
+    // flight per CU.  The share's last NS - 1 positions, which load nothing,
+    // run apart, so every other step follows the same loads: each slot's
+    // tile loads are the last it issues, on every path, and the compiler's
+    // wait before a step covers that step's own tile only, leaving the later
+    // NS - 1 tiles in flight.  (A branch between two load sequences, or a
+    // path that loads nothing, makes its counting merge paths with different
+    // numbers of loads in flight, and it then waits for all of them, the next
+    // tile's prefetch included.)  So the load kind is one for the share:
+    // ordinary loads throughout when any of its tiles is marked as shared
+    // with a neighbouring row, else non-temporal ones.
+    bool keep_any = false;
+    for (int k = ls + lane; k < le; k += 64) keep_any |= s_keep[k] != 0;
+    auto run = [&](auto kind) __attribute__((always_inline)) {
+      constexpr int NS = kSlots;
+      Slot s[NS];
 #pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-          if (ls + i < le) load_slot(ls + i, s[i], NS, kind);
-        auto one = [&](int li, auto kc) __attribute__((always_inline)) {
-          constexpr int k = decltype(kc)::value;
-          load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS, kind);
-          st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
-          after_step(li);
-        };
-        // positions li .. le - 1 (fewer than NS of them), from slot k on
-        auto last = [&](int li, auto kc) __attribute__((always_inline)) {
-          constexpr int k = decltype(kc)::value;
+      for (int i = 0; i < NS - 1; ++i)
+        if (ls + i < le) load_slot(ls + i, s[i], NS, kind);
+      auto one = [&](int li, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        load_slot(li + NS - 1, s[(k + NS - 1) % NS], NS, kind);
+        st.step(s[k].q, F::expand(s[k].t), s_pj[li] * kBS, s[k].lim, sl2, r);
+        after_step(li);
+      };
+      // positions li .. le - 1 (fewer than NS of them), from slot k on
+      auto last = [&](int li, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
 #pragma unroll
-          for (int j = 0; j < NS - 1; ++j) {
-            if (li + j < le) {
-              Slot &sj = s[(k + j) % NS];
-              st.step(sj.q, F::expand(sj.t), s_pj[li + j] * kBS, sj.lim, sl2, r);
-              after_step(li + j);
-            }
-          }
-        };
-        using E0 = std::integral_constant<int, 0>;
-        using E1 = std::integral_constant<int, 1 % NS>;
-        using E2 = std::integral_constant<int, 2 % NS>;
-        using E3 = std::integral_constant<int, 3 % NS>;
-        for (int li = ls;; li += NS) {
-          if (li + NS - 1 >= le) {
-            last(li, E0());
-            break;
-          }
-          one(li, E0());
-          if (li + NS >= le) {
-            last(li + 1, E1());
-            break;
-          }
-          one(li + 1, E1());
-          if constexpr (NS > 2) {
-            if (li + NS + 1 >= le) {
-              last(li + 2, E2());
-              break;
-            }
-            one(li + 2, E2());
-          }
-          if constexpr (NS > 3) {
-            if (li + NS + 2 >= le) {
-              last(li + 3, E3());
-              break;
-            }
-            one(li + 3, E3());
+        for (int j = 0; j < NS - 1; ++j) {
+          if (li + j < le) {
+            Slot &sj = s[(k + j) % NS];
+            st.step(sj.q, F::expand(sj.t), s_pj[li + j] * kBS, sj.lim, sl2, r);
+            after_step(li + j);
           }
         }
       };
-      if (__builtin_amdgcn_ballot_w64(keep_any) == 0)
-        run(std::integral_constant<int, 1>());
-      else
-        run(std::integral_constant<int, 2>());
-    }
+      using E0 = std::integral_constant<int, 0>;
+      using E1 = std::integral_constant<int, 1 % NS>;
+      using E2 = std::integral_constant<int, 2 % NS>;
+      using E3 = std::integral_constant<int, 3 % NS>;
+      for (int li = ls;; li += NS) {
+        if (li + NS - 1 >= le) {
+          last(li, E0());
+          break;
+        }
+        one(li, E0());
+        if (li + NS >= le) {
+          last(li + 1, E1());
+          break;
+        }
+        one(li + 1, E1());
+        if constexpr (NS > 2) {
+          if (li + NS + 1 >= le) {
+            last(li + 2, E2());
+            break;
+          }
+          one(li + 2, E2());
+        }
+        if constexpr (NS > 3) {
+          if (li + NS + 2 >= le) {
+            last(li + 3, E3());
+            break;
+          }
+          one(li + 3, E3());
+        }
+      }
+    };
+    if (__builtin_amdgcn_ballot_w64(keep_any) == 0)
+      run(std::integral_constant<int, 1>());
+    else
+      run(std::integral_constant<int, 2>());
   }
   if constexpr (MODE == kPlanned) TL_MAIN(2 + (w & 3), lane == 0);
   __syncthreads();
