@@ -232,10 +232,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                   (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
       debug_report(!ok, kDbgBlockRange);
       const TileRows tr = map.rows(e0, e1, kh);
-      // A tile read by this row only streams through the caches (non-temporal
-      // loads); one whose block the previous or the next sequence also uses at
+      // Mark a tile whose block the previous or the next sequence also uses at
       // the same place (forked or prefix-sharing sequences, which sit next to
-      // each other in a batch) is loaded so that it stays in the L2 for them.
+      // each other in a batch): a wave share holding one loads with ordinary
+      // loads, which keep it in the L2 for those rows; every other share
+      // streams through the caches (non-temporal loads).
       int keep = 0;
       if (ok) {
         const int i0 = map.first_index(j), bsz = p.block_size;
