@@ -14,7 +14,7 @@
 namespace {
 
 constexpr int kDefaultPartitionTokens = 256;
-constexpr int64_t kStreamKMaxPiecesPerRow = 16;
+constexpr int64_t kStreamKMaxPiecesPerRow = 16;  // a caller's fixed pieces per row on the balanced path
 constexpr int kMaxGridYZ = 65535;
 
 int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
@@ -91,19 +91,18 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   const int64_t part_units = partition_size > 0 ? std::max<int64_t>(1, partition_size / unit) : 0;
   const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, unit) : 0;
   const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
-  // The balanced split pays off when the rows are many and split into few
-  // pieces; a long row cut into dozens of balanced pieces is better served by
-  // the partition grid.  Estimate the pieces per row from the host-side bound.
   // balanced ranges: the default count, or more when that keeps every range
   // within the blocks a workgroup can stage (t_upper bounds the real total)
   const int64_t sk_ranges_default = std::max<int64_t>(
       {1, std::min<int64_t>(pa::kStreamKRanges, t_upper), ceil_div(t_upper, pa::kStreamKTabCache)});
-  const int64_t pieces_per_row =
-      partition_size > 0 ? ceil_div(std::max<int64_t>(blocks_per_row, 1), part_units)
-                         : ceil_div(sk_ranges_default, std::max<int64_t>(rows, 1)) + 1;
-  if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff &&
-      pieces_per_row <= kStreamKMaxPiecesPerRow &&
-      (partition_size == 0 || part_units <= pa::kStreamKTabCache)) {
+  // The library's own split is always the balanced one on the MFMA path (its
+  // merge shares a row cut into many pieces out over the row's ranges).  A
+  // caller's fixed pieces take fixed-size ranges when they are few per row;
+  // more per row, the partition grid, whose pieces are the row's own.
+  const bool fixed_ok = partition_size == 0 ||
+                        (part_units <= pa::kStreamKTabCache &&
+                         ceil_div(std::max<int64_t>(blocks_per_row, 1), part_units) <= kStreamKMaxPiecesPerRow);
+  if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff && fixed_ok) {
     pl.streamk = true;
     if (partition_size > 0) {
       pl.range_blocks = (int)part_units;

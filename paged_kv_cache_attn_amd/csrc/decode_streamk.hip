@@ -198,8 +198,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     T = Th * Hkv;
     G = ranges_used((int)gridDim.x, T, R);
 
-    // no split row ends in this range unless the combine below (or, for a
-    // plan, the staging loop) says so
+    // no split row under this range's first position unless the staging
+    // loop below says so
     if (tid == 0) p.sk_desc[gi] = int4{-1, 0, 0, 0};
 
     s = range_begin(gi, T, G, R);
@@ -249,17 +249,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       s_pj[pos - s] = j;
       s_ln[pos - s] = int2{s_len[lo], nb};
       s_keep[pos - s] = keep;
+      // the merge descriptor: the row under the range's first position, if
+      // it began in an earlier range or goes on past this one, with its span
+      // of ranges (same thread as the -1 written above: pos == s only for
+      // tid 0).  A plan keeps it, so planned calls do no range arithmetic.
+      if (pos == s && (j > 0 || s - j + nb > e)) {
+        const int rs = s - j;
+        const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
+        const int g_last = max(range_of(rs + nb - 1, T, G, R), gi);
+        p.sk_desc[gi] = int4{lo * Hkv + kh, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, g_last};
+      }
       if constexpr (MODE == kPlanOnly) {
-        // the split row whose last piece this range holds is the one under
-        // its first position, if that row began in an earlier range and ends
-        // in this one; the plan keeps its merge descriptor, so planned calls
-        // do no range arithmetic after the stream (same thread as the -1
-        // written above: pos == s only for tid 0)
-        if (pos == s && j > 0 && s - j + nb <= e) {
-          const int rs = s - j;
-          const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
-          p.sk_desc[gi] = int4{lo * Hkv + kh, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
-        }
         const int64_t at = (int64_t)gi * p.plan_stride + (pos - s);
         p.plan_rec[at] = int4{s_rows[pos - s].x, s_rows[pos - s].y, lo * Hkv + kh, j};
         p.plan_rec2[at] = int2{s_len[lo], nb | (keep ? kKeepTile : 0)};
@@ -548,11 +548,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool whole = rs >= s && rs + nb <= e;
     const int slot = rs <= s ? 0 : 1;
     const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
-    if (MODE != kPlanned && !whole && slot == 0 && rs + nb <= e && tid == 0) {
-      // this range holds the last piece of a row that began in an earlier one
-      const int g_first = min(max(range_of(rs, T, G, R), 0), gi);
-      p.sk_desc[gi] = int4{row, g_first, rs <= range_begin(g_first, T, G, R) ? 0 : 1, gi - g_first + 1};
-    }
     // the run's members: the entries from h on with this row start (a bit
     // mask, uniform; empty entries may sit between members).  Most runs have
     // one member: a row that only touches one wave's share.
@@ -636,13 +631,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if constexpr (MODE == kPlanned) TL_MAIN(7, tid == 0);
 }
 
-// One workgroup per range gi: if the range holds the last piece of a row
-// that began in an earlier range (its descriptor says so), the row's pieces
-// are merged, in ascending range order, and the row is written.  Most such
-// rows have exactly two pieces -- the end of range gi - 1 and the start of
-// range gi -- so those are loaded together with the descriptor, in one
-// memory round trip; rows with more pieces take a second one.  A thread
-// owns output elements (column, dim).
+// One workgroup per range gi; its descriptor names the split row under the
+// range's first position, if any, and that row's span of ranges.  A row of
+// at most kShortRow pieces is merged, in ascending range order, by the
+// workgroup of its last range, a thread owning output elements (column,
+// dim).  Most split rows have exactly two pieces -- the end of range gi - 1
+// and the start of range gi -- so those are loaded together with the
+// descriptor, in one memory round trip; rows with more pieces take a second
+// one.  A longer row (few rows cut over many ranges) is shared out: its
+// output elements are cut into chunks of cw consecutive elements, dealt to
+// the ranges whose first piece is the row's, and inside a workgroup the
+// pieces are dealt to the threads (kBatch per memory round trip) and the
+// per-thread results combined through LDS, so no workgroup walks all the
+// pieces alone.  The merge rule is associative, so the grouping changes only
+// the rounding.
 //
 // APPEND: the workgroups also write the step's new K/V rows to their slots
 // (row gi, gi + grid, ...), after every read of the main kernel, as
@@ -651,7 +653,9 @@ template <bool APPEND>
 __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams p) {
   TL_MERGE(0);
   constexpr int kBatch = 8;
-  constexpr int kPer = 2;  // the launch uses g * kD / 2 threads: two elements each
+  constexpr int kShortRow = 8;
+  constexpr int kPer = 2;  // the launch uses max(g * kD / 2, 256) threads: two elements each
+  __shared__ float s_m[1024], s_l[1024], s_o[1024];
   // the same range numbering as the main kernel, so this workgroup runs on
   // the XCD that wrote range gi's pieces (and, but at XCD edges, gi - 1's)
   const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);
@@ -661,10 +665,11 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   const int nrows = p.num_seqs * p.num_kv_heads;
   const int len0 = gi < nrows ? p.seq_lens[gi / p.num_kv_heads] : 1;  // with the descriptor: one round trip
   // speculative: (gp, slot 0), (gp, slot 1), (gi, slot 0) for both elements
+  const int E = g * kD;  // output elements of a row
   float sm[3][kPer], sl[3][kPer], so[3][kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int idx = threadIdx.x + u * blockDim.x;
+    const int idx = min((int)threadIdx.x + u * (int)blockDim.x, E - 1);
     const int cc = idx / kD, d = idx - cc * kD;
     const int64_t pc[3] = {((int64_t)gp * 2 + 0) * g + cc, ((int64_t)gp * 2 + 1) * g + cc, ((int64_t)gi * 2) * g + cc};
 #pragma unroll
@@ -722,13 +727,80 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
     TL_MERGE(1);
     return;
   }
-  const int g_first = min(max(dsc.y, 0), gi), s_first = dsc.z & 1, nc = gi - g_first + 1;
+  const int g_first = min(max(dsc.y, 0), gi), s_first = dsc.z & 1;
+  const int g_last = min(max(dsc.w, gi), (int)gridDim.x - 1), nc = g_last - g_first + 1;
   const int b = row / p.num_kv_heads, kh = row - b * p.num_kv_heads;
   const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+  auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
+    return ((int64_t)(g_first + k) * 2 + (k == 0 ? s_first : 0)) * g + cc;
+  };
+  if (nc > kShortRow) {
+    // chunk width: 64 elements, halved (down to 16) while every chunk still
+    // finds a workgroup; the workgroups are the ranges g_first + s_first ..
+    // g_last (a stale descriptor can give qi < 0: that workgroup idles)
+    const int q0 = g_first + s_first, nw = g_last - q0 + 1, qi = gi - q0;
+    int cw = 64;
+    while (cw > 16 && E / (cw / 2) <= nw) cw >>= 1;
+    const int nchunk = E / cw, lanes = (int)blockDim.x / cw;
+    const int el = (int)threadIdx.x % cw, ln = (int)threadIdx.x / cw;
+    for (int c = qi < 0 ? nchunk : qi; c < nchunk; c += nw) {
+      const int idx = c * cw + el, cc = idx / kD, d = idx - cc * kD;
+      float M = kNegInf, lsum = 0.f, o = 0.f;
+      for (int k0 = ln; k0 < nc; k0 += lanes * kBatch) {
+        float pm[kBatch], pl[kBatch], po[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int kk = k0 + k * lanes;
+          const int64_t pc = piece(min(kk, nc - 1), cc);
+          pm[k] = kk < nc ? p.sk_ml[pc * 2] : kNegInf;
+          pl[k] = p.sk_ml[pc * 2 + 1];
+          po[k] = p.sk_part[pc * kD + d];
+        }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, pm[k]);
+        const float Mu = Mb == kNegInf ? 0.f : Mb;
+        const float cf = fast_exp2(M - Mu);
+        lsum *= cf;
+        o *= cf;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const float wgt = fast_exp2(pm[k] - Mu);
+          lsum += pl[k] * wgt;
+          o += po[k] * wgt;
+        }
+        M = Mb;
+      }
+      s_m[threadIdx.x] = M;
+      s_l[threadIdx.x] = lsum;
+      s_o[threadIdx.x] = o;
+      __syncthreads();
+      if (ln == 0) {
+        float Mt = kNegInf;
+        for (int t = 0; t < lanes; ++t) Mt = fmaxf(Mt, s_m[t * cw + el]);
+        const float Mu = Mt == kNegInf ? 0.f : Mt;
+        float lt = 0.f, ot = 0.f;
+        for (int t = 0; t < lanes; ++t) {
+          const float wgt = fast_exp2(s_m[t * cw + el] - Mu);
+          lt += s_l[t * cw + el] * wgt;
+          ot += s_o[t * cw + el] * wgt;
+        }
+        store_value(p.out, p.out_bf16, (out_row0 + cc) * kD + d, lt > 0.f ? ot * p.v_scale / lt : 0.f);
+      }
+      __syncthreads();
+    }
+    TL_MERGE(1);
+    return;
+  }
+  if (gi != g_last) {  // a short row is merged by its last range
+    TL_MERGE(1);
+    return;
+  }
   if (nc == 2) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = threadIdx.x + u * blockDim.x;
+      if (idx >= E) continue;
       const int cc = idx / kD, d = idx - cc * kD;
       const int f = s_first;  // first piece: (gi - 1, s_first); second: (gi, 0)
       const float m0 = sm[f][u], m1 = sm[2][u];
@@ -742,10 +814,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
     TL_MERGE(1);
     return;
   }
-  auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
-    return ((int64_t)(g_first + k) * 2 + (k == 0 ? s_first : 0)) * g + cc;
-  };
-  for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < E; idx += blockDim.x) {
     const int cc = idx / kD, d = idx - cc * kD;
     float M = kNegInf, lsum = 0.f, o = 0.f;
     for (int k0 = 0; k0 < nc; k0 += kBatch) {
@@ -809,7 +878,7 @@ hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
                        p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_streamk_merge_kernel<true>, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
+    hipLaunchKernelGGL(decode_streamk_merge_kernel<true>, dim3(p.sk_ranges), dim3(std::max(g * kD / 2, 256)), 0, stream, p);
     return hipGetLastError();
   }
   if (p.kv_fp8 && planned)
@@ -822,7 +891,7 @@ hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_streamk_kernel<PA_DECODE_WAVES, false, kFused>), grid, block, park, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_streamk_merge_kernel<false>, dim3(p.sk_ranges), dim3(g * kD / 2), 0, stream, p);
+  hipLaunchKernelGGL(decode_streamk_merge_kernel<false>, dim3(p.sk_ranges), dim3(std::max(g * kD / 2, 256)), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -77,9 +77,9 @@ struct DecodeParams {
   int sk_range_blocks;     // 0: T / sk_ranges blocks each (balanced); > 0: fixed
   float *sk_part;          // [ranges][2][g][D] partial outputs
   float *sk_ml;            // [ranges][2][g][2] partial (max, sum)
-  int4 *sk_desc;           // [ranges] split row whose last piece the range holds
+  int4 *sk_desc;           // [ranges] the split row under the range's first position
                            //   (workspace; for a planned call, the plan's copy):
-                           // {row or -1, first range, slot of the first piece, pieces}
+                           // {row or -1, its first range, slot of its first piece, its last range}
   // a decode plan (balanced path; nullptr: each launch stages its own range)
   int4 *plan_hdr;          // [ranges] {range start, range end, total blocks T, ranges used G}
   int4 *plan_rec;          // [ranges][plan_stride] {tile row 0 / 1024, tile row 8 / 1024, row, j}

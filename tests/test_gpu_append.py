@@ -124,6 +124,21 @@ def test_decode_append_equals_write_then_decode(pa, dtype, bs, Hq, Hkv):
     assert max_err(o1.astype(np.float64), ref) <= TOL["f32" if dtype == "f32" else "bf16"]
 
 
+def test_decode_append_few_long_rows(pa):
+    """Two long sequences of 8 KV heads, each row cut into dozens of pieces: the folded step (its merge shares
+    every row out over the row's ranges and writes the new rows) against the two-call step and the oracle."""
+    lens = [3000, 1201]
+    lay, q, k, v, nk, nv, slots, ks, vs = _setup(lens, 64, 8, 16, "bf16", seed=61)
+    o1, k1, v1, scale = _run(pa, lay, q, k, v, nk, nv, slots, ks, vs, fold=True)
+    o2, k2, v2, _ = _run(pa, lay, q, k, v, nk, nv, slots, ks, vs, fold=False)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2), "caches differ"
+    assert np.array_equal(o1, o2), "outputs differ: max %.3g" % np.nanmax(np.abs(o1 - o2))
+    kh, vh = k.copy(), v.copy()
+    oracle.kv_cache_write(nk, nv, kh, vh, slots)
+    ref = oracle.paged_decode(q, kh, vh, lay.block_tables, lay.seq_lens, scale)
+    assert max_err(o1.astype(np.float64), ref) <= TOL["bf16"]
+
+
 def test_decode_append_full_config(pa):
     """The 8B-shaped decode step (64 lognormal rows) folded, in the configuration bench.py times, against the
     two-call step: bit-identical output and caches."""

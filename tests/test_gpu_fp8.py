@@ -127,7 +127,8 @@ def test_decode_fp8_parity(pa, Hq, Hkv, bs, out_dtype, part):
 
 
 def test_decode_fp8_long_rows_partition_grid(pa):
-    """Rows cut into many one-tile pieces take the partition grid and its merge."""
+    """Rows cut into many one-tile pieces take the partition grid and its merge; the library's own split of
+    the same rows (dozens of pieces each) the balanced kernel and its shared merge."""
     lens = [3000, 7, 2049]
     lay, q, kc, vc = fp8_problem(lens, 32, 8, 128, 16, seed=71, ks=0.05, vs=0.004)
     ref = oracle.paged_decode(q, kc, vc, lay.block_tables, lay.seq_lens, 0.09, k_scale=0.05, v_scale=0.004)

@@ -450,13 +450,39 @@ def test_prefill_one_row_equals_decode(pa):
 
 # ----------------------------------------------------------------------------- balanced decode specifics
 def test_decode_one_row_split_over_many_ranges(pa):
-    """One KV head, one long row: every 16-token block its own range, merged by the last arrival."""
+    """One KV head, one long row: fixed one- and three-tile pieces take the partition grid; the library's
+    own split cuts the row over 313 one-tile ranges, whose merge shares the row out over those ranges."""
     lens = [5000]
     lay, q, k, v = rand_problem(lens, 16, 1, 128, 16, "bf16", seed=13)
     ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.088)
     for part in (16, 48, 0):
         out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.088, "f32", part))
         assert max_err(out, ref) <= TOL["bf16"], part
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,bs,part", [
+    ([5000], 8, 1, 16, 0),                 # one row over 313 ranges: 16-element chunks
+    ([2000] * 7, 64, 8, 16, 0),            # 56 rows of 10-11 pieces: 64-element chunks, some workgroups take
+                                           # two, many rows' first pieces in slot 1
+    ([3000, 0, 1500, 7], 16, 16, 32, 0),   # group 1: 128 elements over a 256-thread workgroup
+    ([2500, 900], 32, 2, 64, 0),           # group 16
+    ([3000] * 4, 32, 8, 16, 256),          # a caller's 256-token pieces: 12 or 13 per row, fixed-size ranges
+])
+def test_decode_long_rows_shared_merge(pa, lens, Hq, Hkv, bs, part):
+    """Rows cut into more than eight pieces: the merge deals each row's output elements out, in chunks of 16
+    to 64, to the ranges holding the row, and its pieces to the threads of each; every output matches the
+    oracle, empty rows are zero, and repeats are bit-identical."""
+    torch = torch_mod()
+    lay, q, k, v = rand_problem(lens, Hq, Hkv, 128, bs, "bf16", seed=31 + Hq + bs)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.085)
+    first = gpu_decode(pa, lay, q, k, v, 0.085, "f32", part)
+    out = out_to_f64(first)
+    assert max_err(out, ref) <= TOL["bf16"], max_err(out, ref)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
+    again = gpu_decode(pa, lay, q, k, v, 0.085, "f32", part)
+    assert torch.equal(first, again)
 
 
 def test_decode_workspace_reuse_and_garbage(pa):

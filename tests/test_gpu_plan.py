@@ -42,6 +42,9 @@ PLAN_CASES = [
     ("mixed", 32, 8, 8, "bf16", 0, "bf16"),
     ("mixed", 32, 4, 64, "fp8", 0, "f32"),
     ("mixed", 16, 16, 32, "fp8", 256, "f32"),
+    ("few_long", 64, 8, 16, "bf16", 0, "f32"),       # rows of dozens of pieces: the shared merge
+    ("few_long", 8, 1, 16, "fp8", 0, "bf16"),
+    ("few_long", 8, 8, 32, "bf16", 0, "f32"),        # group 1
 ]
 
 
@@ -50,6 +53,8 @@ def _lens(kind):
         return list(synth.lognormal_lengths(64, 390, 0.685, 16, 2048, seed=3))
     if kind == "lognormal100":
         return list(synth.lognormal_lengths(100, 200, 0.685, 1, 1024, seed=4))
+    if kind == "few_long":
+        return [3000, 0, 1500, 7]
     return [0, 1, 15, 16, 17, 300, 1000, 0, 63, 64, 65, 2049, 5]
 
 
