@@ -28,6 +28,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// A GQA group of more than 16 query heads (one MFMA tile's columns) is served
+// by the balanced decode as hs sub-groups of g / hs <= 16 heads, each its own
+// row over the same K/V: hs is the smallest divisor of g that is at least
+// ceil(g / 16).  1 for g <= 16.
+int head_split(int g) {
+  int hs = (g + 15) / 16;
+  while (g % hs != 0) ++hs;
+  return hs;
+}
+
 // Partition size (tokens) the decode call uses; 0 selects the default,
 // rounded up to a whole number of blocks.
 int64_t effective_partition(int32_t partition_size, int32_t block_size) {
@@ -73,6 +83,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct DecodePlan {
   bool streamk = false;
   bool too_large = false;
+  bool grid_mfma = false;                // partition grid on the MFMA kernels (else the vector ones)
+  int head_split = 1;                    // balanced path: sub-groups of a large GQA group
   int ranges = 0, range_blocks = 0;      // balanced path
   int part_blocks = 0, nparts = 1;       // partition-grid path
   size_t off_part = 0, off_ml = 0, off_desc = 0, workspace_bytes = 0;
@@ -86,15 +98,20 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   DecodePlan pl;
   const int g = num_heads / num_kv_heads;
   const int64_t rows = (int64_t)num_seqs * num_kv_heads;
+  // balanced path: a large group's sub-groups are rows of their own
+  const int hs = mfma_shape ? head_split(g) : 1, gv = g / hs;
   // the unit of the split: 16-token tiles on the MFMA path, blocks otherwise
   const int unit = mfma_shape ? 16 : block_size;
   const int64_t part_units = partition_size > 0 ? std::max<int64_t>(1, partition_size / unit) : 0;
   const int64_t blocks_per_row = cap > 0 ? ceil_div(cap, unit) : 0;
-  const int64_t t_upper = rows * blocks_per_row;  // flat blocks, at most
+  const int64_t t_upper = rows * hs * blocks_per_row;  // flat blocks, at most
   // balanced ranges: the default count, or more when that keeps every range
-  // within the blocks a workgroup can stage (t_upper bounds the real total)
+  // within the blocks a workgroup can stage (t_upper bounds the real total).
+  // Rows of more than 8 query heads park so much in LDS that one workgroup
+  // fits per CU: half the ranges, so that they all run in one round.
+  const int64_t nr = gv > 8 ? pa::kStreamKRanges / 2 : pa::kStreamKRanges;
   const int64_t sk_ranges_default = std::max<int64_t>(
-      {1, std::min<int64_t>(pa::kStreamKRanges, t_upper), ceil_div(t_upper, pa::kStreamKTabCache)});
+      {1, std::min<int64_t>(nr, t_upper), ceil_div(t_upper, pa::kStreamKTabCache)});
   // The library's own split is always the balanced one on the MFMA path (its
   // merge shares a row cut into many pieces out over the row's ranges).  A
   // caller's fixed pieces take fixed-size ranges when they are few per row;
@@ -102,8 +119,9 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
   const bool fixed_ok = partition_size == 0 ||
                         (part_units <= pa::kStreamKTabCache &&
                          ceil_div(std::max<int64_t>(blocks_per_row, 1), part_units) <= kStreamKMaxPiecesPerRow);
-  if (mfma_shape && num_seqs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff && fixed_ok) {
+  if (mfma_shape && (int64_t)num_seqs * hs <= pa::kStreamKMaxSeqs && t_upper <= 0x7fffffff && fixed_ok) {
     pl.streamk = true;
+    pl.head_split = hs;
     if (partition_size > 0) {
       pl.range_blocks = (int)part_units;
       pl.ranges = (int)std::max<int64_t>(1, ceil_div(t_upper, pl.range_blocks));
@@ -111,8 +129,8 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
       pl.range_blocks = 0;
       pl.ranges = (int)sk_ranges_default;
     }
-    const size_t part = (size_t)pl.ranges * 2 * g * head_dim * sizeof(float);
-    const size_t ml = (size_t)pl.ranges * 2 * g * 2 * sizeof(float);
+    const size_t part = (size_t)pl.ranges * 2 * gv * head_dim * sizeof(float);
+    const size_t ml = (size_t)pl.ranges * 2 * gv * 2 * sizeof(float);
     pl.off_part = 0;
     pl.off_ml = align256(part);
     pl.off_desc = pl.off_ml + align256(ml);
@@ -128,10 +146,14 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads, int head_d
     pl.plan_bytes = pl.plan_off_desc + align256((size_t)pl.ranges * 4 * sizeof(int));
     return pl;
   }
-  const int64_t P = !mfma_shape && partition_size <= 0 ? vec_default_partition(rows, max_seq_len, block_size)
-                                                       : effective_partition(partition_size, block_size);
-  const int64_t pu = std::max<int64_t>(1, P / unit);  // units per partition
-  const int64_t nparts = cap > 0 ? ceil_div(blocks_per_row, pu) : 1;
+  // the partition grid: MFMA kernels up to 16 query heads per KV head,
+  // the vector kernels beyond
+  pl.grid_mfma = mfma_shape && g <= 16;
+  const int gunit = pl.grid_mfma ? 16 : block_size;
+  const int64_t P = !pl.grid_mfma && partition_size <= 0 ? vec_default_partition(rows, max_seq_len, block_size)
+                                                         : effective_partition(partition_size, block_size);
+  const int64_t pu = std::max<int64_t>(1, P / gunit);  // units per partition
+  const int64_t nparts = cap > 0 ? ceil_div(ceil_div(cap, gunit), pu) : 1;
   if (nparts > 0x7fffffff) {
     pl.too_large = true;
     return pl;
@@ -269,8 +291,7 @@ namespace {
 
 bool mfma_decode_shape(int32_t kv_dtype, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size) {
-  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && head_dim == 128 && pa::mfma_block_size(block_size) &&
-         num_heads / num_kv_heads <= 16;
+  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && head_dim == 128 && pa::mfma_block_size(block_size);
 }
 
 // The new token of every sequence for a decode step that also writes it:
@@ -299,8 +320,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   if (!scale_ok(scale)) return PA_ERR_SHAPE;  // the kernels scale after taking the max
   if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
   if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
-  if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size) && num_heads / num_kv_heads <= 16))
-    return PA_ERR_UNSUPPORTED;
+  if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size))) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
@@ -311,13 +331,15 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                                 cap, partition_size, mfma_shape);
   if (plan.too_large) return PA_ERR_UNSUPPORTED;
+  // FP8 caches have MFMA kernels only: a group above 16 needs the balanced path
+  if (fp8 && !plan.streamk && !plan.grid_mfma) return PA_ERR_UNSUPPORTED;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return PA_ERR_WORKSPACE;
   if (planned && plan.streamk && (!plan_buf || plan_bytes < plan.plan_bytes)) return PA_ERR_WORKSPACE;
   // the step's write: folded into the planned bf16 balanced kernels (the
   // main kernel reads the new rows in place of position L - 1, the merge
   // kernel writes them to their slots), otherwise written first
-  const bool fold = append && planned && plan.streamk && kv_dtype == PA_BF16;
+  const bool fold = append && planned && plan.streamk && kv_dtype == PA_BF16 && plan.head_split == 1;
   if (append) {
     if (!append->key || !append->value || !append->slot_mapping) return PA_ERR_NULL;
     if (!fold) {
@@ -352,6 +374,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
   p.num_blocks = num_blocks;
   p.max_len_cap = (int)cap;
   p.scale = scale;
+  p.head_split = plan.streamk ? plan.head_split : 1;
   char *ws = static_cast<char *>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.streamk) {
@@ -375,7 +398,7 @@ int decode_impl(void *out, int32_t out_dtype, const void *q, const void *k_cache
     }
     return launch_status(pa::launch_decode_streamk(p, s));
   }
-  p.tile_tokens = mfma_shape ? 16 : block_size;
+  p.tile_tokens = plan.grid_mfma ? 16 : block_size;
   p.part_blocks = plan.part_blocks;
   p.nparts_max = plan.nparts;
   p.ws_o = plan.workspace_bytes > 0 ? reinterpret_cast<float *>(ws + plan.off_part) : nullptr;
@@ -443,6 +466,7 @@ int paged_attn_decode_plan(void *plan_buf, size_t plan_bytes, int32_t kv_dtype, 
   p.block_size = block_size;
   p.num_blocks = num_blocks;
   p.max_len_cap = (int)cap;
+  p.head_split = plan.head_split;
   p.sk_ranges = plan.ranges;
   p.sk_range_blocks = plan.range_blocks;
   char *pb = static_cast<char *>(plan_buf);

@@ -52,6 +52,21 @@ __device__ __forceinline__ int ranges_used(int grid, int T, int R) {
   return R > 0 ? grid : max(1, min(grid, T));
 }
 
+// Rows are (sequence, KV head) pairs, or, for a GQA group of more than 16
+// query heads, (sub-group, KV head) pairs: each sequence then appears
+// head_split times in a row (same length, same table) and its copy sub
+// serves query heads sub * g .. sub * g + g - 1 of every group, g being the
+// sub-group size (heads per row).  seq_of maps a row's sequence index vb to
+// the caller's sequence, head0 gives the row's first query head.
+__device__ __forceinline__ int seq_of(const DecodeParams &p, int vb) {
+  return p.head_split > 1 ? vb / p.head_split : vb;
+}
+__device__ __forceinline__ int64_t head0(const DecodeParams &p, int vb, int kh, int g) {
+  if (p.head_split <= 1) return (int64_t)vb * p.num_heads + (int64_t)kh * g;
+  const int b = vb / p.head_split, sub = vb - b * p.head_split;
+  return (int64_t)b * p.num_heads + ((int64_t)kh * p.head_split + sub) * g;
+}
+
 __device__ __forceinline__ void store_value(void *out, int out_bf16, int64_t i, float v) {
   if (out_bf16)
     reinterpret_cast<__bf16 *>(out)[i] = (__bf16)v;
@@ -131,8 +146,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4, c = lane & 15;
-  const int B = p.num_seqs, Hkv = p.num_kv_heads;
-  const int g = p.num_heads / Hkv;
+  const int Hkv = p.num_kv_heads;
+  const int B = p.num_seqs * max(p.head_split, 1);       // sequences of rows (seq_of)
+  const int g = p.num_heads / Hkv / max(p.head_split, 1);  // query heads per row
   const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);  // this workgroup's range
   const int R = p.sk_range_blocks;
   if constexpr (MODE == kPlanned) TL_MAIN(0, tid == 0);
@@ -149,7 +165,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (B <= 64) {
       // one wave scans with cross-lane adds; a single barrier publishes it
       if (w == 0) {
-        int L = lane < B ? p.seq_lens[lane] : 0;
+        int L = lane < B ? p.seq_lens[seq_of(p, lane)] : 0;
         L = clamp_len(L, p.max_len_cap);
         const int v = (L + kBS - 1) / kBS;
         int incl = v;
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
       int local = 0;
       for (int b = b0; b < b1; ++b) {
-        int L = p.seq_lens[b];
+        int L = p.seq_lens[seq_of(p, b)];
         L = clamp_len(L, p.max_len_cap);
         s_len[b] = L;
         local += (L + kBS - 1) / kBS;
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int nb = s_pref[lo + 1] - s_pref[lo];
       const int j = rem - s_pref[lo];
       int e0, e1;
-      const bool ok = map.entries(p.block_tables + (int64_t)lo * p.max_blocks_per_seq, j,
+      const bool ok = map.entries(p.block_tables + (int64_t)seq_of(p, lo) * p.max_blocks_per_seq, j,
                                   (s_len[lo] + p.block_size - 1) / p.block_size, e0, e1);
       debug_report(!ok, kDbgBlockRange);
       const TileRows tr = map.rows(e0, e1, kh);
@@ -240,9 +256,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       int keep = 0;
       if (ok) {
         const int i0 = map.first_index(j), bsz = p.block_size;
-        const int32_t *tb = p.block_tables + (int64_t)lo * p.max_blocks_per_seq;
-        if (lo > 0 && i0 < (s_len[lo - 1] + bsz - 1) / bsz) keep |= tb[i0 - p.max_blocks_per_seq] == e0;
-        if (lo + 1 < B && i0 < (s_len[lo + 1] + bsz - 1) / bsz) keep |= tb[i0 + p.max_blocks_per_seq] == e0;
+        const int64_t mb = p.max_blocks_per_seq;
+        if (lo > 0 && i0 < (s_len[lo - 1] + bsz - 1) / bsz)
+          keep |= p.block_tables[seq_of(p, lo - 1) * mb + i0] == e0;
+        if (lo + 1 < B && i0 < (s_len[lo + 1] + bsz - 1) / bsz)
+          keep |= p.block_tables[seq_of(p, lo + 1) * mb + i0] == e0;
       }
       s_rows[pos - s] = ok ? int2{(int)(tr.lo >> 10), (int)(tr.hi >> 10)} : int2{-1, 0};
       s_prow[pos - s] = lo * Hkv + kh;
@@ -291,14 +309,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int k = 0; k < kSlotPer; ++k) {
         const int bi = tid + k * 64 * NW;
-        sv[k] = bi < B ? p.slot_mapping[bi] : -1;
+        sv[k] = bi < p.num_seqs ? p.slot_mapping[bi] : -1;  // (the folded write has one row per sequence)
       }
     }
     asm volatile("" ::: "memory");  // issue those loads before the header is tested
     if constexpr (APPEND) {
 #pragma unroll
       for (int k = 0; k < kSlotPer; ++k)
-        if (tid + k * 64 * NW < B) s_slot[tid + k * 64 * NW] = sv[k];
+        if (tid + k * 64 * NW < p.num_seqs) s_slot[tid + k * 64 * NW] = sv[k];
     }
     s = h.x;
     e = h.y;
@@ -366,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool ok = u.x >= 0;
     const bool need_q = lp < ls || s_prow[lp < le ? lp : le - 1] != row;  // uniform
     if (__builtin_amdgcn_readfirstlane((int)need_q))
-      F::load_q(sl.q, qbase + ((int64_t)b * p.num_heads + (int64_t)kh * g + c_ld) * kD, r);
+      F::load_q(sl.q, qbase + (head0(p, b, kh, g) + c_ld) * kD, r);
     sl.lim = ok ? s_ln[li].x : 0;
     // a masked tile reads the first rows of the cache
     const TileRows tr{(int64_t)max(u.x, 0) << 10, (int64_t)u.y << 10};
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (whole) {
         if (col_ok) {
           const float inv = lw > 0.f ? p.v_scale / lw : 0.f;
-          const int64_t orow = ((int64_t)b * p.num_heads + (int64_t)kh * g + c) * kD;
+          const int64_t orow = (head0(p, b, kh, g) + c) * kD;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -547,7 +565,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int nb = enb[h];
     const bool whole = rs >= s && rs + nb <= e;
     const int slot = rs <= s ? 0 : 1;
-    const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+    const int64_t out_row0 = head0(p, b, kh, g);
     // the run's members: the entries from h on with this row start (a bit
     // mask, uniform; empty entries may sit between members).  Most runs have
     // one member: a row that only touches one wave's share.
@@ -659,11 +677,13 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   // the same range numbering as the main kernel, so this workgroup runs on
   // the XCD that wrote range gi's pieces (and, but at XCD edges, gi - 1's)
   const int gi = (int)xcd_contiguous(blockIdx.x, gridDim.x);
-  const int g = p.num_heads / p.num_kv_heads;
+  const int hs = max(p.head_split, 1);
+  const int g = p.num_heads / p.num_kv_heads / hs;  // query heads per row
   const int gp = gi > 0 ? gi - 1 : 0;
   const int4 dsc = p.sk_desc[gi];
-  const int nrows = p.num_seqs * p.num_kv_heads;
-  const int len0 = gi < nrows ? p.seq_lens[gi / p.num_kv_heads] : 1;  // with the descriptor: one round trip
+  const int nrows = p.num_seqs * hs * p.num_kv_heads;
+  const int nreal = p.num_seqs * p.num_kv_heads;  // (sequence, KV head) rows: the folded write's
+  const int len0 = gi < nrows ? p.seq_lens[seq_of(p, gi / p.num_kv_heads)] : 1;  // with the descriptor: one round trip
   // speculative: (gp, slot 0), (gp, slot 1), (gi, slot 0) for both elements
   const int E = g * kD;  // output elements of a row
   float sm[3][kPer], sl[3][kPer], so[3][kPer];
@@ -685,7 +705,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   u32x4 wdat = {0u, 0u, 0u, 0u};
   const int wpart = threadIdx.x / (kD / 8), wch = threadIdx.x % (kD / 8);
   if constexpr (APPEND) {
-    if (gi < nrows && threadIdx.x < 2 * (kD / 8)) {
+    if (gi < nreal && threadIdx.x < 2 * (kD / 8)) {
       wsm = p.slot_mapping[gi / p.num_kv_heads];
       wdat = ld16(reinterpret_cast<const uint16_t *>(wpart ? p.new_v : p.new_k) + (int64_t)gi * kD + 8 * wch);
     }
@@ -694,17 +714,17 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   // rows with no tokens (no piece, no range) get zeros, spread over the
   // workgroups: row gi, gi + grid, ...
   for (int zr = gi; zr < nrows; zr += (int)gridDim.x) {
-    if (clamp_len(zr == gi ? len0 : p.seq_lens[zr / p.num_kv_heads], p.max_len_cap) != 0) continue;
+    if (clamp_len(zr == gi ? len0 : p.seq_lens[seq_of(p, zr / p.num_kv_heads)], p.max_len_cap) != 0) continue;
     const int b = zr / p.num_kv_heads, kh = zr - b * p.num_kv_heads;
     for (int idx = threadIdx.x; idx < g * kD; idx += blockDim.x)
-      store_value(p.out, p.out_bf16, ((int64_t)b * p.num_heads + (int64_t)kh * g) * kD + idx, 0.f);
+      store_value(p.out, p.out_bf16, head0(p, b, kh, g) * kD + idx, 0.f);
   }
   if constexpr (APPEND) {
     // rows gi, gi + grid, ...: 16-byte chunks, threads 0 .. 15 the K row,
     // 16 .. 31 the V row (block sizes of this path are powers of two)
     const int lb = __builtin_ctz((unsigned)p.block_size);
     const int64_t nslots = (int64_t)p.num_blocks << lb;
-    for (int wr = gi; wr < nrows; wr += (int)gridDim.x) {
+    for (int wr = gi; wr < nreal; wr += (int)gridDim.x) {
       if (threadIdx.x >= 2 * (kD / 8)) break;
       const int kh = wr % p.num_kv_heads;
       int64_t sm = wsm;
@@ -730,7 +750,7 @@ __global__ __launch_bounds__(1024) void decode_streamk_merge_kernel(DecodeParams
   const int g_first = min(max(dsc.y, 0), gi), s_first = dsc.z & 1;
   const int g_last = min(max(dsc.w, gi), (int)gridDim.x - 1), nc = g_last - g_first + 1;
   const int b = row / p.num_kv_heads, kh = row - b * p.num_kv_heads;
-  const int64_t out_row0 = (int64_t)b * p.num_heads + (int64_t)kh * g;
+  const int64_t out_row0 = head0(p, b, kh, g);
   auto piece = [&](int k, int cc) -> int64_t {  // (range, slot, column) index of piece k
     return ((int64_t)(g_first + k) * 2 + (k == 0 ? s_first : 0)) * g + cc;
   };
@@ -868,7 +888,7 @@ hipError_t launch_decode_streamk_plan(const DecodeParams &p, hipStream_t stream)
 }
 
 hipError_t launch_decode_streamk(const DecodeParams &p, hipStream_t stream) {
-  const int g = p.num_heads / p.num_kv_heads;
+  const int g = p.num_heads / p.num_kv_heads / std::max(p.head_split, 1);  // query heads per row
   const size_t park = (size_t)PA_DECODE_WAVES * 2 * g * (kD + 2) * sizeof(float);
   const dim3 grid(p.sk_ranges), block(64 * PA_DECODE_WAVES);
   const bool planned = p.plan_hdr != nullptr;

@@ -66,6 +66,8 @@ struct DecodeParams {
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int max_len_cap;         // min(max_seq_len, max_blocks_per_seq * block_size)
   float scale;
+  int head_split;          // balanced path: hs >= 1 sub-groups per GQA group, each g / hs heads,
+                           //   each its own row; the rows of sequence b are those of b * hs .. + hs - 1
   int tile_tokens;         // tokens per unit of part_blocks / the flat space: 16 on the MFMA
                            // path (16-token tiles), block_size on the vector path
   int part_blocks;         // units per split-K partition

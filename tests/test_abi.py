@@ -283,7 +283,12 @@ def test_fp8_validation(pa):
     assert dec(a5=-1.0) == PA_ERR_SHAPE
     assert dec(a13=64) == PA_ERR_UNSUPPORTED                  # FP8 serves head_dim 128 only
     assert dec(a14=4) == PA_ERR_UNSUPPORTED                   # and the MFMA block sizes
-    assert dec(a11=136, a12=8) == PA_ERR_UNSUPPORTED          # and groups of at most 16
+    # a group of 17 runs as 17 one-head sub-groups on the balanced split (so this call, without its
+    # workspace, is refused for that); with a caller's 16-token pieces on 8K-token rows (512 per row, the
+    # partition grid) it has no FP8 kernel
+    assert dec(a11=136, a12=8) == PA_ERR_WORKSPACE
+    assert dec(a11=136, a12=8, a8=512, a16=8192, a18=16) == PA_ERR_UNSUPPORTED
+    assert dec(a11=128, a12=8, a8=512, a16=8192, a18=16) == PA_ERR_WORKSPACE  # group 16: the MFMA grid
     assert dec(a1=2) == PA_ERR_UNSUPPORTED                    # out cannot be FP8
     assert dec(a2=N) == PA_ERR_NULL
     assert dec(a10=0) == PA_OK

@@ -92,6 +92,7 @@ CASES = [
     ("bf16", 64, 64, 8),
     ("fp8", 16, 32, 8),
     ("f32", 16, 8, 2),
+    ("bf16", 16, 32, 1),    # a group of 32 (sub-groups): written first, then attended
 ]
 
 

@@ -98,6 +98,8 @@ def test_kv_cache_write_fp8_exact_ties(pa):
 FP8_DECODE_CASES = [
     # Hq, Hkv, bs, out, partition
     (32, 8, 16, "f32", 0),
+    (32, 1, 16, "f32", 0),      # a group of 32: two sub-groups of 16 heads
+    (48, 2, 32, "bf16", 0),     # groups of 24: two sub-groups of 12
     (64, 8, 16, "f32", 512),
     (16, 16, 16, "f32", 64),
     (32, 2, 16, "f32", 128),

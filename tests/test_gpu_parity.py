@@ -485,6 +485,24 @@ def test_decode_long_rows_shared_merge(pa, lens, Hq, Hkv, bs, part):
     assert torch.equal(first, again)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 1), (96, 2), (48, 2), (40, 2), (17, 1), (64, 1)])
+def test_decode_large_groups(pa, Hq, Hkv):
+    """GQA groups above 16 query heads (32, 48, 24, 20, 17, 64): the balanced decode serves each as sub-groups
+    of at most 16 heads (16, 16, 12, 10, 1 and 16 heads), each its own row over the same K/V; with a caller's
+    pieces of more than 16 per row the vector kernels serve the group.  Every output matches the oracle."""
+    lens = [0, 1, 17, 300, 1000, 2049, 5]
+    lay, q, k, v = rand_problem(lens, Hq, Hkv, 128, 16, "bf16", seed=Hq + Hkv)
+    ref = oracle.paged_decode(q, k, v, lay.block_tables, lay.seq_lens, 0.09)
+    for part, odt in ((0, "f32"), (256, "bf16"), (16, "f32")):
+        out = out_to_f64(gpu_decode(pa, lay, q, k, v, 0.09, odt, part))
+        if odt == "bf16":
+            excess = np.abs(out - ref) - (TOL["bf16"] + np.abs(ref) * 2.0 ** -8)
+            assert excess.max() <= 0, (part, excess.max())
+        else:
+            assert max_err(out, ref) <= TOL["bf16"], (part, max_err(out, ref))
+        assert np.all(out[0] == 0)
+
+
 def test_decode_workspace_reuse_and_garbage(pa):
     """Stale or garbage workspace contents are ignored: every piece the merge reads was written earlier in
     the same call, so repeated calls on one workspace filled with garbage all match the oracle."""

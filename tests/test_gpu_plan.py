@@ -45,6 +45,8 @@ PLAN_CASES = [
     ("few_long", 64, 8, 16, "bf16", 0, "f32"),       # rows of dozens of pieces: the shared merge
     ("few_long", 8, 1, 16, "fp8", 0, "bf16"),
     ("few_long", 8, 8, 32, "bf16", 0, "f32"),        # group 1
+    ("mixed", 32, 1, 16, "bf16", 0, "f32"),          # a group of 32: two sub-groups of 16 heads
+    ("mixed", 96, 2, 16, "fp8", 0, "bf16"),          # groups of 48: three sub-groups
 ]
 
 
