@@ -53,13 +53,13 @@
  *   - The swap calls also take one HOST pointer (stated where it appears).
  *   - Supported shapes.  Attention calls: head_dim in {64, 128}, any
  *     block_size >= 1, num_heads % num_kv_heads == 0 (the MFMA kernels serve
- *     bf16 KV with head_dim 128, block_size in {8, 16, 32, 64, 128} and a GQA
- *     group of at most 16 (prefill: a divisor of 16), walking each sequence
- *     in 16-token tiles; decode serves a larger group there too, as
- *     sub-groups of at most 16 heads, when its balanced split takes the call
- *     (num_seqs times the sub-group count at most 2048, and not a caller's
- *     partition_size of more than 16 pieces per row); other supported shapes
- *     run on plain vector kernels),
+ *     bf16 KV with head_dim 128 and block_size in {8, 16, 32, 64, 128},
+ *     walking each sequence in 16-token tiles: prefill with any GQA group
+ *     (as sub-groups whose size divides 16), decode with a group of at most
+ *     16, or a larger one as sub-groups of at most 16 heads when its
+ *     balanced split takes the call (num_seqs times the sub-group count at
+ *     most 2048, and not a caller's partition_size of more than 16 pieces
+ *     per row); other supported shapes run on plain vector kernels),
  *     one physical block of num_kv_heads * block_size * head_dim elements
  *     below 2^31 and a whole cache (num_blocks such blocks) below 2^41.
  *     kv_cache_write, block_copy and the swap calls: any block_size >= 1 and any head_dim whose row is a
@@ -264,9 +264,9 @@ PA_EXPORT int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void 
  *     value(code) (every E4M3 value is a bf16 value), with k_scale folded into
  *     the score scale and v_scale into the final normalisation;
  *   - the FP8 attention calls serve head_dim 128, block_size in
- *     {8, 16, 32, 64, 128} and the GQA groups of the MFMA kernels above (at
- *     most 16, or larger where decode takes the balanced split; prefill: a
- *     divisor of 16); other shapes return PA_ERR_UNSUPPORTED.
+ *     {8, 16, 32, 64, 128} and the GQA groups of the MFMA kernels above
+ *     (prefill: any; decode: at most 16, or larger where it takes the
+ *     balanced split); other shapes return PA_ERR_UNSUPPORTED.
  *
  * kv_cache_write_fp8 -- kv_cache_write into FP8 caches: key and value rows
  * ([num_tokens][num_kv_heads][head_dim], src_dtype PA_F32 or PA_BF16) are

@@ -536,8 +536,12 @@ int prefill_impl(void *out, int32_t out_dtype, const void *q, const void *k_cach
   if (fp8 && !scale_ok(k_scale)) return PA_ERR_SHAPE;
   if (fp8 && !scale_ok(v_scale)) return PA_ERR_SHAPE;
   const int g = num_heads / num_kv_heads;
-  if (fp8 && !(head_dim == 128 && pa::mfma_block_size(block_size) && g <= 16 && 16 % g == 0))
-    return PA_ERR_UNSUPPORTED;
+  const bool mfma = (kv_dtype == PA_BF16 || fp8) && head_dim == 128 && pa::mfma_block_size(block_size);
+  if (fp8 && !mfma) return PA_ERR_UNSUPPORTED;
+  // MFMA kernels: a column group is 16 / gs tokens x gs heads, gs the largest
+  // power of two up to 16 that divides g; g / gs sub-groups per KV head
+  int gs = 16;
+  while (g % gs != 0) gs >>= 1;
   if (max_query_len < 0 || num_query_tokens < 0) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens)
@@ -567,6 +571,7 @@ int prefill_impl(void *out, int32_t out_dtype, const void *q, const void *k_cach
   p.num_query_tokens = num_query_tokens;
   p.max_len_cap = (int)cap;
   p.scale = scale;
+  p.head_split = mfma ? g / gs : 1;
   return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -117,6 +117,8 @@ struct PrefillParams {
   int num_query_tokens;    // rows of q / out; rows at or beyond are never touched
   int max_len_cap;
   float scale;
+  int head_split;          // MFMA kernels: hs sub-groups per GQA group, each g / hs heads (a
+                           //   divisor of 16) served as if by a KV head of its own
 };
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);

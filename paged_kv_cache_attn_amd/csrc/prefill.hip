@@ -117,9 +117,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // built from them) in scalar registers
   const unsigned grp = __builtin_amdgcn_readfirstlane(set * kset + off % nset);
   const int tile = __builtin_amdgcn_readfirstlane(ntiles - 1 - (int)(off / nset));
-  const int kh = (int)(grp % (unsigned)p.num_kv_heads);
-  const int b = (int)(grp / (unsigned)p.num_kv_heads);
-  const int g = p.num_heads / p.num_kv_heads;
+  // a group is (sequence, KV head, sub-group): the query heads of a KV head
+  // are served hs at a time (hs = 1 unless the group size does not divide
+  // 16), the sub-groups of one KV head next to each other
+  const int hs = max(p.head_split, 1);
+  const unsigned nkv = (unsigned)(p.num_kv_heads * hs);
+  const int kv = (int)(grp % nkv);
+  const int b = (int)(grp / nkv);
+  const int kh = kv / hs;
+  const int g = p.num_heads / p.num_kv_heads / hs;  // query heads per column group row
+  const int64_t hbase = (int64_t)kh * (g * hs) + (int64_t)(kv - kh * hs) * g;  // the sub-group's first head
   const int tpgrp = 16 / g;              // chunk tokens per column group
   const int tpw = CG * tpgrp;            // per wave
   const int tpg = NW * tpw;              // per workgroup
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // (clamped to the query rows, whatever query_start_loc holds)
     const int64_t row_ld = min((int64_t)q0 + (col_ok[cg] ? qi : last_qi_wg), (int64_t)p.num_query_tokens - 1);
     load_q_operand_d128(qb[cg],
-                        reinterpret_cast<const uint16_t *>(p.q) + (row_ld * p.num_heads + (int64_t)kh * g + hh) * D,
+                        reinterpret_cast<const uint16_t *>(p.q) + (row_ld * p.num_heads + hbase + hh) * D,
                         r);
   }
 
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l = row_sum4(st[cg].l);
     const float inv = l > 0.f ? p.v_scale / l : 0.f;
     const int qi = tile * tpg + w * tpw + cg * tpgrp + ti;
-    const int64_t row = ((int64_t)q0 + qi) * p.num_heads + (int64_t)kh * g + hh;
+    const int64_t row = ((int64_t)q0 + qi) * p.num_heads + hbase + hh;
     if (!col_ok[cg]) continue;
     if (p.out_bf16) {
       uint16_t *o = reinterpret_cast<uint16_t *>(p.out) + row * D + 4 * r;
@@ -598,14 +605,15 @@ PA_DEBUG_WORD_ACCESSOR(debug_word_prefill)
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_query_len == 0) return hipSuccess;
-  const int g = p.num_heads / p.num_kv_heads;
-  const bool mfma =
-      (p.kv_bf16 || p.kv_fp8) && p.head_dim == 128 && mfma_block_size(p.block_size) && g <= 16 && (16 % g) == 0;
+  const int hs = max(p.head_split, 1);
+  const int g = p.num_heads / p.num_kv_heads / hs;  // heads per sub-group
+  const bool mfma = (p.kv_bf16 || p.kv_fp8) && p.head_dim == 128 && mfma_block_size(p.block_size);
   if (mfma) {
+    if (g * hs * p.num_kv_heads != p.num_heads || g > 16 || 16 % g != 0) return hipErrorInvalidValue;
     constexpr int NW = PA_PREFILL_WAVES, CG = PA_PREFILL_GROUPS;
     const int tpg = NW * CG * (16 / g);
     const int64_t ntiles = (p.max_query_len + tpg - 1) / tpg;
-    const int64_t items = ntiles * p.num_kv_heads * p.num_seqs;
+    const int64_t items = ntiles * p.num_kv_heads * hs * p.num_seqs;
     if (items * 64 * NW > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)items), block(64 * NW);
 #define PA_PREFILL_LAUNCH(BSZ, FP8)                                                                   \

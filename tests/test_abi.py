@@ -295,7 +295,8 @@ def test_fp8_validation(pa):
     pf = pa.lib.paged_attn_prefill_chunk_fp8
     # out, out_dtype, q, k, v, ks, vs, bt, maxblk, qsl, sl, B, Tq, Hq, Hkv, D, bs, NB, maxq, maxlen, scale, stream
     pbase = [P, 0, P, P, P, 0.5, 0.5, P, 16, P, P, 4, 8, 24, 8, 128, 16, 64, 4, 256, 0.1, N]
-    assert pf(*pbase) == PA_ERR_UNSUPPORTED                   # group 3 does not divide 16
+    assert pf(*pbase[:15], 64, *pbase[16:]) == PA_ERR_UNSUPPORTED   # FP8 serves head_dim 128 only
+    assert pf(*pbase[:16], 4, *pbase[17:]) == PA_ERR_UNSUPPORTED    # and the MFMA block sizes
     pbase[13] = 32
     assert pf(*pbase[:6], 0.0, *pbase[7:]) == PA_ERR_SHAPE
     assert pf(*pbase[:11], 0, *pbase[12:]) == PA_OK

@@ -156,7 +156,7 @@ def test_decode_fp8_equals_bf16_on_decoded_values(pa):
     assert max_err(out_to_f64(out_f), out_to_f64(out_b)) <= 1e-5
 
 
-@pytest.mark.parametrize("Hq,Hkv,bs", [(32, 8, 16), (64, 8, 16), (8, 8, 32), (32, 8, 8)])
+@pytest.mark.parametrize("Hq,Hkv,bs", [(32, 8, 16), (64, 8, 16), (8, 8, 32), (32, 8, 8), (24, 8, 16), (32, 1, 16)])
 def test_prefill_fp8_parity(pa, Hq, Hkv, bs):
     torch = torch_mod()
     total = [40, 64, 17, 5, 300, 1, 129]

@@ -352,7 +352,11 @@ PREFILL_CASES = [
     ("bf16", 128, 64, 8),     # group 8
     ("bf16", 128, 8, 8),      # group 1
     ("f32", 64, 8, 2),        # vector path
-    ("bf16", 128, 24, 8),     # group 3: vector path
+    ("bf16", 128, 24, 8),     # group 3: three one-head sub-groups on the MFMA kernel
+    ("bf16", 128, 48, 4),     # group 12: three sub-groups of 4 heads
+    ("bf16", 128, 32, 1),     # group 32: two sub-groups of 16 heads
+    ("bf16", 128, 40, 8),     # group 5
+    ("bf16", 64, 24, 8),      # head size 64, group 3: vector path
 ]
 
 
