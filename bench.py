@@ -741,16 +741,24 @@ def bench_shared_prefix(args, torch, pa, W, w, layers):
     unique = w.extra["unique_blocks"] * w.block_size * Hkv * D * w.elem_bytes * 2
     copy = None
     if len(copies):
+        # the layers' copies in one HIP graph, replayed (a Python launch loop
+        # would time the host, not the copies)
         for _ in range(3):
             pa.block_copy(K[0], V[0], pairs)
         torch.cuda.synchronize()
+        gcp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gcp):
+            for l in range(layers):
+                pa.block_copy(K[l], V[l], pairs)
+        gcp.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for l in range(layers):
-            pa.block_copy(K[l], V[l], pairs)
+        for _ in range(args.steps):
+            gcp.replay()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / layers
+        us = e0.elapsed_time(e1) * 1e3 / (layers * args.steps)
         cbytes = len(copies) * 2 * 2 * Hkv * w.block_size * D * w.elem_bytes  # K and V, read + write
         copy = {"pairs": len(copies), "us_per_call": round(us, 3), "GBs": round(cbytes / us / 1e3, 1)}
     if pre is not None:

@@ -613,8 +613,8 @@ int block_copy(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_p
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
-  if ((int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype) / 16 > 0x7fffffff)
-    return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype) / 16 > 0x7fff0000)
+    return PA_ERR_UNSUPPORTED;  // chunk indexes (plus a slice) stay within int
   return launch_status(pa::launch_block_copy(k_cache, v_cache, pairs, num_pairs, num_blocks,
                                              num_kv_heads, block_size, head_dim, elem_bytes(dtype),
                                              static_cast<hipStream_t>(stream)));

@@ -274,7 +274,7 @@ hipError_t launch_block_copy(void *k_cache, void *v_cache, const int64_t *pairs,
                              int num_blocks, int num_kv_heads, int block_size, int head_dim,
                              int elem_bytes, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
-  const int block_chunks = num_kv_heads * block_size * head_dim * elem_bytes / 16;
+  const int block_chunks = (int)((int64_t)num_kv_heads * block_size * head_dim * elem_bytes / 16);
 #if PAGED_ATTN_DEBUG
   hipLaunchKernelGGL(debug_pair_conflicts_kernel, dim3((num_pairs + 255) / 256), dim3(256), 0, stream, pairs,
                      num_pairs);

@@ -72,9 +72,14 @@ def test_kv_cache_write_bit_exact(pa, dtype, D, bs):
     assert np.array_equal(to_host(vg), vc)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_block_copy_bit_exact(pa, dtype):
-    NB, Hkv, bs, D = 40, 8, 16, 128
+@pytest.mark.parametrize("dtype,Hkv,bs,D", [
+    ("bf16", 8, 16, 128),     # 2048 16-byte chunks per block: two rounds of 4 per thread
+    ("f32", 8, 16, 128),      # four rounds
+    ("bf16", 5, 32, 128),     # 2560 chunks: two rounds and a tail of 512
+    ("f32", 1, 8, 64),        # 128 chunks: the tail loop alone, half the threads idle
+])
+def test_block_copy_bit_exact(pa, dtype, Hkv, bs, D):
+    NB = 40
     kc = W.host_values((NB, Hkv, bs, D), 1.0, 5, dtype)
     vc = W.host_values((NB, Hkv, bs, D), 1.0, 6, dtype)
     pairs = np.array([[1, 30], [2, 31], [7, 7], [9, 33], [0, 39], [12, NB + 3]], np.int64)
