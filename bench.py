@@ -101,6 +101,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode",
                     choices=["llama8b_decode", "tiny_decode", "llama8b_decode_f32", "llama70b_long", "llama8b_decode_fp8", "llama70b_long_fp8",
+                             "llama70b_one_long",
                              "chunked_prefill_fp8", "shared_prefix", "shared_prefix_cow",
                              "chunked_prefill", "block_size_sweep", "swap", "mixed_decode",
                              "copy_calibration", "llama8b_decode_timeline", "llama70b_long_timeline"])
@@ -1088,8 +1089,8 @@ def main():
         layers = args.layers or 32
         part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part)
-    elif args.workload in ("llama70b_long", "llama70b_long_fp8"):
-        w = W.llama70b_long(block_size=args.block_size)
+    elif args.workload in ("llama70b_long", "llama70b_long_fp8", "llama70b_one_long"):
+        w = W.llama70b_long(block_size=args.block_size) if args.workload != "llama70b_one_long" else W.llama70b_one_long()
         layers = args.layers or 4
         part = 0 if args.partition < 0 else args.partition
         res = bench_decode(args, torch, pa, W, w, layers, part, fp8=fp8)

@@ -11,6 +11,8 @@
                      copy-on-write.
   llama70b_long      Llama-3.1-70B-shaped layer (Hq 64, Hkv 8), 8 sequences of
                      32768 tokens, split-K over 512-token partitions.
+  llama70b_one_long  the same layer, one sequence of 131072 tokens: eight rows
+                     cut into dozens of pieces each.
   chunked_prefill    16 sequences, 1024 cached tokens + a 512-token chunk.
 
 Length model: the pages' lecture simulators use ShareGPT-like truncated
@@ -144,6 +146,13 @@ def llama70b_long(batch: int = 8, seq_len: int = 32768, seed: int = 4, block_siz
     lay = build_paged_layout([seq_len] * batch, block_size, seed=seed + 1000, pool_factor=1.0)
     name = "llama70b_long_bf16" + ("" if block_size == 16 else "_bs%d" % block_size)
     return DecodeWorkload(name, lay, 64, 8, 128, "bf16", 1.0, seed=seed, partition_size=512)
+
+
+def llama70b_one_long(seq_len: int = 131072, seed: int = 6) -> DecodeWorkload:
+    """One long request alone: a single sequence, so each of the 8 (sequence, KV head) rows spans many of
+    the split's pieces."""
+    lay = build_paged_layout([seq_len], 16, seed=seed + 1000, pool_factor=1.0)
+    return DecodeWorkload("llama70b_one_long_bf16", lay, 64, 8, 128, "bf16", 1.0, seed=seed, partition_size=512)
 
 
 def shared_prefix(prompts: int = 16, prompt_len: int = 512, samples: int = 8, max_private: int = 256,
