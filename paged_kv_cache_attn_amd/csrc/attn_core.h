@@ -367,19 +367,23 @@ struct MfmaAttnState {
 };
 
 // Prefill variant: two 16-token blocks at a time, so the PV product can use
-// the full-rate v_mfma_f32_16x16x32_bf16 (K = 32 keys).  For a lane the 8
-// contraction indices k = 8r .. 8r+7 stand for keys 4r..4r+3 of block A and
-// 4r..4r+3 of block B; the P^T operand (from the two QK outputs) and the
-// V^T operand use the same order.  The V^T operand of output dims
-// 16t .. 16t+15 arrives ready-made (vt[t], from LDS transpose reads): lane
-// (r, c) holds V_A[4r..4r+3][16t + c] then V_B[4r..4r+3][16t + c].  So
+// the full-rate 16x16x32 MFMA (K = 32 keys).  For a lane the 8 contraction
+// indices k = 8r .. 8r+7 stand for keys 4r..4r+3 of block A and 4r..4r+3 of
+// block B; the P^T operand (from the two QK outputs) and the V^T operand use
+// the same order.  The V^T operand of output dims 16t .. 16t+15 arrives
+// ready-made (vt[t], from LDS transpose reads): lane (r, c) holds
+// V_A[4r..4r+3][16t + c] then V_B[4r..4r+3][16t + c].  So
 //   acc[t][i] = O[column c][dim 16t + 4r + i].
+// The PV product runs in fp16 (v_mfma_f32_16x16x32_f16): V is held as fp16
+// in LDS (widened from the cache on its way there) and each weight is
+// rounded to fp16 once, a relative error of at most 2^-11 per weight; the
+// sum l is taken from the unrounded fp32 weights.
 // The output is rescaled only when a column's running max grows by more than
 // 2^kLazyRescale, so most pairs skip the 32-register rescale; weights can
-// then exceed 1 (by at most that factor), which fp32 sums and the bf16
-// hi + lo split carry without loss.  Scores stay unscaled until the exponent:
-// m is kept in log2 units and each weight is exp2(s * sl2 - m) with one fma
-// (scaling by sl2 > 0 commutes with the max).
+// then exceed 1 (by at most that factor), which fp32 sums and fp16 carry.
+// Scores stay unscaled until the exponent: m is kept in log2 units and each
+// weight is exp2(s * sl2 - m) with one fma (scaling by sl2 > 0 commutes with
+// the max).
 
 struct MfmaAttnPairState {
   float m;
@@ -419,26 +423,20 @@ struct MfmaAttnPairState {
     raise_lazy_max(mx * sl2, m, nm, l, acc);
   }
 
-  // The weights exp2(x * sl2 - m) as bf16 hi + lo operand parts; adds them to l.
-  __device__ __forceinline__ void weights(const float x[8], float sl2, bf16x8 &pb_hi, bf16x8 &pb_lo) {
+  // The weights exp2(x * sl2 - m) as the fp16 operand; adds them to l.
+  __device__ __forceinline__ void weights(const float x[8], float sl2, f16x8 &pb) {
     float e[8];
 #pragma unroll
     for (int v = 0; v < 8; ++v) e[v] = fast_exp2(__builtin_fmaf(x[v], sl2, nm));
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) split_bf16x2(e[2 * u], e[2 * u + 1], hi[u], lo[u]);
     l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    pb_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    pb_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    pb = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3]), pack_f16x2(e[4], e[5]),
+                                         pack_f16x2(e[6], e[7])});
   }
 
-  // O^T += V^T P^T for the eight 16-dim tiles, hi part then lo part.
-  __device__ __forceinline__ void pv(const bf16x8 vt[8], const bf16x8 &pb_hi, const bf16x8 &pb_lo) {
+  // O^T += V^T P^T for the eight 16-dim tiles.
+  __device__ __forceinline__ void pv(const f16x8 vt[8], const f16x8 &pb) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc[t] = mfma_16x16x32_bf16(vt[t], pb_hi, acc[t]);
-      acc[t] = mfma_16x16x32_bf16(vt[t], pb_lo, acc[t]);
-    }
+    for (int t = 0; t < 8; ++t) acc[t] = mfma_16x16x32_f16(vt[t], pb, acc[t]);
   }
 
   // One pair of blocks for this lane's column: vt are the V^T operands.  When
@@ -446,7 +444,7 @@ struct MfmaAttnPairState {
   // visible to every column of the wave), keys of A at or past lim_a and keys
   // of B at or past lim_b are masked for this lane's column.
   __device__ __forceinline__ void step(const bf16x8 qb[4], const u32x4 ka[4], const u32x4 kb[4],
-                                       const bf16x8 vt[8], int tok0, int lim_a, int lim_b, bool mask,
+                                       const f16x8 vt[8], int tok0, int lim_a, int lim_b, bool mask,
                                        float sl2, int r) {
     float x[8];
     scores(qb, ka, kb, x);
@@ -459,9 +457,9 @@ struct MfmaAttnPairState {
       }
     }
     raise_max(x, sl2);
-    bf16x8 pb_hi, pb_lo;
-    weights(x, sl2, pb_hi, pb_lo);
-    pv(vt, pb_hi, pb_lo);
+    f16x8 pb;
+    weights(x, sl2, pb);
+    pv(vt, pb);
   }
 };
 
@@ -476,7 +474,7 @@ struct MfmaAttnPairState {
 template <class LoadV>
 __device__ __forceinline__ void pair_step_x2(MfmaAttnPairState &s0, MfmaAttnPairState &s1, const bf16x8 q0[4],
                                              const bf16x8 q1[4], const u32x4 ka[4], const u32x4 kb[4],
-                                             LoadV &&load_v, const bf16x8 vt[8], int tok0, int lim_a0, int lim_b0,
+                                             LoadV &&load_v, const f16x8 vt[8], int tok0, int lim_a0, int lim_b0,
                                              bool mask0, int lim_a1, int lim_b1, bool mask1, float sl2, int r) {
   float x0[8], x1[8];
   MfmaAttnPairState::scores(q0, ka, kb, x0);
@@ -499,11 +497,11 @@ __device__ __forceinline__ void pair_step_x2(MfmaAttnPairState &s0, MfmaAttnPair
   }
   s0.raise_max(x0, sl2);
   s1.raise_max(x1, sl2);
-  bf16x8 h0, l0, h1, l1;
-  s0.weights(x0, sl2, h0, l0);
-  s0.pv(vt, h0, l0);
-  s1.weights(x1, sl2, h1, l1);
-  s1.pv(vt, h1, l1);
+  f16x8 p0, p1;
+  s0.weights(x0, sl2, p0);
+  s0.pv(vt, p0);
+  s1.weights(x1, sl2, p1);
+  s1.pv(vt, p1);
 }
 
 }  // namespace pa

@@ -21,6 +21,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -35,6 +37,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Round-to-nearest-even fp32 -> fp16 of two values, packed lo | hi << 16
+// (v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 p = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// Two packed bf16 to two packed fp16.  Exact for magnitudes in fp16's normal
+// range [2^-14, 65504] (8 significant bits fit in 11); smaller magnitudes
+// land on fp16's subnormal grid (an absolute error below 2^-25), larger ones
+// overflow to infinity.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -123,6 +140,14 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// vm_wait<N> that also waits for every LDS (and scalar-memory) operation of
+// this wave, so LDS stores issued before it are done when a barrier follows.
+template <int N>
+__device__ __forceinline__ void vm_lgkm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
+}
+
 // All waves of the workgroup meet; the compiler moves no memory access across
 // it.  Unlike __syncthreads it waits for none of this wave's loads, so loads
 // into LDS stages that are not read yet stay in flight.
@@ -135,6 +160,11 @@ __device__ __forceinline__ void workgroup_barrier() {
 __device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
                                                       const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_16x16x32_f16(const f16x8 &a, const f16x8 &b,
+                                                     const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ floatx4 mfma_16x16x16_bf16(const u32x2 &a, const u32x2 &b,
@@ -221,6 +251,16 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t a, uint32_t b) {
   return u32x4{fp8x2_to_bf16x2<false>(a), fp8x2_to_bf16x2<true>(a), fp8x2_to_bf16x2<false>(b),
                fp8x2_to_bf16x2<true>(b)};
+}
+// The same eight codes to eight fp16, exactly: every E4M3 value (at most 448
+// in magnitude, at least 2^-9 apart from zero) is an fp16 value.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
+}
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t a, uint32_t b) {
+  return u32x4{fp8x2_to_f16x2<false>(a), fp8x2_to_f16x2<true>(a), fp8x2_to_f16x2<false>(b),
+               fp8x2_to_f16x2<true>(b)};
 }
 // fp32 -> code, nearest with ties to even and saturation at +-448: the clamp
 // supplies the saturation (v_cvt_pk_fp8_f32 rounds to nearest-even and turns

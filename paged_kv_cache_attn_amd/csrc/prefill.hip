@@ -77,9 +77,14 @@ __device__ __forceinline__ void store_out(void *out, int out_bf16, int64_t idx, 
 // ceil(max_query_len / (NW * CG * 16 / g)).  The block size BSZ is a template
 // argument so the table walk folds to constants for each supported size.
 //
+// V is held in LDS as fp16 for the fp16 PV product: bf16 caches load a pair's
+// V tiles as they are and each lane converts the slots it loaded in place,
+// one pair ahead of their use; FP8 caches widen on the way in.
+//
 // FP8 (E4M3) caches: a pair is 512 16-byte chunks in HBM instead of 1024;
-// each chunk is expanded to bf16 (exactly) on its way into LDS, so the LDS
-// layout and everything after it are those of the bf16 cache.  k_scale is
+// each chunk is expanded on its way into LDS (K to bf16, V to fp16, both
+// exactly), so the LDS layout and everything after it are those of the bf16
+// cache.  k_scale is
 // folded into the score scale and v_scale into the final normalisation.
 template <int NW, int CG, int BSZ, bool FP8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_d128_kernel(
@@ -277,15 +282,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int kind = u >> kTileShift, q = u & (kTileChunks - 1);
       uint8_t *tb = stage_mem(stage) + kind * kTile;
       if (FP8) {
-        // 16 codes = bf16 chunks 2 kc8 and 2 kc8 + 1 of row t
+        // 16 codes = 16-bit chunks 2 kc8 and 2 kc8 + 1 of row t (K as bf16,
+        // V as fp16: both exact)
         const int t = q >> 3, kc8 = q & 7;
-        *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, t, 2 * kc8)) = fp8x8_to_bf16x8(regs[k][0], regs[k][1]);
-        *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, t, 2 * kc8 + 1)) =
-            fp8x8_to_bf16x8(regs[k][2], regs[k][3]);
+        const bool is_v = kind & 1;
+        *reinterpret_cast<u32x4 *>(tb + lds_off(is_v, t, 2 * kc8)) =
+            is_v ? fp8x8_to_f16x8(regs[k][0], regs[k][1]) : fp8x8_to_bf16x8(regs[k][0], regs[k][1]);
+        *reinterpret_cast<u32x4 *>(tb + lds_off(is_v, t, 2 * kc8 + 1)) =
+            is_v ? fp8x8_to_f16x8(regs[k][2], regs[k][3]) : fp8x8_to_bf16x8(regs[k][2], regs[k][3]);
       } else {
         *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, q >> 4, q & 15)) = regs[k];
       }
     }
+  };
+  // bf16 caches: the V tiles of a pair arrive in LDS as bf16 and are turned
+  // into fp16 in place before any wave reads them; each lane converts the
+  // two 16-byte slots its own loads filled (loads 1 and 3: V_a and V_b), so
+  // it needs only its own loads done, and the barrier before the pair's V
+  // reads publishes the result.
+  auto convert_v = [&](auto st) __attribute__((always_inline)) {
+    static_assert(kRowsContig, "slots of a lane's V loads");
+    uint8_t *own = stage_mem(st) + w * 1024 + lane * 16;
+    u32x4 *pa = reinterpret_cast<u32x4 *>(own + 1 * kTile), *pb = reinterpret_cast<u32x4 *>(own + 3 * kTile);
+    const u32x4 a = *pa, b = *pb;
+    *pa = u32x4{bf16x2_to_f16x2(a[0]), bf16x2_to_f16x2(a[1]), bf16x2_to_f16x2(a[2]), bf16x2_to_f16x2(a[3])};
+    *pb = u32x4{bf16x2_to_f16x2(b[0]), bf16x2_to_f16x2(b[1]), bf16x2_to_f16x2(b[2]), bf16x2_to_f16x2(b[3])};
   };
   // V^T operand address of this lane inside a V tile for dim tile dt: lane
   // (r, j, q) = (r, c >> 2, c & 3) points at V[4r + j][16 dt + 4q].
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       kb[i] = *reinterpret_cast<const u32x4 *>(base + 2 * kTile + ck);
     }
   };
-  auto lread_v = [&](auto stage, bf16x8 *vt) __attribute__((always_inline)) {
+  auto lread_v = [&](auto stage, f16x8 *vt) __attribute__((always_inline)) {
     const uint8_t *base = stage_mem(stage);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -313,12 +334,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 1 * kTile + off));
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 3 * kTile + off));
       const u32x2 a2 = __builtin_bit_cast(u32x2, va), b2 = __builtin_bit_cast(u32x2, vb);
-      vt[dt] = __builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], b2[0], b2[1]});
+      vt[dt] = __builtin_bit_cast(f16x8, u32x4{a2[0], a2[1], b2[0], b2[1]});
     }
   };
   auto compute = [&](auto stage, int pr, int okbits, MfmaAttnPairState *st) __attribute__((always_inline)) {
     u32x4 ka[4], kb[4];
-    bf16x8 vt[8];
+    f16x8 vt[8];
     lread_k(stage, ka, kb);
     const int tok0 = 32 * pr;
     const bool oka = okbits & 1, okb = okbits & 2;
@@ -350,7 +371,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
-  if (kDma && CG == 2 && npair > 0) {
+  static_assert(!kDma || CG == 2, "bf16 caches take the pipelined two-group loop");
+  if (kDma && npair > 0) {
     // Software-pipelined: iteration X takes the softmax and PV products of
     // pair X while the score products of pair X + 1 run, so the two column
     // groups' softmax chains overlap matrix work.  Pair X lands in stage
@@ -377,6 +399,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     else
       vm_wait<0>();
     workgroup_barrier();
+    convert_v(S0());
     {
       u32x4 ka[4], kb[4];
       lread_k(S0(), ka, kb);
@@ -384,14 +407,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       MfmaAttnPairState::scores(qb[CG - 1], ka, kb, x1);
     }
     auto piter = [&](int X, auto cur, auto nxt, auto ld) __attribute__((always_inline)) -> bool {
+      // (the LDS stores of pair X's fp16 V, made in the previous iteration,
+      // are waited for too)
       if (X + 2 < npair)
-        vm_wait<kChunksPerThread>();
+        vm_lgkm_wait<kChunksPerThread>();
       else
-        vm_wait<0>();
+        vm_lgkm_wait<0>();
       workgroup_barrier();
       if (X + 3 < npair) ok[decltype(ld)::value] = dma_from(X + 3, ld, tv_next);
       tv_next = pair_table(X + 4);
-      bf16x8 vt[8];
+      f16x8 vt[8];
       u32x4 ka[4], kb[4];
       lread_v(cur, vt);
       lread_k(nxt, ka, kb);
@@ -423,23 +448,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       float y0[8], y1[8];
       MfmaAttnPairState::scores(qb[0], ka, kb, y0);
       MfmaAttnPairState::scores(qb[CG - 1], ka, kb, y1);
-      bf16x8 h0, l0, h1, l1;
-      st[0].weights(x0, sl2, h0, l0);
-      st[0].pv(vt, h0, l0);
-      st[CG - 1].weights(x1, sl2, h1, l1);
-      st[CG - 1].pv(vt, h1, l1);
+      f16x8 p0, p1;
+      st[0].weights(x0, sl2, p0);
+      st[0].pv(vt, p0);
+      st[CG - 1].weights(x1, sl2, p1);
+      st[CG - 1].pv(vt, p1);
+      // pair X + 1's V, read by every wave in the next iteration (here, where
+      // the matrix unit still has this pair's products queued)
+      if (X + 1 < npair) convert_v(nxt);
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         x0[v] = y0[v];
         x1[v] = y1[v];
       }
-      // Scheduling of the block above (from the last rescale test on): its 48
-      // MFMAs (16 score products of pair X + 1, 32 PV products of pair X) each
+      // Scheduling of the block above (from the last rescale test on): its 32
+      // MFMAs (16 score products of pair X + 1, 16 PV products of pair X) each
       // followed by up to three VALU instructions (weights, exponentials,
-      // hi/lo split), so the vector work issues while the matrix unit is busy
+      // fp16 packing), so the vector work issues while the matrix unit is busy
       // instead of in runs between MFMA runs.  Only placement changes.
 #pragma unroll
-      for (int i = 0; i < 48; ++i) {
+      for (int i = 0; i < 32; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // three VALU (incl. transcendental)
       }
@@ -450,33 +478,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (!piter(X + 1, S1(), S2(), S0())) break;
       if (!piter(X + 2, S2(), S3(), S1())) break;
       if (!piter(X + 3, S3(), S0(), S2())) break;
-    }
-  } else if (kDma && npair > 0) {
-    // Pair X lands in stage X % 4; its loads are issued three pairs ahead,
-    // right after the barrier that ends every read of that stage's previous
-    // pair.  Before pair X is read each thread waits for its own loads of it
-    // (the two later pairs may still be in flight: 2 * kChunksPerThread
-    // loads), and the barrier then covers every thread's.  A pair index past
-    // the end re-loads the last pair, so the count of loads in flight is the
-    // same in every iteration.
-    int ok[4];
-    ok[0] = dma(0, S0());
-    ok[1] = dma(1, S1());
-    ok[2] = dma(2, S2());
-    ok[3] = 0;
-    auto iter = [&](int X, auto cur, auto nxt) __attribute__((always_inline)) -> bool {
-      vm_wait<2 * kChunksPerThread>();
-      workgroup_barrier();
-      ok[decltype(nxt)::value] = dma(X + 3, nxt);
-      seen |= ok[decltype(cur)::value];
-      compute(cur, X, ok[decltype(cur)::value], st);
-      return X + 1 < npair;
-    };
-    for (int X = 0;; X += 4) {
-      if (!iter(X, S0(), S3())) break;
-      if (!iter(X + 1, S1(), S0())) break;
-      if (!iter(X + 2, S2(), S1())) break;
-      if (!iter(X + 3, S3(), S2())) break;
     }
   } else if (npair > 0) {
     // Pair X sits in register set X % 3 and LDS stage X % 3.  Its loads are
