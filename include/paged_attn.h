@@ -242,6 +242,10 @@ PA_EXPORT int paged_attn_decode(void *out, int32_t out_dtype, const void *q, con
  * Row i of sequence b sits at position seq_lens[b] - n_b + i and attends to
  * tokens 0 .. that position (inclusive).  The prefix need not end on a block
  * boundary.
+ * Precision (bf16 caches, head_dim 128): the softmax weights enter the PV
+ * product rounded once to fp16 and V is widened to fp16, so V entries must
+ * not exceed 65504 in magnitude (larger ones overflow to infinity); the
+ * rounding moves an output by at most 2^-11 * max |v| over its keys.
  */
 PA_EXPORT int paged_attn_prefill_chunk(void *out, int32_t out_dtype, const void *q, const void *k_cache,
                              const void *v_cache, int32_t kv_dtype, const int32_t *block_tables,
