@@ -279,17 +279,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int k = 0; k < kChunksPerThread; ++k) {
       const int u = tid + k * 64 * NW;
-      const int kind = u >> kTileShift, q = u & (kTileChunks - 1);
+      // (a tile spans at least one wave's chunks, so the tile kind is the
+      // wave's: computed from w, it stays in scalar registers)
+      static_assert(kTileShift >= 6, "a tile holds whole waves' chunks");
+      const int kind = (w * 64 + k * 64 * NW) >> kTileShift, q = u & (kTileChunks - 1);
       uint8_t *tb = stage_mem(stage) + kind * kTile;
       if (FP8) {
         // 16 codes = 16-bit chunks 2 kc8 and 2 kc8 + 1 of row t (K as bf16,
         // V as fp16: both exact)
         const int t = q >> 3, kc8 = q & 7;
-        const bool is_v = kind & 1;
-        *reinterpret_cast<u32x4 *>(tb + lds_off(is_v, t, 2 * kc8)) =
-            is_v ? fp8x8_to_f16x8(regs[k][0], regs[k][1]) : fp8x8_to_bf16x8(regs[k][0], regs[k][1]);
-        *reinterpret_cast<u32x4 *>(tb + lds_off(is_v, t, 2 * kc8 + 1)) =
-            is_v ? fp8x8_to_f16x8(regs[k][2], regs[k][3]) : fp8x8_to_bf16x8(regs[k][2], regs[k][3]);
+        if (kind & 1) {
+          *reinterpret_cast<u32x4 *>(tb + lds_off(true, t, 2 * kc8)) = fp8x8_to_f16x8(regs[k][0], regs[k][1]);
+          *reinterpret_cast<u32x4 *>(tb + lds_off(true, t, 2 * kc8 + 1)) = fp8x8_to_f16x8(regs[k][2], regs[k][3]);
+        } else {
+          *reinterpret_cast<u32x4 *>(tb + lds_off(false, t, 2 * kc8)) = fp8x8_to_bf16x8(regs[k][0], regs[k][1]);
+          *reinterpret_cast<u32x4 *>(tb + lds_off(false, t, 2 * kc8 + 1)) =
+              fp8x8_to_bf16x8(regs[k][2], regs[k][3]);
+        }
       } else {
         *reinterpret_cast<u32x4 *>(tb + lds_off(kind & 1, q >> 4, q & 15)) = regs[k];
       }
