@@ -452,6 +452,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st[0].raise_max(x0, sl2);
       st[CG - 1].raise_max(x1, sl2);
       float y0[8], y1[8];
+      // The block of matrix products (the next pair's scores, this pair's
+      // PV products and the softmax work placed between them) runs at a
+      // raised wave priority, so that a wave with matrix work ready issues
+      // ahead of the SIMD's other wave when both are ready.
+      __builtin_amdgcn_s_setprio(1);
       MfmaAttnPairState::scores(qb[0], ka, kb, y0);
       MfmaAttnPairState::scores(qb[CG - 1], ka, kb, y1);
       f16x8 p0, p1;
@@ -459,6 +464,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st[0].pv(vt, p0);
       st[CG - 1].weights(x1, sl2, p1);
       st[CG - 1].pv(vt, p1);
+      __builtin_amdgcn_s_setprio(0);
       // pair X + 1's V, read by every wave in the next iteration (here, where
       // the matrix unit still has this pair's products queued)
       if (X + 1 < npair) convert_v(nxt);
